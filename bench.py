@@ -1,0 +1,296 @@
+"""Benchmark of one MoE decode layer-step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies L] [--no-batches] [--no-cpu]
+
+Workload (headline line): one TP16 shard at batch 1 - hidden 7168, Wqkv
+7168x512, Wo 512x7168, fp32 router 7168x384 with sigmoid top-8, 384 SwiGLU
+experts with ffn shard 128 and a shared expert with ffn 128, bf16 weights,
+uniform-random routing.  Batches 8 (uniform and Zipf speculative-verify) and
+64 (TP8 shard, 32 hot experts) are measured the same way and reported under
+"batches".
+
+Protocol: L device-side copies of the layer (weights, expert pool, router)
+are rotated every step so that no step finds its weights in the 256 MB
+Infinity Cache (L * touched bytes >= 1 GB); inputs are resident in HBM before
+the timed region.  W warm-up steps, then K timed steps between HIP events on
+the launching stream, once with eager launches and once replaying one HIP
+graph per copy (the headline).  A third pass with per-launch HIP events gives
+each kernel's average duration, from which the roofline object is computed for
+the kernel that takes the most time.  The CPU baseline is the fp64 oracle run
+on a bounded sample of the same workload on the host cores.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs per decode layer-step & achieved HBM GB/s (% of peak), batch 1/8/64"
+HBM_PEAK_GBPS = 8000.0
+HEADLINE_CFG = 1
+BATCH_CFGS = (2, 4, 3)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- bytes
+def algorithmic_bytes(layer) -> dict:
+    """Unique weight bytes each launch must read plus its activation I/O.
+
+    Intermediates that stay on chip or in L2 between launches (hg, inv_rms,
+    the permutation lists, expert activations) are counted once where they
+    are produced and consumed only as activation traffic of the consumer
+    (h rows and ffn activations), as the floor any implementation pays."""
+    s = layer.shape
+    B, H, Dq, Do, E, k, F, Fs = (s.batch, s.hidden, s.qkv_out, s.attn_dim, s.n_experts,
+                                 s.top_k, s.expert_ffn, s.shared_ffn)
+    n_act = len(layer.touched_experts())
+    pairs = B * k
+    b = {}
+    b["proj_out_in"] = 2 * (Dq * H + H * Do + H) + 2 * B * (H + Do) + 4 * B * H * 2 + 4 * B * Dq
+    b["shared_gateup"] = 2 * 2 * Fs * H + 4 * B * H + 4 * B * Fs
+    b["router_topk_permute"] = 4 * E * H + 4 * B * H + 4 * B * E + 8 * pairs
+    b["expert_gateup"] = n_act * 2 * 2 * F * H + 4 * B * H + 4 * pairs * F
+    b["expert_down_combine"] = 2 * (n_act * H * F + H * Fs) + 4 * (pairs * F + B * Fs) + 4 * B * H
+    # whole step: unique weights + step I/O (x, attn, resid in/out, qkv, logits, idx, w, y)
+    weights = 2 * (Dq * H + H * Do + H) + 4 * E * H + n_act * 3 * 2 * F * H + 3 * 2 * Fs * H
+    io = 2 * B * (H + Do) + 4 * B * H * 2 + 4 * B * Dq + 4 * B * E + 8 * pairs + 4 * B * H
+    b["step"] = weights + io
+    b["step_flops"] = 2 * B * (Dq * H + H * Do + E * H) + 2 * pairs * 3 * F * H + 2 * B * 3 * Fs * H
+    return b
+
+
+# ----------------------------------------------------------------- GPU side
+def make_copies(layer, n_copies):
+    import torch
+    from synth import device as sdev
+    w0 = sdev.upload_weights(layer, fill_untouched="none")
+    touched = [int(e) for e in layer.touched_experts()]
+    copies = [w0]
+    for _ in range(1, n_copies):
+        w = {}
+        for key, t in w0.items():
+            if key in ("w1", "w3", "w2"):
+                c = torch.empty_like(t)
+                for e in touched:
+                    c[e].copy_(t[e])
+                w[key] = c
+            else:
+                w[key] = t.clone()
+        copies.append(w)
+    torch.cuda.synchronize()
+    return copies
+
+
+def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True):
+    import torch
+    from decode_step_moe_amd import DecodeLayer
+    from synth import device as sdev, routing, gen
+
+    raw = gen.draw(cfg_id)
+    layer = routing.shape_router(raw, routing.stored_h(cfg_id))
+    nbytes = algorithmic_bytes(layer)
+    if n_copies is None:
+        n_copies = max(4, int(np.ceil(1.0e9 / nbytes["step"])))
+    log(f"[bench] cfg {cfg_id} {layer.shape.name}: {len(layer.touched_experts())} experts, "
+        f"{nbytes['step'] / 1e6:.2f} MB/step, {n_copies} copies")
+    copies = make_copies(layer, n_copies)
+    cfg = sdev.config_of(layer)
+    handles = [DecodeLayer(cfg, w) for w in copies]
+    x, attn, resid = sdev.upload_inputs(layer)
+    outs = [h.alloc_outputs(layer.shape.batch) for h in handles]
+    ios = [h.make_io(x, attn, resid, o) for h, o in zip(handles, outs)]
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        handles[i % n_copies].step_io(ios[i % n_copies], stream)
+
+    # consistency: every copy produces identical results
+    for i in range(n_copies):
+        run(i)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.topk_idx, outs[0].topk_idx) and torch.equal(o.moe_out, outs[0].moe_out)
+    assert np.array_equal(np.sort(outs[0].topk_idx.cpu().numpy(), 1), np.sort(layer.targets, 1))
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    eager_ms = timed(run)
+    # one graph per copy
+    graphs = []
+    side = torch.cuda.Stream()
+    for i in range(n_copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            handles[i].step_io(ios[i], side)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    graph_ms = timed(lambda i: graphs[i % n_copies].replay())
+    # graph results equal eager results
+    ref = outs[0].moe_out.clone()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].moe_out, ref)
+
+    kern = {}
+    if want_kernels:
+        for h in handles:
+            h.set_profiling(True)
+        acc = {}
+        for i in range(warmup):
+            run(i)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            run(i)
+            for k_, v in handles[i % n_copies].kernel_times_ms().items():
+                acc.setdefault(k_, []).append(v)
+        for h in handles:
+            h.set_profiling(False)
+        kern = {k_: float(np.mean(v)) for k_, v in acc.items()}
+    res = {"cfg": cfg_id, "workload": layer.shape.name, "batch": layer.shape.batch,
+           "copies": n_copies, "eager_us": eager_ms * 1e3, "graph_us": graph_ms * 1e3,
+           "bytes": nbytes, "kernel_us": {k_: v * 1e3 for k_, v in kern.items()},
+           "active_experts": int(len(layer.touched_experts()))}
+    del graphs, handles, copies
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, layer
+
+
+# ----------------------------------------------------------------- CPU baseline
+def cpu_baseline(layer, budget_s=10.0):
+    """The fp64 oracle as it stands, on a bounded sample of the same workload."""
+    from oracle import decode_layer_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    raw = layer.raw
+
+    def one():
+        ref.decode_step(raw.x, raw.attn, raw.resid, raw.w_qkv, raw.w_o, raw.gain, layer.w_router,
+                        raw.expert, raw.s1, raw.s3, raw.s2, raw.shape.top_k)
+
+    one()  # draws (and caches) the touched experts outside the timed sample
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        one()
+        n += 1
+    dt = (time.perf_counter() - t0) / n
+    return {"value": dt * 1e6, "unit": "us/layer-step", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full layer-steps of the batch-1 TP16-shard workload (float64 NumPy), "
+                      f"{n * dt:.1f} s", "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ----------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=None)
+    ap.add_argument("--no-batches", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer-step is one tensor-parallel shard's work on one GPU)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import decode_step_moe_amd  # noqa: F401  (fails loudly without the built library)
+
+    head, layer = time_config(HEADLINE_CFG, args.steps, args.warmup, args.copies)
+    batches = {}
+    if not args.no_batches:
+        for c in BATCH_CFGS:
+            r, _ = time_config(c, max(20, args.steps // 2), args.warmup, None)
+            batches[r["workload"]] = _summary(r)
+    us = head["graph_us"]
+    b = head["bytes"]
+    kern = head["kernel_us"]
+    dom = max(kern, key=kern.get)
+    achieved = b[dom] / (kern[dom] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "hidden": 7168, "batch": 1, "qkv_out": 512,
+                   "attn_dim": 512, "n_experts": 384, "top_k": 8, "expert_ffn": 128,
+                   "shared_ffn": 128, "routing": "uniform-random", "timing": "hip-graph replay",
+                   "copies_rotated": head["copies"]},
+        "hbm_gbps": round(b["step"] / (us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(b["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "tok_per_s_per_shard": round(1 / (us * 1e-6), 1),
+        "eager_us": round(head["eager_us"], 3),
+        "launches_per_step": 5,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": b[dom],
+                     "avg_launch_us": round(kern[dom], 3)},
+        "kernels_us": {k_: round(v, 3) for k_, v in kern.items()},
+        "batches": batches,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def _summary(r):
+    us = r["graph_us"]
+    return {"batch": r["batch"], "graph_us": round(us, 3), "eager_us": round(r["eager_us"], 3),
+            "hbm_gbps": round(r["bytes"]["step"] / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(r["bytes"]["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tok_per_s_per_shard": round(r["batch"] / (us * 1e-6), 1),
+            "active_experts": r["active_experts"], "copies": r["copies"],
+            "kernels_us": {k_: round(v, 3) for k_, v in r["kernel_us"].items()}}
+
+
+if __name__ == "__main__":
+    main()

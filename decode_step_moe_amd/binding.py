@@ -1,0 +1,231 @@
+"""Thin ctypes binding of libdecode_layer.so (include/decode_layer.h).
+
+Argument marshalling only: dtype / shape / device / contiguity checks on the
+torch tensors, then their data pointers and the current HIP stream go to the
+C ABI.  Every step of the layer runs in the library's HIP kernels; there is
+no Python or CPU fallback - if the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdecode_layer.so")
+
+DL_OK, DL_ERR_INVALID_ARG, DL_ERR_UNSUPPORTED, DL_ERR_HIP, DL_ERR_OOM = 0, -1, -2, -3, -4
+_ERR_NAMES = {0: "DL_OK", -1: "DL_ERR_INVALID_ARG", -2: "DL_ERR_UNSUPPORTED", -3: "DL_ERR_HIP",
+              -4: "DL_ERR_OOM"}
+
+
+class DecodeLayerError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("qkv_out", ctypes.c_int32),
+                ("attn_dim", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
+                ("shared_ffn", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("score_fn", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_qkv", "w_o", "norm_gain", "w_router", "w1", "w3", "w2", "s1", "s3", "s2")]
+
+
+class IO(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32)] + [(n, ctypes.c_void_p) for n in
+                ("x", "attn", "resid_in", "qkv", "resid_out", "router_logits", "topk_idx",
+                 "topk_w", "moe_out", "h_out")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m decode_step_moe_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.decode_layer_init.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
+                                        ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]
+        L.decode_layer_init.restype = ctypes.c_int
+        L.decode_layer_step.argtypes = [ctypes.c_void_p, ctypes.POINTER(IO), ctypes.c_void_p]
+        L.decode_layer_step.restype = ctypes.c_int
+        L.decode_layer_destroy.argtypes = [ctypes.c_void_p]
+        L.decode_layer_destroy.restype = ctypes.c_int
+        L.decode_layer_check_config.argtypes = [ctypes.POINTER(Config)]
+        L.decode_layer_check_config.restype = ctypes.c_int
+        L.decode_layer_check_io.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(IO)]
+        L.decode_layer_check_io.restype = ctypes.c_int
+        L.decode_layer_last_error.argtypes = [ctypes.c_void_p]
+        L.decode_layer_last_error.restype = ctypes.c_char_p
+        L.decode_layer_set_profiling.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        L.decode_layer_set_profiling.restype = ctypes.c_int
+        L.decode_layer_kernel_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_int]
+        L.decode_layer_kernel_times.restype = ctypes.c_int
+        L.decode_layer_scratch_bytes.argtypes = [ctypes.POINTER(Config)]
+        L.decode_layer_scratch_bytes.restype = ctypes.c_size_t
+        _lib = L
+    return _lib
+
+
+def last_error(handle=None) -> str:
+    return lib().decode_layer_last_error(handle).decode()
+
+
+def make_config(hidden, qkv_out, attn_dim, n_experts, top_k, expert_ffn, shared_ffn, max_batch,
+                rms_eps=1e-6, score_fn=0, renormalize=1) -> Config:
+    return Config(hidden, qkv_out, attn_dim, n_experts, top_k, expert_ffn, shared_ffn, max_batch,
+                  rms_eps, score_fn, renormalize)
+
+
+def check_config(cfg: Config) -> int:
+    return lib().decode_layer_check_config(ctypes.byref(cfg))
+
+
+def check_io(cfg: Config, io: IO) -> int:
+    return lib().decode_layer_check_io(ctypes.byref(cfg), ctypes.byref(io))
+
+
+def scratch_bytes(cfg: Config) -> int:
+    return lib().decode_layer_scratch_bytes(ctypes.byref(cfg))
+
+
+def _ptr(t, dtype, shape, name):
+    import torch
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    return t.data_ptr() if t.numel() else None
+
+
+@dataclass
+class StepOutputs:
+    qkv: object
+    resid_out: object
+    router_logits: object
+    topk_idx: object
+    topk_w: object
+    moe_out: object
+    h_out: object = None
+
+
+class DecodeLayer:
+    """One layer shard's weights bound to a library handle.
+
+    `weights` maps w_qkv, w_o, norm_gain, w_router, w1, w3, w2, s1, s3, s2 to
+    GPU tensors (bf16 except w_router fp32; s1/s3/s2 absent iff shared_ffn 0).
+    The tensors are referenced, not copied, and must stay unchanged.
+    """
+
+    def __init__(self, cfg: Config, weights: dict, device: int = 0):
+        import torch
+        self.cfg = cfg
+        self._keep = dict(weights)
+        H, Dq, Do, E, F, Fs = (cfg.hidden, cfg.qkv_out, cfg.attn_dim, cfg.n_experts,
+                               cfg.expert_ffn, cfg.shared_ffn)
+        bf = torch.bfloat16
+        w = Weights(
+            _ptr(weights["w_qkv"], bf, (Dq, H), "w_qkv"), _ptr(weights["w_o"], bf, (H, Do), "w_o"),
+            _ptr(weights["norm_gain"], bf, (H,), "norm_gain"),
+            _ptr(weights["w_router"], torch.float32, (E, H), "w_router"),
+            _ptr(weights["w1"], bf, (E, F, H), "w1"), _ptr(weights["w3"], bf, (E, F, H), "w3"),
+            _ptr(weights["w2"], bf, (E, H, F), "w2"),
+            _ptr(weights.get("s1"), bf, (Fs, H), "s1") if Fs else None,
+            _ptr(weights.get("s3"), bf, (Fs, H), "s3") if Fs else None,
+            _ptr(weights.get("s2"), bf, (H, Fs), "s2") if Fs else None)
+        h = ctypes.c_void_p()
+        rc = lib().decode_layer_init(ctypes.byref(cfg), ctypes.byref(w), device, ctypes.byref(h))
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error())
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().decode_layer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    LAUNCH_NAMES = ("proj_out_in", "shared_gateup", "router_topk_permute", "expert_gateup",
+                    "expert_down_combine")
+
+    def set_profiling(self, enable: bool):
+        rc = lib().decode_layer_set_profiling(self._h, int(enable))
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error(self._h))
+
+    def kernel_times_ms(self) -> dict:
+        """Per-launch durations (ms) of the last step run with profiling on."""
+        buf = (ctypes.c_float * len(self.LAUNCH_NAMES))()
+        n = lib().decode_layer_kernel_times(self._h, buf, len(buf))
+        if n < 0:
+            raise DecodeLayerError(n, last_error(self._h))
+        return {name: float(buf[i]) for i, name in enumerate(self.LAUNCH_NAMES[:n])}
+
+    def alloc_outputs(self, batch: int, device="cuda", with_h: bool = False,
+                      with_logits: bool = True) -> StepOutputs:
+        import torch
+        c = self.cfg
+        f32 = torch.float32
+        return StepOutputs(
+            torch.empty(batch, c.qkv_out, dtype=f32, device=device),
+            torch.empty(batch, c.hidden, dtype=f32, device=device),
+            torch.empty(batch, c.n_experts, dtype=f32, device=device) if with_logits else None,
+            torch.empty(batch, c.top_k, dtype=torch.int32, device=device),
+            torch.empty(batch, c.top_k, dtype=f32, device=device),
+            torch.empty(batch, c.hidden, dtype=f32, device=device),
+            torch.empty(batch, c.hidden, dtype=f32, device=device) if with_h else None)
+
+    def make_io(self, x, attn, resid_in, out: StepOutputs) -> IO:
+        import torch
+        c = self.cfg
+        B = x.shape[0]
+        bf, f32 = torch.bfloat16, torch.float32
+        return IO(B, _ptr(x, bf, (B, c.hidden), "x"), _ptr(attn, bf, (B, c.attn_dim), "attn"),
+                  _ptr(resid_in, f32, (B, c.hidden), "resid_in"),
+                  _ptr(out.qkv, f32, (B, c.qkv_out), "qkv"),
+                  _ptr(out.resid_out, f32, (B, c.hidden), "resid_out"),
+                  _ptr(out.router_logits, f32, (B, c.n_experts), "router_logits"),
+                  _ptr(out.topk_idx, torch.int32, (B, c.top_k), "topk_idx"),
+                  _ptr(out.topk_w, f32, (B, c.top_k), "topk_w"),
+                  _ptr(out.moe_out, f32, (B, c.hidden), "moe_out"),
+                  _ptr(out.h_out, f32, (B, c.hidden), "h_out"))
+
+    def step_io(self, io: IO, stream=None):
+        """Enqueue one step from a prepared IO block on `stream` (default: current)."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        rc = lib().decode_layer_step(self._h, ctypes.byref(io), ctypes.c_void_p(stream.cuda_stream))
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error(self._h))
+
+    def step(self, x, attn, resid_in, out: StepOutputs | None = None, stream=None,
+             with_h: bool = False) -> StepOutputs:
+        if out is None:
+            out = self.alloc_outputs(x.shape[0], device=x.device, with_h=with_h)
+        self.step_io(self.make_io(x, attn, resid_in, out), stream)
+        return out

@@ -1,0 +1,165 @@
+// Device helpers shared by the decode-layer kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dl {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;           // 4 waves per workgroup everywhere
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ---- bf16 <-> fp32 (bf16 kept as raw 16-bit patterns) ---------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4 &w, float (&f)[8]) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+  f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+  f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+// ---- 16-byte global loads --------------------------------------------------
+// Weights are streamed once per step: load them non-temporally so that they
+// do not evict the small activation vectors every wave re-reads from L2.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+  v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld_stream16f(const void *p) {
+  v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ float4 ld16f(const void *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// ---- wave reductions -------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---- activation loaders: 8 consecutive values of token t as fp32 ----------
+// Activations are small (one row per token) and re-read by many waves, so
+// they use ordinary cached loads.
+struct ActBf16 {          // bf16 [tokens][ld]
+  const uint16_t *base;
+  int ld;
+  __device__ __forceinline__ void load8(int t, int k, float (&a)[8]) const {
+    unpack8(ld16(base + (size_t)t * ld + k), a);
+  }
+};
+
+struct ActF32 {           // fp32 [tokens][ld]
+  const float *base;
+  int ld;
+  __device__ __forceinline__ void load8(int t, int k, float (&a)[8]) const {
+    const float *p = base + (size_t)t * ld + k;
+    float4 u = ld16f(p), v = ld16f(p + 4);
+    a[0] = u.x; a[1] = u.y; a[2] = u.z; a[3] = u.w;
+    a[4] = v.x; a[5] = v.y; a[6] = v.z; a[7] = v.w;
+  }
+};
+
+// fp32 activations gathered through a token list (routed experts).
+template <int NT>
+struct ActF32Gather {
+  const float *base;
+  int ld;
+  int tok[NT];
+  __device__ __forceinline__ void load8(int t, int k, float (&a)[8]) const {
+    const float *p = base + (size_t)tok[t] * ld + k;
+    float4 u = ld16f(p), v = ld16f(p + 4);
+    a[0] = u.x; a[1] = u.y; a[2] = u.z; a[3] = u.w;
+    a[4] = v.x; a[5] = v.y; a[6] = v.z; a[7] = v.w;
+  }
+};
+
+// ---- the skinny-GEMM inner loop ------------------------------------------
+// acc[r][t] += sum over this lane's K positions of W_r[k] * act_t[k], for NR
+// bf16 weight rows and NT tokens.  The lane visits k = k0, k0+kstride, ...
+// (< K), 8 elements (16 bytes of weights) per visit; K, k0 and kstride are
+// multiples of 8.  U visits are unrolled so that U*NR independent 16-byte
+// weight loads are in flight before the first one is consumed.
+template <int NR, int NT, int U, class Act>
+__device__ __forceinline__ void stream_rows_bf16(const uint16_t *const (&w)[NR], const Act &act,
+                                                 int k0, int kstride, int K, float (&acc)[NR][NT]) {
+  int k = k0;
+  for (; k + (U - 1) * kstride < K; k += U * kstride) {
+    uint4 wv[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) wv[u][r] = ld_stream16(w[r] + k + u * kstride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float a[NT][8];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) act.load8(t, k + u * kstride, a[t]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float wf[8];
+        unpack8(wv[u][r], wf);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][t] = fmaf(wf[e], a[t][e], acc[r][t]);
+      }
+    }
+  }
+  for (; k < K; k += kstride) {
+    uint4 wv[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) wv[r] = ld_stream16(w[r] + k);
+    float a[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) act.load8(t, k, a[t]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      float wf[8];
+      unpack8(wv[r], wf);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][t] = fmaf(wf[e], a[t][e], acc[r][t]);
+    }
+  }
+}
+
+// ---- cross-workgroup hand-off ------------------------------------------------
+// Every workgroup of a phase publishes its partial results, then counts
+// itself in `counter`; the workgroup that arrives last sees every other
+// workgroup's results.  Release (before the count) and acquire (after it)
+// are at agent scope, which on a multi-XCD part also writes back / invalidates
+// the per-XCD L2 as needed.  Nothing produced by another workgroup is read
+// before the acquire; only static weights may be loaded earlier.
+// Returns true in every thread of the last workgroup.  The last workgroup
+// re-arms the counter for the next step.
+__device__ __forceinline__ bool arrive_last(unsigned *counter, unsigned nblocks, int *lds_flag) {
+  __threadfence();          // release this thread's stores at agent scope
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = (prev == nblocks - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  bool last = *lds_flag != 0;
+  if (last) {
+    __threadfence();        // acquire for every thread of the last workgroup
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return last;
+}
+
+}  // namespace dl

@@ -1,0 +1,436 @@
+// Host side of the C ABI declared in include/decode_layer.h: validation,
+// the handle (scratch, second stream, events) and the launch sequence of one
+// step.  Nothing here computes layer math; every step of the layer runs in
+// the kernels of proj.hip, router.hip and experts.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/decode_layer.h"
+#include "kernels.h"
+
+using namespace dl;
+
+namespace {
+
+thread_local std::string g_thread_err = "no error";
+
+struct Scratch {
+  float *hg = nullptr;        // [maxB][H]   g * r1
+  float *ss_part = nullptr;   // [nblk_o][maxB]
+  float *inv_rms = nullptr;   // [maxB]
+  float *logits = nullptr;    // [maxB][E]
+  int *pair_tok = nullptr;    // [maxB*k]
+  float *pair_w = nullptr;    // [maxB*k]
+  int *act_exp = nullptr;     // [E]
+  int *act_cnt = nullptr;     // [E]
+  int *act_off = nullptr;     // [E]
+  int *n_active = nullptr;    // [1]
+  float *act = nullptr;       // [maxB*k][F]
+  float *act_s = nullptr;     // [maxB][Fs]
+  unsigned *counters = nullptr;  // [2]: out-projection, router
+};
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t off[13];
+  size_t total;
+};
+
+int nblk_o_of(const decode_layer_config &c) { return (c.hidden + kORowsPerBlock - 1) / kORowsPerBlock; }
+
+Layout layout_of(const decode_layer_config &c) {
+  const size_t B = c.max_batch, H = c.hidden, E = c.n_experts, K = c.top_k;
+  const size_t sizes[13] = {
+      B * H * 4, (size_t)nblk_o_of(c) * B * 4, B * 4, B * E * 4, B * K * 4, B * K * 4,
+      E * 4, E * 4, E * 4, 4, B * K * (size_t)c.expert_ffn * 4, B * (size_t)(c.shared_ffn > 0 ? c.shared_ffn : 1) * 4,
+      2 * 4};
+  Layout L;
+  size_t o = 0;
+  for (int i = 0; i < 13; ++i) { L.off[i] = o; o += align256(sizes[i]); }
+  L.total = o;
+  return L;
+}
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct decode_layer {
+  decode_layer_config cfg;
+  decode_layer_weights w;
+  int device = 0;
+  void *scratch_base = nullptr;
+  Scratch s;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  bool profiling = false;
+  bool profiled_step = false;
+  hipEvent_t ev_prof[DECODE_LAYER_N_LAUNCHES][2] = {};
+  bool launched[DECODE_LAYER_N_LAUNCHES] = {};
+  std::string err = "no error";
+};
+
+// Event pair around launch `i` when profiling is on.
+struct ProfScope {
+  decode_layer *h;
+  int i;
+  hipStream_t s;
+  hipError_t begin() {
+    if (!h->profiling) return hipSuccess;
+    h->launched[i] = true;
+    return hipEventRecord(h->ev_prof[i][0], s);
+  }
+  hipError_t end() { return h->profiling ? hipEventRecord(h->ev_prof[i][1], s) : hipSuccess; }
+};
+
+static int fail(decode_layer *h, int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (h) h->err = buf;
+  g_thread_err = buf;
+  return code;
+}
+
+static int check_config(const decode_layer_config *c, decode_layer *h) {
+  if (!c) return fail(h, DL_ERR_INVALID_ARG, "config is NULL");
+  if (c->hidden < 8 || c->hidden > 16384 || c->hidden % 8)
+    return fail(h, DL_ERR_UNSUPPORTED, "hidden=%d: need 8..16384 and a multiple of 8", c->hidden);
+  if (c->qkv_out < 1 || c->qkv_out > 65536)
+    return fail(h, DL_ERR_UNSUPPORTED, "qkv_out=%d: need 1..65536", c->qkv_out);
+  if (c->attn_dim < 8 || c->attn_dim > 16384 || c->attn_dim % 8)
+    return fail(h, DL_ERR_UNSUPPORTED, "attn_dim=%d: need 8..16384 and a multiple of 8", c->attn_dim);
+  if (c->n_experts < 1 || c->n_experts > kMaxExperts)
+    return fail(h, DL_ERR_UNSUPPORTED, "n_experts=%d: need 1..%d", c->n_experts, kMaxExperts);
+  if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > kMaxTopK)
+    return fail(h, DL_ERR_UNSUPPORTED, "top_k=%d: need 1..min(n_experts, %d)", c->top_k, kMaxTopK);
+  if (c->expert_ffn < 32 || c->expert_ffn > 256 || !pow2(c->expert_ffn))
+    return fail(h, DL_ERR_UNSUPPORTED, "expert_ffn=%d: need 32, 64, 128 or 256", c->expert_ffn);
+  if (c->shared_ffn != 0 && (c->shared_ffn < 32 || c->shared_ffn > 256 || !pow2(c->shared_ffn)))
+    return fail(h, DL_ERR_UNSUPPORTED, "shared_ffn=%d: need 0, 32, 64, 128 or 256", c->shared_ffn);
+  if (c->max_batch < 1 || c->max_batch > kMaxBatch)
+    return fail(h, DL_ERR_UNSUPPORTED, "max_batch=%d: need 1..%d", c->max_batch, kMaxBatch);
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps))
+    return fail(h, DL_ERR_UNSUPPORTED, "rms_eps must be positive and finite");
+  if (c->score_fn != 0) return fail(h, DL_ERR_UNSUPPORTED, "score_fn=%d: only 0 (sigmoid) is supported", c->score_fn);
+  if (c->renormalize != 1)
+    return fail(h, DL_ERR_UNSUPPORTED, "renormalize=%d: only 1 is supported", c->renormalize);
+  return DL_OK;
+}
+
+static int check_weights(const decode_layer_config *c, const decode_layer_weights *w, decode_layer *h) {
+  if (!w) return fail(h, DL_ERR_INVALID_ARG, "weights is NULL");
+  const void *req[] = {w->w_qkv, w->w_o, w->norm_gain, w->w_router, w->w1, w->w3, w->w2};
+  const char *names[] = {"w_qkv", "w_o", "norm_gain", "w_router", "w1", "w3", "w2"};
+  for (int i = 0; i < 7; ++i) {
+    if (!req[i]) return fail(h, DL_ERR_INVALID_ARG, "weights.%s is NULL", names[i]);
+    if (!aligned16(req[i])) return fail(h, DL_ERR_INVALID_ARG, "weights.%s is not 16-byte aligned", names[i]);
+  }
+  const void *sh[] = {w->s1, w->s3, w->s2};
+  const char *shn[] = {"s1", "s3", "s2"};
+  for (int i = 0; i < 3; ++i) {
+    if (c->shared_ffn > 0 && !sh[i]) return fail(h, DL_ERR_INVALID_ARG, "weights.%s is NULL but shared_ffn > 0", shn[i]);
+    if (sh[i] && !aligned16(sh[i])) return fail(h, DL_ERR_INVALID_ARG, "weights.%s is not 16-byte aligned", shn[i]);
+  }
+  return DL_OK;
+}
+
+static int check_io(const decode_layer_config *c, const decode_layer_io *io, decode_layer *h) {
+  if (!io) return fail(h, DL_ERR_INVALID_ARG, "io is NULL");
+  if (io->batch < 0) return fail(h, DL_ERR_INVALID_ARG, "batch=%d is negative", io->batch);
+  if (io->batch > c->max_batch)
+    return fail(h, DL_ERR_UNSUPPORTED, "batch=%d exceeds max_batch=%d", io->batch, c->max_batch);
+  if (io->batch == 0) return DL_OK;
+  const void *req[] = {io->x, io->attn, io->resid_in, io->qkv, io->resid_out, io->topk_idx, io->topk_w, io->moe_out};
+  const char *names[] = {"x", "attn", "resid_in", "qkv", "resid_out", "topk_idx", "topk_w", "moe_out"};
+  for (int i = 0; i < 8; ++i) {
+    if (!req[i]) return fail(h, DL_ERR_INVALID_ARG, "io.%s is NULL", names[i]);
+    if (!aligned16(req[i])) return fail(h, DL_ERR_INVALID_ARG, "io.%s is not 16-byte aligned", names[i]);
+  }
+  if (io->router_logits && !aligned16(io->router_logits))
+    return fail(h, DL_ERR_INVALID_ARG, "io.router_logits is not 16-byte aligned");
+  if (io->h_out && !aligned16(io->h_out)) return fail(h, DL_ERR_INVALID_ARG, "io.h_out is not 16-byte aligned");
+  if (io->resid_out != io->resid_in) {
+    // partial overlap of the residual buffers would race; exact aliasing is allowed
+    const char *a0 = (const char *)io->resid_in, *b0 = (const char *)io->resid_out;
+    size_t n = (size_t)io->batch * c->hidden * 4;
+    if (a0 < b0 + n && b0 < a0 + n) return fail(h, DL_ERR_INVALID_ARG, "io.resid_out partially overlaps io.resid_in");
+  }
+  return DL_OK;
+}
+
+#define HIP_TRY(h, expr)                                                                         \
+  do {                                                                                           \
+    hipError_t e_ = (expr);                                                                      \
+    if (e_ != hipSuccess) return fail(h, DL_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" {
+
+int decode_layer_check_config(const decode_layer_config *cfg) { return check_config(cfg, nullptr); }
+
+int decode_layer_check_io(const decode_layer_config *cfg, const decode_layer_io *io) {
+  int rc = check_config(cfg, nullptr);
+  if (rc != DL_OK) return rc;
+  return check_io(cfg, io, nullptr);
+}
+
+size_t decode_layer_scratch_bytes(const decode_layer_config *cfg) {
+  if (check_config(cfg, nullptr) != DL_OK) return 0;
+  return layout_of(*cfg).total;
+}
+
+const char *decode_layer_last_error(const decode_layer *h) {
+  return h ? h->err.c_str() : g_thread_err.c_str();
+}
+
+int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights *w, int device,
+                      decode_layer **out) {
+  if (!out) return fail(nullptr, DL_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg, nullptr);
+  if (rc != DL_OK) return rc;
+  rc = check_weights(cfg, w, nullptr);
+  if (rc != DL_OK) return rc;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0)
+    return fail(nullptr, DL_ERR_HIP, "no HIP device available");
+  if (device < 0 || device >= ndev) return fail(nullptr, DL_ERR_INVALID_ARG, "device %d out of range (%d devices)", device, ndev);
+  decode_layer *h = new (std::nothrow) decode_layer;
+  if (!h) return fail(nullptr, DL_ERR_OOM, "host allocation failed");
+  h->cfg = *cfg;
+  h->w = *w;
+  h->device = device;
+  auto cleanup = [&](int code) {
+    g_thread_err = h->err;
+    decode_layer_destroy(h);
+    return code;
+  };
+  if (hipSetDevice(device) != hipSuccess) return cleanup(fail(h, DL_ERR_HIP, "hipSetDevice(%d) failed", device));
+  Layout L = layout_of(*cfg);
+  if (hipMalloc(&h->scratch_base, L.total) != hipSuccess) {
+    h->scratch_base = nullptr;
+    return cleanup(fail(h, DL_ERR_OOM, "hipMalloc of %zu scratch bytes failed", L.total));
+  }
+  char *b = (char *)h->scratch_base;
+  h->s.hg = (float *)(b + L.off[0]);
+  h->s.ss_part = (float *)(b + L.off[1]);
+  h->s.inv_rms = (float *)(b + L.off[2]);
+  h->s.logits = (float *)(b + L.off[3]);
+  h->s.pair_tok = (int *)(b + L.off[4]);
+  h->s.pair_w = (float *)(b + L.off[5]);
+  h->s.act_exp = (int *)(b + L.off[6]);
+  h->s.act_cnt = (int *)(b + L.off[7]);
+  h->s.act_off = (int *)(b + L.off[8]);
+  h->s.n_active = (int *)(b + L.off[9]);
+  h->s.act = (float *)(b + L.off[10]);
+  h->s.act_s = (float *)(b + L.off[11]);
+  h->s.counters = (unsigned *)(b + L.off[12]);
+  // The hand-off counters start at zero and are re-armed by the kernels
+  // themselves, so no step ever needs a memset.
+  if (hipMemset(h->scratch_base, 0, L.total) != hipSuccess) return cleanup(fail(h, DL_ERR_HIP, "hipMemset failed"));
+  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) {
+    h->side = nullptr;
+    return cleanup(fail(h, DL_ERR_HIP, "hipStreamCreateWithFlags failed"));
+  }
+  if (hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess) {
+    h->ev_fork = nullptr;
+    return cleanup(fail(h, DL_ERR_HIP, "hipEventCreate failed"));
+  }
+  if (hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+    h->ev_join = nullptr;
+    return cleanup(fail(h, DL_ERR_HIP, "hipEventCreate failed"));
+  }
+  if (hipDeviceSynchronize() != hipSuccess) return cleanup(fail(h, DL_ERR_HIP, "hipDeviceSynchronize failed"));
+  *out = h;
+  return DL_OK;
+}
+
+int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stream) {
+  if (!h) return fail(nullptr, DL_ERR_INVALID_ARG, "handle is NULL");
+  int rc = check_io(&h->cfg, io, h);
+  if (rc != DL_OK) return rc;
+  if (io->batch == 0) return DL_OK;
+  const decode_layer_config &c = h->cfg;
+  hipStream_t st = (hipStream_t)hip_stream;
+  HIP_TRY(h, hipSetDevice(h->device));
+  const int B = io->batch;
+
+  ProjArgs pa{};
+  pa.x = (const uint16_t *)io->x;
+  pa.w_qkv = (const uint16_t *)h->w.w_qkv;
+  pa.qkv = io->qkv;
+  pa.attn = (const uint16_t *)io->attn;
+  pa.w_o = (const uint16_t *)h->w.w_o;
+  pa.gain = (const uint16_t *)h->w.norm_gain;
+  pa.resid_in = io->resid_in;
+  pa.resid_out = io->resid_out;
+  pa.hg = h->s.hg;
+  pa.ss_part = h->s.ss_part;
+  pa.inv_rms = h->s.inv_rms;
+  pa.counter = h->s.counters + 0;
+  pa.B = B;
+  pa.H = c.hidden;
+  pa.Dq = c.qkv_out;
+  pa.Do = c.attn_dim;
+  pa.eps = c.rms_eps;
+  pa.nblk_o = nblk_o_of(c);
+  pa.nblk_qkv = (c.qkv_out + kQkvRowsPerBlock - 1) / kQkvRowsPerBlock;
+  if (h->profiling)
+    for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i) h->launched[i] = false;
+  ProfScope p0{h, 0, st};
+  HIP_TRY(h, p0.begin());
+  HIP_TRY(h, launch_proj(pa, st));
+  HIP_TRY(h, p0.end());
+
+  if (c.shared_ffn > 0) {
+    HIP_TRY(h, hipEventRecord(h->ev_fork, st));
+    HIP_TRY(h, hipStreamWaitEvent(h->side, h->ev_fork, 0));
+    GateUpArgs ga{};
+    ga.w1 = (const uint16_t *)h->w.s1;
+    ga.w3 = (const uint16_t *)h->w.s3;
+    ga.hg = h->s.hg;
+    ga.inv_rms = h->s.inv_rms;
+    ga.act = h->s.act_s;
+    ga.B = B;
+    ga.H = c.hidden;
+    ga.F = c.shared_ffn;
+    ga.shared = 1;
+    ProfScope p1{h, 1, h->side};
+    HIP_TRY(h, p1.begin());
+    HIP_TRY(h, launch_gateup(ga, c.shared_ffn / kGateRowsPerBlock, h->side));
+    HIP_TRY(h, p1.end());
+    HIP_TRY(h, hipEventRecord(h->ev_join, h->side));
+  }
+
+  RouterArgs ra{};
+  ra.w_router = h->w.w_router;
+  ra.hg = h->s.hg;
+  ra.inv_rms = h->s.inv_rms;
+  ra.logits = h->s.logits;
+  ra.logits_out = io->router_logits;
+  ra.h_out = io->h_out;
+  ra.topk_idx = io->topk_idx;
+  ra.topk_w = io->topk_w;
+  ra.n_active = h->s.n_active;
+  ra.act_exp = h->s.act_exp;
+  ra.act_cnt = h->s.act_cnt;
+  ra.act_off = h->s.act_off;
+  ra.pair_tok = h->s.pair_tok;
+  ra.pair_w = h->s.pair_w;
+  ra.counter = h->s.counters + 1;
+  ra.B = B;
+  ra.H = c.hidden;
+  ra.E = c.n_experts;
+  ra.K = c.top_k;
+  ProfScope p2{h, 2, st};
+  HIP_TRY(h, p2.begin());
+  HIP_TRY(h, launch_router(ra, st));
+  HIP_TRY(h, p2.end());
+
+  GateUpArgs ga{};
+  ga.w1 = (const uint16_t *)h->w.w1;
+  ga.w3 = (const uint16_t *)h->w.w3;
+  ga.hg = h->s.hg;
+  ga.inv_rms = h->s.inv_rms;
+  ga.act = h->s.act;
+  ga.n_active = h->s.n_active;
+  ga.act_exp = h->s.act_exp;
+  ga.act_cnt = h->s.act_cnt;
+  ga.act_off = h->s.act_off;
+  ga.pair_tok = h->s.pair_tok;
+  ga.B = B;
+  ga.H = c.hidden;
+  ga.F = c.expert_ffn;
+  ga.shared = 0;
+  {
+    int max_active = B * c.top_k < c.n_experts ? B * c.top_k : c.n_experts;
+    long items = (long)max_active * (c.expert_ffn / kGateRowsPerBlock);
+    int grid = (int)(items < 2048 ? items : 2048);
+    ProfScope p3{h, 3, st};
+    HIP_TRY(h, p3.begin());
+    HIP_TRY(h, launch_gateup(ga, grid, st));
+    HIP_TRY(h, p3.end());
+  }
+
+  if (c.shared_ffn > 0) HIP_TRY(h, hipStreamWaitEvent(st, h->ev_join, 0));
+
+  DownArgs da{};
+  da.w2 = (const uint16_t *)h->w.w2;
+  da.s2 = (const uint16_t *)h->w.s2;
+  da.act = h->s.act;
+  da.act_s = h->s.act_s;
+  da.pair_w = h->s.pair_w;
+  da.n_active = h->s.n_active;
+  da.act_exp = h->s.act_exp;
+  da.act_cnt = h->s.act_cnt;
+  da.act_off = h->s.act_off;
+  da.pair_tok = h->s.pair_tok;
+  da.y = io->moe_out;
+  da.B = B;
+  da.H = c.hidden;
+  da.F = c.expert_ffn;
+  da.Fs = c.shared_ffn;
+  ProfScope p4{h, 4, st};
+  HIP_TRY(h, p4.begin());
+  HIP_TRY(h, launch_down(da, st));
+  HIP_TRY(h, p4.end());
+  if (h->profiling) h->profiled_step = true;
+  return DL_OK;
+}
+
+int decode_layer_set_profiling(decode_layer *h, int enable) {
+  if (!h) return fail(nullptr, DL_ERR_INVALID_ARG, "handle is NULL");
+  HIP_TRY(h, hipSetDevice(h->device));
+  if (enable && !h->ev_prof[0][0]) {
+    for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i)
+      for (int j = 0; j < 2; ++j) HIP_TRY(h, hipEventCreate(&h->ev_prof[i][j]));
+  }
+  h->profiling = enable != 0;
+  h->profiled_step = false;
+  return DL_OK;
+}
+
+int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity) {
+  if (!h || !ms || capacity < 0) return fail(h, DL_ERR_INVALID_ARG, "NULL handle or output");
+  if (!h->profiling || !h->profiled_step) return fail(h, DL_ERR_INVALID_ARG, "no profiled step to report");
+  HIP_TRY(h, hipSetDevice(h->device));
+  int n = capacity < DECODE_LAYER_N_LAUNCHES ? capacity : DECODE_LAYER_N_LAUNCHES;
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.f;
+    if (!h->launched[i]) continue;
+    HIP_TRY(h, hipEventSynchronize(h->ev_prof[i][1]));
+    HIP_TRY(h, hipEventElapsedTime(&ms[i], h->ev_prof[i][0], h->ev_prof[i][1]));
+  }
+  return n;
+}
+
+int decode_layer_destroy(decode_layer *h) {
+  if (!h) return DL_OK;
+  (void)hipSetDevice(h->device);
+  if (h->side) (void)hipStreamSynchronize(h->side);
+  for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i)
+    for (int j = 0; j < 2; ++j)
+      if (h->ev_prof[i][j]) (void)hipEventDestroy(h->ev_prof[i][j]);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->scratch_base) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->scratch_base);
+  }
+  delete h;
+  return DL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+/*
+ * decode_layer.h - C ABI of an MI355X (gfx950) library that runs one decode
+ * step of a mixture-of-experts transformer layer, for 1..64 tokens, on one
+ * GPU's tensor-parallel shard.
+ *
+ * The step is the one the vLLM "latency_specialized" decode backend for
+ * Kimi K3 specialises (bigchange.ai "Kimi K3 vLLM GPU inference benchmark",
+ * section "Where the time was going"; wireai.ir "vLLM's speed jump on NVIDIA
+ * Blackwell servers; record 842 tokens/s for Kimi K3", section "Four key
+ * changes behind the jump"):
+ *   1. attention input projection          qkv = x Wqkv^T
+ *   2. attention output projection, fused with the residual add and RMSNorm
+ *                                          r1 = r + attn Wo^T
+ *                                          h  = g * r1 / sqrt(mean(r1^2) + eps)
+ *   3. router scores and top-k selection   l = h Wr^T, s = sigmoid(l),
+ *                                          idx = top-k of s, w = s_idx / sum s_idx
+ *   4. routed SwiGLU experts and the always-on shared expert
+ *        y[t] = FFN_shared(h[t]) + sum_j w[t,j] FFN_{idx[t,j]}(h[t]),
+ *        FFN(v) = W2 (silu(W1 v) * (W3 v)).
+ * On one shard the cross-GPU reductions that the pages fuse into the
+ * out-projection and the MoE tail are the identity: the residual adds this
+ * shard's projection, and y is returned as this shard's partial sum (it is
+ * NOT added to the residual).
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major [out][in]: row j holds the weights of output j,
+ *     and the input dimension is contiguous.
+ *   - bf16 means IEEE bfloat16 bit patterns (uint16 storage).
+ *   - All device pointers must be 16-byte aligned.
+ *   - No exception crosses the ABI.  Functions return DL_OK (0) or a negative
+ *     DL_ERR_* code; decode_layer_last_error() then describes the failure.
+ *   - Argument and configuration errors are detected on the host before any
+ *     HIP call is made.  Configurations outside the supported envelope return
+ *     DL_ERR_UNSUPPORTED, so a caller can fall back to a generic path (the
+ *     pages' backend is opt-in and falls back for unsupported steps:
+ *     bigchange.ai, opening section; wireai.ir, "Conditions and limits for
+ *     production deployment").
+ */
+#ifndef DECODE_LAYER_H
+#define DECODE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DL_OK = 0,
+  DL_ERR_INVALID_ARG = -1, /* NULL or misaligned pointer, negative size        */
+  DL_ERR_UNSUPPORTED = -2, /* shape or option outside the supported envelope   */
+  DL_ERR_HIP = -3,         /* a HIP runtime call failed (no device, launch ...) */
+  DL_ERR_OOM = -4          /* device allocation of the handle's scratch failed  */
+};
+
+/* Shapes and options, fixed when the handle is created.
+ * Supported envelope (anything else -> DL_ERR_UNSUPPORTED):
+ *   hidden H      : 8..16384, multiple of 8
+ *   qkv_out Dq    : 1..65536
+ *   attn_dim Do   : 8..16384, multiple of 8
+ *   n_experts E   : 1..1024
+ *   top_k k       : 1..min(E, 32)
+ *   expert_ffn F  : 32, 64, 128 or 256
+ *   shared_ffn Fs : 0 (no shared expert) or 32, 64, 128 or 256
+ *   max_batch     : 1..64
+ *   rms_eps       : > 0 and finite
+ *   score_fn      : 0 = sigmoid (the only value supported)
+ *   renormalize   : 1 = top-k weights divided by their sum (the only value supported)
+ */
+typedef struct {
+  int32_t hidden;
+  int32_t qkv_out;
+  int32_t attn_dim;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t expert_ffn;
+  int32_t shared_ffn;
+  int32_t max_batch;
+  float rms_eps;
+  int32_t score_fn;
+  int32_t renormalize;
+} decode_layer_config;
+
+/* Weights of one layer shard: device pointers owned by the caller.  They
+ * must stay allocated and unchanged while the handle is in use; the library
+ * never writes them and keeps no copy. */
+typedef struct {
+  const void *w_qkv;     /* bf16 [Dq][H]                    */
+  const void *w_o;       /* bf16 [H][Do]                    */
+  const void *norm_gain; /* bf16 [H]                        */
+  const float *w_router; /* fp32 [E][H]                     */
+  const void *w1;        /* bf16 [E][F][H]  expert gate      */
+  const void *w3;        /* bf16 [E][F][H]  expert up        */
+  const void *w2;        /* bf16 [E][H][F]  expert down      */
+  const void *s1;        /* bf16 [Fs][H]    shared gate (NULL iff Fs == 0) */
+  const void *s3;        /* bf16 [Fs][H]    shared up        */
+  const void *s2;        /* bf16 [H][Fs]    shared down      */
+} decode_layer_weights;
+
+/* Per-step tensors: device pointers owned by the caller, valid until the
+ * work enqueued by decode_layer_step has completed on its stream. */
+typedef struct {
+  int32_t batch;          /* B tokens, 0..max_batch; 0 is a no-op          */
+  const void *x;          /* bf16 [B][H]  attention input                   */
+  const void *attn;       /* bf16 [B][Do] attention-core output             */
+  const float *resid_in;  /* fp32 [B][H]  residual stream                   */
+  float *qkv;             /* out fp32 [B][Dq]                               */
+  float *resid_out;       /* out fp32 [B][H]  r + attn Wo^T; may equal resid_in */
+  float *router_logits;   /* out fp32 [B][E]; may be NULL                   */
+  int32_t *topk_idx;      /* out int32 [B][k], descending score, ties to the lower id */
+  float *topk_w;          /* out fp32 [B][k], sums to 1 per token          */
+  float *moe_out;         /* out fp32 [B][H]  shard-partial MoE output y    */
+  float *h_out;           /* out fp32 [B][H]  normalised hidden h; may be NULL */
+} decode_layer_io;
+
+typedef struct decode_layer decode_layer; /* opaque handle */
+
+/* Validate `cfg` and `w`, then create a handle on HIP device `device`:
+ * allocates the handle's device scratch (a few MB at most), a second HIP
+ * stream for the shared expert and the events that fork and join it.
+ * No kernel runs.  On success *out receives the handle; on failure *out is
+ * set to NULL.  Errors: DL_ERR_INVALID_ARG (NULL pointers, misaligned
+ * weights), DL_ERR_UNSUPPORTED (shape outside the envelope), DL_ERR_HIP
+ * (no such device), DL_ERR_OOM. */
+int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights *w,
+                      int device, decode_layer **out);
+
+/* Enqueue one layer-step on `hip_stream` (a hipStream_t; NULL = the null
+ * stream) and return without synchronising.  Device work: up to five kernel
+ * launches, four on `hip_stream` and one (the shared expert's gate/up
+ * projection) on the handle's second stream, which is forked from and joined
+ * back into `hip_stream` with events, so the call can be captured in a HIP
+ * graph.  No allocation, no host copy, no memset.
+ * `io` is validated on the host first (DL_ERR_INVALID_ARG /
+ * DL_ERR_UNSUPPORTED, nothing enqueued).  A failed launch returns DL_ERR_HIP;
+ * faults inside kernels surface at the caller's next synchronisation.
+ * One step per handle may be in flight at a time (the scratch is per
+ * handle); distinct handles may run concurrently. */
+int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stream);
+
+/* Wait for the handle's streams, free its scratch, stream and events. NULL is a no-op. */
+int decode_layer_destroy(decode_layer *h);
+
+/* Host-only check of a configuration (the validation decode_layer_init does
+ * before touching the GPU).  Returns DL_OK, DL_ERR_INVALID_ARG or DL_ERR_UNSUPPORTED. */
+int decode_layer_check_config(const decode_layer_config *cfg);
+
+/* Host-only check of one step's arguments against a configuration (the
+ * validation decode_layer_step does before enqueuing anything). */
+int decode_layer_check_io(const decode_layer_config *cfg, const decode_layer_io *io);
+
+/* Text of the last error on `h`, or of the calling thread's last error when
+ * `h` is NULL (e.g. a failed decode_layer_init).  Never NULL; the string is
+ * owned by the library and valid until the next call on the same handle or thread. */
+const char *decode_layer_last_error(const decode_layer *h);
+
+/* Measurement support, not needed for normal use.  While profiling is
+ * enabled on a handle, every decode_layer_step also records a HIP event pair
+ * around each of its kernel launches, on the stream that launch uses.
+ * decode_layer_kernel_times() waits for the last step's events and writes
+ * the launches' durations in milliseconds, in the fixed order
+ *   0 out-projection + input projection, 1 shared expert gate/up,
+ *   2 router + top-k + permute, 3 routed expert gate/up, 4 expert down + combine
+ * (0 for a launch the configuration does not make).  It returns the number of
+ * entries written (<= capacity) or a negative DL_ERR_* code (DL_ERR_INVALID_ARG
+ * if profiling is off or no step ran since it was enabled).  Enabling creates
+ * the events (DL_ERR_HIP on failure); do not enable it while capturing a graph. */
+#define DECODE_LAYER_N_LAUNCHES 5
+int decode_layer_set_profiling(decode_layer *h, int enable);
+int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
+
+/* Bytes of device scratch a handle with this configuration allocates
+ * (0 if the configuration is invalid). */
+size_t decode_layer_scratch_bytes(const decode_layer_config *cfg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_LAYER_H */

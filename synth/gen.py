@@ -105,16 +105,21 @@ class RawLayer:
         self._expert_cache.clear()
 
 
-def draw(cfg: int, seed: int | None = None, batch: int | None = None) -> RawLayer:
+def draw(cfg: int, seed: int | None = None, batch: int | None = None,
+         top_k: int | None = None, shared_ffn: int | None = None) -> RawLayer:
     """Draw every tensor of workload `cfg` (default seed = cfg).
 
-    `batch` overrides the token count (edge-case tests); activations for a
-    smaller batch are the leading rows of the full draw.
+    `batch`, `top_k` and `shared_ffn` override the workload's values (edge-case
+    tests); activations for a smaller batch are the leading rows of the full
+    draw, and every other tensor is drawn exactly as for the workload.
     """
     s = SHAPES[cfg]
-    if batch is not None:
-        s = LayerShape(s.name + f"_b{batch}", s.hidden, batch, s.qkv_out, s.attn_dim,
-                       s.n_experts, s.top_k, s.expert_ffn, s.shared_ffn, s.routing)
+    if batch is not None or top_k is not None or shared_ffn is not None:
+        b = s.batch if batch is None else batch
+        k = s.top_k if top_k is None else top_k
+        fs = s.shared_ffn if shared_ffn is None else shared_ffn
+        s = LayerShape(s.name + f"_b{b}_k{k}_fs{fs}", s.hidden, b, s.qkv_out, s.attn_dim,
+                       s.n_experts, k, s.expert_ffn, fs, s.routing)
     if seed is None:
         seed = cfg
     H, B = s.hidden, s.batch

@@ -1,0 +1,122 @@
+"""The C ABI on the host (CPU only, no GPU calls that compute).
+
+* the built library loads and exports every function include/decode_layer.h declares;
+* configuration and step-argument validation return the documented codes and
+  a non-empty error text, before any HIP call;
+* decode_layer_init on a machine without a GPU fails cleanly with DL_ERR_HIP.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_step_moe_amd as dl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "decode_layer.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(decode_layer_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert "decode_layer_init" in names and "decode_layer_step" in names
+    lib = ctypes.CDLL(dl.binding.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def good():
+    return dl.make_config(7168, 512, 512, 384, 8, 128, 128, 64)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("hidden", 7170, dl.DL_ERR_UNSUPPORTED), ("hidden", 0, dl.DL_ERR_UNSUPPORTED),
+    ("attn_dim", 12, dl.DL_ERR_UNSUPPORTED), ("qkv_out", 0, dl.DL_ERR_UNSUPPORTED),
+    ("n_experts", 2000, dl.DL_ERR_UNSUPPORTED), ("top_k", 0, dl.DL_ERR_UNSUPPORTED),
+    ("top_k", 33, dl.DL_ERR_UNSUPPORTED), ("expert_ffn", 100, dl.DL_ERR_UNSUPPORTED),
+    ("expert_ffn", 512, dl.DL_ERR_UNSUPPORTED), ("shared_ffn", 96, dl.DL_ERR_UNSUPPORTED),
+    ("max_batch", 65, dl.DL_ERR_UNSUPPORTED), ("max_batch", 0, dl.DL_ERR_UNSUPPORTED),
+    ("rms_eps", 0.0, dl.DL_ERR_UNSUPPORTED), ("rms_eps", float("inf"), dl.DL_ERR_UNSUPPORTED),
+    ("score_fn", 1, dl.DL_ERR_UNSUPPORTED), ("renormalize", 0, dl.DL_ERR_UNSUPPORTED),
+])
+def test_config_validation(field, value, code):
+    c = good()
+    assert dl.check_config(c) == dl.DL_OK
+    setattr(c, field, value)
+    assert dl.check_config(c) == code
+    assert field.split("_")[0] in dl.last_error() or len(dl.last_error()) > 10
+    assert dl.scratch_bytes(c) == 0
+
+
+def test_top_k_above_experts_is_unsupported():
+    c = dl.make_config(512, 768, 768, 8, 9, 256, 256, 1)
+    assert dl.check_config(c) == dl.DL_ERR_UNSUPPORTED
+
+
+def test_shared_expert_optional_and_scratch_size():
+    c = dl.make_config(512, 768, 768, 8, 2, 256, 0, 1)
+    assert dl.check_config(c) == dl.DL_OK
+    assert dl.scratch_bytes(good()) > 0
+
+
+def _io(batch=1, **kw):
+    ptrs = dict(x=0x1000, attn=0x2000, resid_in=0x3000, qkv=0x4000, resid_out=0x100000,
+                router_logits=None, topk_idx=0x5000, topk_w=0x6000, moe_out=0x200000, h_out=None)
+    ptrs.update(kw)
+    return dl.IO(batch, *[ptrs[n] for n in ("x", "attn", "resid_in", "qkv", "resid_out",
+                                             "router_logits", "topk_idx", "topk_w", "moe_out",
+                                             "h_out")])
+
+
+def test_io_validation():
+    c = good()
+    assert dl.check_io(c, _io()) == dl.DL_OK
+    assert dl.check_io(c, _io(batch=0, x=None)) == dl.DL_OK          # no-op
+    assert dl.check_io(c, _io(batch=-1)) == dl.DL_ERR_INVALID_ARG
+    assert dl.check_io(c, _io(batch=65)) == dl.DL_ERR_UNSUPPORTED
+    assert dl.check_io(c, _io(x=None)) == dl.DL_ERR_INVALID_ARG
+    assert "io.x" in dl.last_error()
+    assert dl.check_io(c, _io(moe_out=0x200004)) == dl.DL_ERR_INVALID_ARG   # misaligned
+    assert dl.check_io(c, _io(router_logits=0x7008)) == dl.DL_ERR_INVALID_ARG
+    assert dl.check_io(c, _io(resid_out=0x3000)) == dl.DL_OK                # exact alias allowed
+    assert dl.check_io(c, _io(resid_out=0x3010)) == dl.DL_ERR_INVALID_ARG   # partial overlap
+
+
+def test_init_rejects_bad_arguments_before_touching_the_gpu():
+    lib = dl.lib()
+    out = ctypes.c_void_p(123)
+    w = dl.Weights(*([0x1000] * 10))
+    bad = good()
+    bad.top_k = 0
+    rc = lib.decode_layer_init(ctypes.byref(bad), ctypes.byref(w), 0, ctypes.byref(out))
+    assert rc == dl.DL_ERR_UNSUPPORTED and not out.value
+    w_null = dl.Weights(*([0x1000] * 3 + [None] + [0x1000] * 6))
+    rc = lib.decode_layer_init(ctypes.byref(good()), ctypes.byref(w_null), 0, ctypes.byref(out))
+    assert rc == dl.DL_ERR_INVALID_ARG and "w_router" in dl.last_error()
+    w_mis = dl.Weights(*([0x1000] * 4 + [0x1002] + [0x1000] * 5))
+    rc = lib.decode_layer_init(ctypes.byref(good()), ctypes.byref(w_mis), 0, ctypes.byref(out))
+    assert rc == dl.DL_ERR_INVALID_ARG and "aligned" in dl.last_error()
+
+
+def test_step_and_destroy_null_handle():
+    lib = dl.lib()
+    assert lib.decode_layer_step(None, ctypes.byref(_io()), None) == dl.DL_ERR_INVALID_ARG
+    assert lib.decode_layer_destroy(None) == dl.DL_OK
+    assert lib.decode_layer_set_profiling(None, 1) == dl.DL_ERR_INVALID_ARG
+
+
+def test_init_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = dl.lib()
+    out = ctypes.c_void_p()
+    w = dl.Weights(*([0x1000] * 10))
+    rc = lib.decode_layer_init(ctypes.byref(good()), ctypes.byref(w), 0, ctypes.byref(out))
+    assert rc == dl.DL_ERR_HIP and not out.value
+    assert len(dl.last_error()) > 0

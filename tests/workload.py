@@ -13,8 +13,9 @@ def oracle_h(raw) -> np.ndarray:
     return ref.rms_norm(r1, raw.gain)[0]
 
 
-def build(cfg: int, seed=None, batch=None, h_source: str = "oracle") -> routing.RoutedLayer:
-    raw = gen.draw(cfg, seed, batch)
+def build(cfg: int, seed=None, batch=None, h_source: str = "oracle", top_k=None,
+          shared_ffn=None) -> routing.RoutedLayer:
+    raw = gen.draw(cfg, seed, batch, top_k=top_k, shared_ffn=shared_ffn)
     h = routing.stored_h(cfg) if h_source == "stored" else oracle_h(raw)
     return routing.shape_router(raw, h)
 
