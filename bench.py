@@ -68,6 +68,7 @@ def algorithmic_bytes(layer) -> dict:
     weights = 2 * (Dq * H + H * Do + H) + 4 * E * H + n_act * 3 * 2 * F * H + 3 * 2 * Fs * H
     io = 2 * B * (H + Do) + 4 * B * H * 2 + 4 * B * Dq + 4 * B * E + 8 * pairs + 4 * B * H
     b["step"] = weights + io
+    b["single_launch_step"] = b["step"]
     b["step_flops"] = 2 * B * (Dq * H + H * Do + E * H) + 2 * pairs * 3 * F * H + 2 * B * 3 * Fs * H
     return b
 
@@ -94,7 +95,7 @@ def make_copies(layer, n_copies):
     return copies
 
 
-def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True):
+def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True, path=0):
     import torch
     from decode_step_moe_amd import DecodeLayer
     from synth import device as sdev, routing, gen
@@ -107,8 +108,9 @@ def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True):
     log(f"[bench] cfg {cfg_id} {layer.shape.name}: {len(layer.touched_experts())} experts, "
         f"{nbytes['step'] / 1e6:.2f} MB/step, {n_copies} copies")
     copies = make_copies(layer, n_copies)
-    cfg = sdev.config_of(layer)
+    cfg = sdev.config_of(layer, path=path)
     handles = [DecodeLayer(cfg, w) for w in copies]
+    single = path != 1 and layer.shape.batch <= handles[0].single_max_batch
     x, attn, resid = sdev.upload_inputs(layer)
     outs = [h.alloc_outputs(layer.shape.batch) for h in handles]
     ios = [h.make_io(x, attn, resid, o) for h, o in zip(handles, outs)]
@@ -138,21 +140,32 @@ def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True):
         return t0.elapsed_time(t1) / steps
 
     eager_ms = timed(run)
-    # one graph per copy
-    graphs = []
+    # one graph holding one step of every copy (as a decode step holds every
+    # layer), replayed until at least `steps` steps have run
     side = torch.cuda.Stream()
-    for i in range(n_copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(n_copies):
             handles[i].step_io(ios[i], side)
-        graphs.append(g)
     torch.cuda.synchronize()
-    graph_ms = timed(lambda i: graphs[i % n_copies].replay())
+    reps = max(1, -(-steps // n_copies))
+    for _ in range(max(1, warmup // n_copies)):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = t0.elapsed_time(t1) / (reps * n_copies)
     # graph results equal eager results
     ref = outs[0].moe_out.clone()
-    graphs[0].replay()
+    g.replay()
     torch.cuda.synchronize()
     assert torch.equal(outs[0].moe_out, ref)
+    del g
 
     kern = {}
     if want_kernels:
@@ -169,11 +182,14 @@ def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True):
         for h in handles:
             h.set_profiling(False)
         kern = {k_: float(np.mean(v)) for k_, v in acc.items()}
+    for h in handles:
+        assert h.status() == 0, "a single-launch hand-off wait expired"
     res = {"cfg": cfg_id, "workload": layer.shape.name, "batch": layer.shape.batch,
            "copies": n_copies, "eager_us": eager_ms * 1e3, "graph_us": graph_ms * 1e3,
            "bytes": nbytes, "kernel_us": {k_: v * 1e3 for k_, v in kern.items()},
-           "active_experts": int(len(layer.touched_experts()))}
-    del graphs, handles, copies
+           "active_experts": int(len(layer.touched_experts())),
+           "path": "single" if single else "multi", "launches": 1 if single else 5}
+    del handles, copies
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res, layer
@@ -238,6 +254,8 @@ def main():
     import decode_step_moe_amd  # noqa: F401  (fails loudly without the built library)
 
     head, layer = time_config(HEADLINE_CFG, args.steps, args.warmup, args.copies)
+    multi, _ = time_config(HEADLINE_CFG, args.steps, args.warmup, args.copies, want_kernels=False,
+                           path=1)
     batches = {}
     if not args.no_batches:
         for c in BATCH_CFGS:
@@ -263,13 +281,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": head["workload"], "hidden": 7168, "batch": 1, "qkv_out": 512,
                    "attn_dim": 512, "n_experts": 384, "top_k": 8, "expert_ffn": 128,
-                   "shared_ffn": 128, "routing": "uniform-random", "timing": "hip-graph replay",
+                   "shared_ffn": 128, "routing": "uniform-random", "timing": "hip-graph replay, one step of each rotated copy per graph",
                    "copies_rotated": head["copies"]},
         "hbm_gbps": round(b["step"] / (us * 1e-6) / 1e9, 1),
         "hbm_frac": round(b["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "tok_per_s_per_shard": round(1 / (us * 1e-6), 1),
         "eager_us": round(head["eager_us"], 3),
-        "launches_per_step": 5,
+        "launches_per_step": head["launches"],
+        "path": head["path"],
+        "multi_launch_path": {"graph_us": round(multi["graph_us"], 3),
+                              "eager_us": round(multi["eager_us"], 3), "launches_per_step": 5},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": b[dom],
@@ -289,6 +310,7 @@ def _summary(r):
             "hbm_frac": round(r["bytes"]["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "tok_per_s_per_shard": round(r["batch"] / (us * 1e-6), 1),
             "active_experts": r["active_experts"], "copies": r["copies"],
+            "path": r["path"], "launches_per_step": r["launches"],
             "kernels_us": {k_: round(v, 3) for k_, v in r["kernel_us"].items()}}
 
 

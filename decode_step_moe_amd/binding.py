@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdecode_layer.so")
 
 DL_OK, DL_ERR_INVALID_ARG, DL_ERR_UNSUPPORTED, DL_ERR_HIP, DL_ERR_OOM = 0, -1, -2, -3, -4
+DL_PATH_AUTO, DL_PATH_MULTI, DL_PATH_SINGLE = 0, 1, 2
 _ERR_NAMES = {0: "DL_OK", -1: "DL_ERR_INVALID_ARG", -2: "DL_ERR_UNSUPPORTED", -3: "DL_ERR_HIP",
               -4: "DL_ERR_OOM"}
 
@@ -31,7 +32,7 @@ class Config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
                 ("shared_ffn", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("score_fn", ctypes.c_int32),
-                ("renormalize", ctypes.c_int32)]
+                ("renormalize", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -74,8 +75,19 @@ def lib() -> ctypes.CDLL:
         L.decode_layer_kernel_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
                                                 ctypes.c_int]
         L.decode_layer_kernel_times.restype = ctypes.c_int
-        L.decode_layer_scratch_bytes.argtypes = [ctypes.POINTER(Config)]
+        L.decode_layer_scratch_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int]
         L.decode_layer_scratch_bytes.restype = ctypes.c_size_t
+        L.decode_layer_single_max_batch.argtypes = [ctypes.c_void_p]
+        L.decode_layer_single_max_batch.restype = ctypes.c_int
+        L.decode_layer_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32),
+                                          ctypes.c_int]
+        L.decode_layer_status.restype = ctypes.c_int
+        L.decode_layer_set_trace.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.decode_layer_set_trace.restype = ctypes.c_int
+        L.decode_layer_trace_points.argtypes = []
+        L.decode_layer_trace_points.restype = ctypes.c_int
+        L.decode_layer_grid.argtypes = [ctypes.c_void_p]
+        L.decode_layer_grid.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -85,9 +97,9 @@ def last_error(handle=None) -> str:
 
 
 def make_config(hidden, qkv_out, attn_dim, n_experts, top_k, expert_ffn, shared_ffn, max_batch,
-                rms_eps=1e-6, score_fn=0, renormalize=1) -> Config:
+                rms_eps=1e-6, score_fn=0, renormalize=1, path=DL_PATH_AUTO) -> Config:
     return Config(hidden, qkv_out, attn_dim, n_experts, top_k, expert_ffn, shared_ffn, max_batch,
-                  rms_eps, score_fn, renormalize)
+                  rms_eps, score_fn, renormalize, path)
 
 
 def check_config(cfg: Config) -> int:
@@ -98,8 +110,8 @@ def check_io(cfg: Config, io: IO) -> int:
     return lib().decode_layer_check_io(ctypes.byref(cfg), ctypes.byref(io))
 
 
-def scratch_bytes(cfg: Config) -> int:
-    return lib().decode_layer_scratch_bytes(ctypes.byref(cfg))
+def scratch_bytes(cfg: Config, n_cu: int = 0) -> int:
+    return lib().decode_layer_scratch_bytes(ctypes.byref(cfg), n_cu)
 
 
 def _ptr(t, dtype, shape, name):
@@ -170,7 +182,39 @@ class DecodeLayer:
             pass
 
     LAUNCH_NAMES = ("proj_out_in", "shared_gateup", "router_topk_permute", "expert_gateup",
-                    "expert_down_combine")
+                    "expert_down_combine", "single_launch_step")
+
+    @property
+    def single_max_batch(self) -> int:
+        """Largest batch the single-launch path takes with this handle (0: none)."""
+        return lib().decode_layer_single_max_batch(self._h)
+
+    def set_trace(self, buf):
+        """Phase trace of the single-launch kernel into a uint64 GPU tensor of
+        [grid][trace_points] (None: off)."""
+        import torch
+        ptr = None
+        if buf is not None:
+            n = lib().decode_layer_grid(self._h) * lib().decode_layer_trace_points()
+            if buf.dtype != torch.int64 or buf.numel() < n or not buf.is_cuda or not buf.is_contiguous():
+                raise ValueError(f"trace buffer: need a contiguous int64 GPU tensor of >= {n} values")
+            ptr = buf.data_ptr()
+        rc = lib().decode_layer_set_trace(self._h, ptr)
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error(self._h))
+
+    @property
+    def grid(self) -> int:
+        return lib().decode_layer_grid(self._h)
+
+    def status(self, clear: bool = False) -> int:
+        """Device status word (synchronise first): bit 0 a hand-off wait expired,
+        bit 1 the step counter is exhausted."""
+        v = ctypes.c_uint32()
+        rc = lib().decode_layer_status(self._h, ctypes.byref(v), int(clear))
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error(self._h))
+        return int(v.value)
 
     def set_profiling(self, enable: bool):
         rc = lib().decode_layer_set_profiling(self._h, int(enable))
@@ -183,7 +227,7 @@ class DecodeLayer:
         n = lib().decode_layer_kernel_times(self._h, buf, len(buf))
         if n < 0:
             raise DecodeLayerError(n, last_error(self._h))
-        return {name: float(buf[i]) for i, name in enumerate(self.LAUNCH_NAMES[:n])}
+        return {name: float(buf[i]) for i, name in enumerate(self.LAUNCH_NAMES[:n]) if buf[i] > 0}
 
     def alloc_outputs(self, batch: int, device="cuda", with_h: bool = False,
                       with_logits: bool = True) -> StepOutputs:

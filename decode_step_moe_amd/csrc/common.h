@@ -38,15 +38,47 @@ __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ float4 ld16f(const void *p) { return *reinterpret_cast<const float4 *>(p); }
 
 // ---- wave reductions -------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// DPP lane permutes inside rows of 16 lanes, then readlane across the 4 rows:
+// VALU and scalar work only (no LDS-routed shuffle on the dependent chain).
+// Every lane of a row adds the same two operands at each step (only their
+// order differs, and fp addition is commutative), so all lanes agree bit for
+// bit and the result does not depend on the lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each half-row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each row
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  v += dpp_mov<kDppMirror>(v);
   return v;
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+// Sum over the wave, returned (uniform) in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64),
+// returned in every lane of the group.
 __device__ __forceinline__ float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if (width >= 2) v += dpp_mov<kDppXor1>(v);
+  if (width >= 4) v += dpp_mov<kDppXor2>(v);
+  if (width >= 8) v += dpp_mov<kDppHalfMirror>(v);
+  if (width >= 16) v += dpp_mov<kDppMirror>(v);
+  if (width >= 32) v += __shfl_xor(v, 16, kWave);
+  if (width >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
 }
 

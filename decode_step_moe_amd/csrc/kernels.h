@@ -22,6 +22,45 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxBatch = 64;
 
+// Single-launch path (fused.hip): one 512-thread workgroup per CU, all
+// resident at once.  Limits of its LDS layout.
+constexpr int kFusedThreads = 512;
+constexpr int kFusedMaxB = 8;         // tokens
+constexpr int kFusedMaxSlice = 32;    // rows of H per workgroup
+constexpr int kFusedMaxPairs = 64;    // B * k
+constexpr int kFusedBig = 8192;       // B * E logits, then B * k * F activations
+constexpr int kFusedActS = 4096;      // B * Fs shared activations
+constexpr int kFusedMaxH = 8192;      // router / shared rows held in registers
+constexpr int kFusedMaxE = 512;       // at most 2 router rows per workgroup (with 256 CUs)
+
+struct FusedArgs {
+  const uint16_t *x, *w_qkv;
+  float *qkv;
+  const uint16_t *attn, *w_o, *gain;
+  const float *resid_in;
+  float *resid_out;
+  const float *w_router;
+  float *logits_out;
+  int32_t *topk_idx;
+  float *topk_w;
+  const uint16_t *w1, *w3, *w2, *s1, *s3, *s2;
+  float *moe_out, *h_out;
+  // scratch: gained residual and the tagged hand-off arrays
+  float *hg;          // [B][H]
+  uint64_t *pss;      // [G][B]     partial sums of r1^2
+  uint64_t *logit;    // [B][E]
+  uint64_t *act;      // [B*k][F]   routed SwiGLU activations, pairs grouped by expert
+  uint64_t *act_s;    // [B][Fs]    shared SwiGLU activations
+  unsigned *epoch;    // steps completed on this handle
+  unsigned *status;   // bit 0: a hand-off wait expired; bit 1: step counter exhausted
+  int B, H, Dq, Do, E, K, F, Fs;
+  int slice;          // rows of H per workgroup, a multiple of 4
+  float eps;
+  int spin_limit;
+  uint64_t *trace;    // optional [G][kTracePoints] wall-clock stamps (nullptr: off)
+};
+constexpr int kTracePoints = 16;
+
 struct ProjArgs {
   const uint16_t *x, *w_qkv;
   float *qkv;
@@ -66,5 +105,8 @@ hipError_t launch_proj(const ProjArgs &a, hipStream_t s);
 hipError_t launch_router(const RouterArgs &a, hipStream_t s);
 hipError_t launch_gateup(const GateUpArgs &a, int grid, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, hipStream_t s);
+hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s);
+// Resident workgroups of the single-launch kernel per CU (0 if it cannot run).
+int fused_blocks_per_cu();
 
 }  // namespace dl

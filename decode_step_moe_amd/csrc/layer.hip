@@ -20,6 +20,38 @@ namespace {
 
 thread_local std::string g_thread_err = "no error";
 
+// Single-launch path: grid size and the largest batch its LDS layout allows.
+struct SinglePlan {
+  int grid = 0;       // workgroups = CUs
+  int slice = 0;      // rows of H per workgroup
+  int max_batch = 0;  // 0: path unavailable
+};
+
+int single_max_batch_for(const decode_layer_config &c, int grid, int slice) {
+  if (grid < 1 || grid > kFusedThreads || slice > kFusedMaxSlice) return 0;
+  // router rows (<= 2 per workgroup) and shared rows (<= 1) are held in registers
+  if (c.hidden > kFusedMaxH || c.n_experts > kFusedMaxE || c.n_experts > 2 * grid) return 0;
+  if (c.shared_ffn > grid || (c.shared_ffn != 0 && c.shared_ffn != c.expert_ffn)) return 0;
+  int best = 0;
+  for (int b = 1; b <= kFusedMaxB && b <= c.max_batch; ++b) {
+    if (b * c.top_k > kFusedMaxPairs || b * c.n_experts > kFusedBig ||
+        b * c.top_k * c.expert_ffn > kFusedBig || b * c.shared_ffn > kFusedActS)
+      break;
+    best = b;
+  }
+  return best;
+}
+
+SinglePlan plan_single(const decode_layer_config &c, int n_cu) {
+  SinglePlan p;
+  if (c.path == DL_PATH_MULTI || n_cu < 1) return p;
+  p.grid = n_cu;
+  int sl = (c.hidden + n_cu - 1) / n_cu;
+  p.slice = (sl + 3) & ~3;
+  p.max_batch = single_max_batch_for(c, p.grid, p.slice);
+  return p;
+}
+
 struct Scratch {
   float *hg = nullptr;        // [maxB][H]   g * r1
   float *ss_part = nullptr;   // [nblk_o][maxB]
@@ -34,28 +66,43 @@ struct Scratch {
   float *act = nullptr;       // [maxB*k][F]
   float *act_s = nullptr;     // [maxB][Fs]
   unsigned *counters = nullptr;  // [2]: out-projection, router
+  // single-launch hand-off arrays (tagged 64-bit values)
+  uint64_t *pss = nullptr, *logit = nullptr, *act64 = nullptr, *act_s64 = nullptr;
+  unsigned *epoch = nullptr;     // [1] steps completed
+  unsigned *status = nullptr;    // [1]
 };
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+constexpr int kNumBuf = 19;
 struct Layout {
-  size_t off[13];
+  size_t off[kNumBuf];
   size_t total;
 };
 
 int nblk_o_of(const decode_layer_config &c) { return (c.hidden + kORowsPerBlock - 1) / kORowsPerBlock; }
 
-Layout layout_of(const decode_layer_config &c) {
+Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
   const size_t B = c.max_batch, H = c.hidden, E = c.n_experts, K = c.top_k;
-  const size_t sizes[13] = {
+  const size_t Bs = sp.max_batch, G = sp.grid;
+  const size_t sizes[kNumBuf] = {
       B * H * 4, (size_t)nblk_o_of(c) * B * 4, B * 4, B * E * 4, B * K * 4, B * K * 4,
       E * 4, E * 4, E * 4, 4, B * K * (size_t)c.expert_ffn * 4, B * (size_t)(c.shared_ffn > 0 ? c.shared_ffn : 1) * 4,
-      2 * 4};
+      2 * 4,
+      // single-launch arrays (empty when the path is unavailable)
+      G * Bs * 8, Bs * E * 8, Bs * K * (size_t)c.expert_ffn * 8, Bs * (size_t)c.shared_ffn * 8,
+      4, 4};
   Layout L;
   size_t o = 0;
-  for (int i = 0; i < 13; ++i) { L.off[i] = o; o += align256(sizes[i]); }
+  for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
   L.total = o;
   return L;
+}
+
+int cu_count(int device) {
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+  return n;
 }
 
 bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -69,8 +116,10 @@ struct decode_layer {
   int device = 0;
   void *scratch_base = nullptr;
   Scratch s;
+  SinglePlan single;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  void *trace = nullptr;   // caller's device buffer for the phase trace
   bool profiling = false;
   bool profiled_step = false;
   hipEvent_t ev_prof[DECODE_LAYER_N_LAUNCHES][2] = {};
@@ -125,6 +174,8 @@ static int check_config(const decode_layer_config *c, decode_layer *h) {
   if (c->score_fn != 0) return fail(h, DL_ERR_UNSUPPORTED, "score_fn=%d: only 0 (sigmoid) is supported", c->score_fn);
   if (c->renormalize != 1)
     return fail(h, DL_ERR_UNSUPPORTED, "renormalize=%d: only 1 is supported", c->renormalize);
+  if (c->path != DL_PATH_AUTO && c->path != DL_PATH_MULTI && c->path != DL_PATH_SINGLE)
+    return fail(h, DL_ERR_UNSUPPORTED, "path=%d: need DL_PATH_AUTO, DL_PATH_MULTI or DL_PATH_SINGLE", c->path);
   return DL_OK;
 }
 
@@ -185,9 +236,9 @@ int decode_layer_check_io(const decode_layer_config *cfg, const decode_layer_io 
   return check_io(cfg, io, nullptr);
 }
 
-size_t decode_layer_scratch_bytes(const decode_layer_config *cfg) {
+size_t decode_layer_scratch_bytes(const decode_layer_config *cfg, int n_cu) {
   if (check_config(cfg, nullptr) != DL_OK) return 0;
-  return layout_of(*cfg).total;
+  return layout_of(*cfg, plan_single(*cfg, n_cu)).total;
 }
 
 const char *decode_layer_last_error(const decode_layer *h) {
@@ -217,7 +268,11 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
     return code;
   };
   if (hipSetDevice(device) != hipSuccess) return cleanup(fail(h, DL_ERR_HIP, "hipSetDevice(%d) failed", device));
-  Layout L = layout_of(*cfg);
+  h->single = plan_single(*cfg, cu_count(device));
+  if (h->single.max_batch > 0 && fused_blocks_per_cu() < 1) h->single = SinglePlan{};
+  if (cfg->path == DL_PATH_SINGLE && h->single.max_batch == 0)
+    return cleanup(fail(h, DL_ERR_UNSUPPORTED, "the single-launch path cannot run this configuration on this device"));
+  Layout L = layout_of(*cfg, h->single);
   if (hipMalloc(&h->scratch_base, L.total) != hipSuccess) {
     h->scratch_base = nullptr;
     return cleanup(fail(h, DL_ERR_OOM, "hipMalloc of %zu scratch bytes failed", L.total));
@@ -236,8 +291,15 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
   h->s.act = (float *)(b + L.off[10]);
   h->s.act_s = (float *)(b + L.off[11]);
   h->s.counters = (unsigned *)(b + L.off[12]);
+  h->s.pss = (uint64_t *)(b + L.off[13]);
+  h->s.logit = (uint64_t *)(b + L.off[14]);
+  h->s.act64 = (uint64_t *)(b + L.off[15]);
+  h->s.act_s64 = (uint64_t *)(b + L.off[16]);
+  h->s.epoch = (unsigned *)(b + L.off[17]);
+  h->s.status = (unsigned *)(b + L.off[18]);
   // The hand-off counters start at zero and are re-armed by the kernels
-  // themselves, so no step ever needs a memset.
+  // themselves, and the tagged hand-off values start with tag 0, which no
+  // step uses (tags are the step counter + 1), so no step ever needs a memset.
   if (hipMemset(h->scratch_base, 0, L.total) != hipSuccess) return cleanup(fail(h, DL_ERR_HIP, "hipMemset failed"));
   if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) {
     h->side = nullptr;
@@ -263,8 +325,61 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
   if (io->batch == 0) return DL_OK;
   const decode_layer_config &c = h->cfg;
   hipStream_t st = (hipStream_t)hip_stream;
-  HIP_TRY(h, hipSetDevice(h->device));
   const int B = io->batch;
+  const bool single = c.path != DL_PATH_MULTI && B <= h->single.max_batch;
+  if (c.path == DL_PATH_SINGLE && !single)
+    return fail(h, DL_ERR_UNSUPPORTED, "batch=%d exceeds the single-launch limit %d", B, h->single.max_batch);
+  HIP_TRY(h, hipSetDevice(h->device));
+  if (h->profiling)
+    for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i) h->launched[i] = false;
+  if (single) {
+    FusedArgs fa{};
+    fa.x = (const uint16_t *)io->x;
+    fa.w_qkv = (const uint16_t *)h->w.w_qkv;
+    fa.qkv = io->qkv;
+    fa.attn = (const uint16_t *)io->attn;
+    fa.w_o = (const uint16_t *)h->w.w_o;
+    fa.gain = (const uint16_t *)h->w.norm_gain;
+    fa.resid_in = io->resid_in;
+    fa.resid_out = io->resid_out;
+    fa.w_router = h->w.w_router;
+    fa.logits_out = io->router_logits;
+    fa.topk_idx = io->topk_idx;
+    fa.topk_w = io->topk_w;
+    fa.w1 = (const uint16_t *)h->w.w1;
+    fa.w3 = (const uint16_t *)h->w.w3;
+    fa.w2 = (const uint16_t *)h->w.w2;
+    fa.s1 = (const uint16_t *)h->w.s1;
+    fa.s3 = (const uint16_t *)h->w.s3;
+    fa.s2 = (const uint16_t *)h->w.s2;
+    fa.moe_out = io->moe_out;
+    fa.h_out = io->h_out;
+    fa.hg = h->s.hg;
+    fa.pss = h->s.pss;
+    fa.logit = h->s.logit;
+    fa.act = h->s.act64;
+    fa.act_s = h->s.act_s64;
+    fa.epoch = h->s.epoch;
+    fa.status = h->s.status;
+    fa.B = B;
+    fa.H = c.hidden;
+    fa.Dq = c.qkv_out;
+    fa.Do = c.attn_dim;
+    fa.E = c.n_experts;
+    fa.K = c.top_k;
+    fa.F = c.expert_ffn;
+    fa.Fs = c.shared_ffn;
+    fa.slice = h->single.slice;
+    fa.eps = c.rms_eps;
+    fa.spin_limit = 1 << 20;   // about a second of polling per wait
+    fa.trace = (uint64_t *)h->trace;
+    ProfScope p5{h, 5, st};
+    HIP_TRY(h, p5.begin());
+    HIP_TRY(h, launch_fused(fa, h->single.grid, st));
+    HIP_TRY(h, p5.end());
+    if (h->profiling) h->profiled_step = true;
+    return DL_OK;
+  }
 
   ProjArgs pa{};
   pa.x = (const uint16_t *)io->x;
@@ -286,8 +401,6 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
   pa.eps = c.rms_eps;
   pa.nblk_o = nblk_o_of(c);
   pa.nblk_qkv = (c.qkv_out + kQkvRowsPerBlock - 1) / kQkvRowsPerBlock;
-  if (h->profiling)
-    for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i) h->launched[i] = false;
   ProfScope p0{h, 0, st};
   HIP_TRY(h, p0.begin());
   HIP_TRY(h, launch_proj(pa, st));
@@ -388,6 +501,33 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
   if (h->profiling) h->profiled_step = true;
   return DL_OK;
 }
+
+int decode_layer_single_max_batch(const decode_layer *h) { return h ? h->single.max_batch : 0; }
+
+int decode_layer_status(decode_layer *h, uint32_t *status, int clear) {
+  if (!h || !status) return fail(h, DL_ERR_INVALID_ARG, "NULL handle or output");
+  HIP_TRY(h, hipSetDevice(h->device));
+  unsigned v = 0;
+  HIP_TRY(h, hipMemcpy(&v, h->s.status, sizeof v, hipMemcpyDeviceToHost));
+  *status = v;
+  if (clear && (v & 1u)) {
+    unsigned keep = v & ~1u;
+    HIP_TRY(h, hipMemcpy(h->s.status, &keep, sizeof keep, hipMemcpyHostToDevice));
+  }
+  return DL_OK;
+}
+
+int decode_layer_set_trace(decode_layer *h, void *device_buffer) {
+  if (!h) return fail(nullptr, DL_ERR_INVALID_ARG, "handle is NULL");
+  if (device_buffer && !aligned16(device_buffer))
+    return fail(h, DL_ERR_INVALID_ARG, "trace buffer is not 16-byte aligned");
+  h->trace = device_buffer;
+  return DL_OK;
+}
+
+int decode_layer_trace_points(void) { return kTracePoints; }
+
+int decode_layer_grid(const decode_layer *h) { return h ? h->single.grid : 0; }
 
 int decode_layer_set_profiling(decode_layer *h, int enable) {
   if (!h) return fail(nullptr, DL_ERR_INVALID_ARG, "handle is NULL");

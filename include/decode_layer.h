@@ -67,7 +67,31 @@ enum {
  *   rms_eps       : > 0 and finite
  *   score_fn      : 0 = sigmoid (the only value supported)
  *   renormalize   : 1 = top-k weights divided by their sum (the only value supported)
+ *   path          : DL_PATH_AUTO, DL_PATH_MULTI or DL_PATH_SINGLE (below)
+ *
+ * Execution paths.  The pages' backend is shape-aware: small-batch kernels at
+ * one or two tokens, split-K kernels beyond (wireai.ir "vLLM's speed jump on
+ * NVIDIA Blackwell servers; record 842 tokens/s for Kimi K3", section "Four
+ * key changes behind the jump", bullet 1).  This library has two:
+ *   DL_PATH_SINGLE  the whole step in ONE launch: one workgroup per CU, all
+ *                   resident, phases handing data to each other through
+ *                   device memory (the shared expert's and the router's
+ *                   weights stream while the norm is being exchanged).
+ *                   Available when hidden <= 8192 and <= 32 * (number of
+ *                   CUs), n_experts <= 512 and <= 2 * CUs, shared_ffn == 0 or
+ *                   == expert_ffn and <= CUs; for batches up to
+ *                   decode_layer_single_max_batch(), which is at most 8 and
+ *                   also bounded by B*k <= 64, B*E <= 8192, B*k*F <= 8192 and
+ *                   B*Fs <= 4096.
+ *   DL_PATH_MULTI   five launches (input/out-projection, router + top-k +
+ *                   permutation, routed gate/up, down + combine) with the
+ *                   shared expert's gate/up on the handle's second stream.
+ *                   Any batch in the envelope.
+ *   DL_PATH_AUTO    SINGLE when the step's batch allows it, else MULTI.
+ * Forcing DL_PATH_SINGLE makes a step with a larger batch fail with
+ * DL_ERR_UNSUPPORTED.
  */
+enum { DL_PATH_AUTO = 0, DL_PATH_MULTI = 1, DL_PATH_SINGLE = 2 };
 typedef struct {
   int32_t hidden;
   int32_t qkv_out;
@@ -80,6 +104,7 @@ typedef struct {
   float rms_eps;
   int32_t score_fn;
   int32_t renormalize;
+  int32_t path;
 } decode_layer_config;
 
 /* Weights of one layer shard: device pointers owned by the caller.  They
@@ -127,17 +152,33 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
                       int device, decode_layer **out);
 
 /* Enqueue one layer-step on `hip_stream` (a hipStream_t; NULL = the null
- * stream) and return without synchronising.  Device work: up to five kernel
+ * stream) and return without synchronising.  Device work: on the single-launch
+ * path one kernel on `hip_stream`; on the multi-launch path up to five kernel
  * launches, four on `hip_stream` and one (the shared expert's gate/up
  * projection) on the handle's second stream, which is forked from and joined
- * back into `hip_stream` with events, so the call can be captured in a HIP
- * graph.  No allocation, no host copy, no memset.
+ * back into `hip_stream` with events.  Either can be captured in a HIP graph.
+ * No allocation, no host copy, no memset.
+ * The single-launch kernel needs all of its workgroups (one per CU) resident
+ * at once; work on other streams may delay it but cannot deadlock it.  Its
+ * waits are bounded: if one expires (about a second) the step's outputs are
+ * undefined and decode_layer_status() reports it.
  * `io` is validated on the host first (DL_ERR_INVALID_ARG /
  * DL_ERR_UNSUPPORTED, nothing enqueued).  A failed launch returns DL_ERR_HIP;
  * faults inside kernels surface at the caller's next synchronisation.
  * One step per handle may be in flight at a time (the scratch is per
  * handle); distinct handles may run concurrently. */
 int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stream);
+
+/* Largest batch the single-launch path accepts with this handle (0 if none). */
+int decode_layer_single_max_batch(const decode_layer *h);
+
+/* Device-side status of the handle, read synchronously (synchronise the
+ * step's stream first).  Bits: 1 = a single-launch hand-off wait expired (that
+ * step's outputs are undefined); 2 = the handle's 32-bit step counter is
+ * exhausted (after 2^32 - 1 single-launch steps; the kernel then does nothing
+ * and the handle must be re-created).  `clear` != 0 resets bit 1 afterwards.
+ * Returns DL_OK or DL_ERR_HIP / DL_ERR_INVALID_ARG. */
+int decode_layer_status(decode_layer *h, uint32_t *status, int clear);
 
 /* Wait for the handle's streams, free its scratch, stream and events. NULL is a no-op. */
 int decode_layer_destroy(decode_layer *h);
@@ -161,18 +202,36 @@ const char *decode_layer_last_error(const decode_layer *h);
  * decode_layer_kernel_times() waits for the last step's events and writes
  * the launches' durations in milliseconds, in the fixed order
  *   0 out-projection + input projection, 1 shared expert gate/up,
- *   2 router + top-k + permute, 3 routed expert gate/up, 4 expert down + combine
- * (0 for a launch the configuration does not make).  It returns the number of
+ *   2 router + top-k + permute, 3 routed expert gate/up, 4 expert down + combine,
+ *   5 single-launch step
+ * (0 for a launch the last step did not make).  It returns the number of
  * entries written (<= capacity) or a negative DL_ERR_* code (DL_ERR_INVALID_ARG
  * if profiling is off or no step ran since it was enabled).  Enabling creates
  * the events (DL_ERR_HIP on failure); do not enable it while capturing a graph. */
-#define DECODE_LAYER_N_LAUNCHES 5
+#define DECODE_LAYER_N_LAUNCHES 6
 int decode_layer_set_profiling(decode_layer *h, int enable);
 int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
 
-/* Bytes of device scratch a handle with this configuration allocates
- * (0 if the configuration is invalid). */
-size_t decode_layer_scratch_bytes(const decode_layer_config *cfg);
+/* Phase trace of the single-launch kernel, for measurement.  With a non-NULL
+ * device buffer of decode_layer_grid(h) * decode_layer_trace_points() uint64
+ * values (caller-owned, 16-byte aligned), every later single-launch step has
+ * thread 0 of each workgroup w write the device wall clock (100 MHz) into
+ * buffer[w * points + p] at these points: 0 start, 1 out-projection done,
+ * 2 norm partials published and phase-B weights requested, 4 norm known,
+ * 5 logits and shared activations published, 7 all logits read, 13 top-k
+ * done, 8 expert lists built, 9 routed activations published,
+ * 10 activations read, 11 y written, 3 end (after qkv); others unused.
+ * NULL turns it off.  Returns DL_OK or DL_ERR_INVALID_ARG. */
+int decode_layer_set_trace(decode_layer *h, void *device_buffer);
+int decode_layer_trace_points(void);
+/* Workgroups of the single-launch kernel (the device's CU count; 0 if the path is unavailable). */
+int decode_layer_grid(const decode_layer *h);
+
+/* Bytes of device scratch a handle with this configuration allocates on a
+ * device with `n_cu` compute units (0 if the configuration is invalid).  The
+ * single-launch path's hand-off arrays grow with n_cu; n_cu = 0 gives the size
+ * without them (the multi-launch path alone).  Host-only. */
+size_t decode_layer_scratch_bytes(const decode_layer_config *cfg, int n_cu);
 
 #ifdef __cplusplus
 }

@@ -66,8 +66,9 @@ def upload_inputs(layer: RoutedLayer, device="cuda"):
             f32_tensor(raw.resid, device))
 
 
-def config_of(layer: RoutedLayer, max_batch: int | None = None, eps: float = 1e-6):
+def config_of(layer: RoutedLayer, max_batch: int | None = None, eps: float = 1e-6, path: int = 0):
     from decode_step_moe_amd import make_config
     s = layer.shape
     return make_config(s.hidden, s.qkv_out, s.attn_dim, s.n_experts, s.top_k, s.expert_ffn,
-                       s.shared_ffn, max_batch if max_batch is not None else max(s.batch, 1), eps)
+                       s.shared_ffn, max_batch if max_batch is not None else max(s.batch, 1), eps,
+                       path=path)

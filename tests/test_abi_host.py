@@ -43,6 +43,7 @@ def good():
     ("max_batch", 65, dl.DL_ERR_UNSUPPORTED), ("max_batch", 0, dl.DL_ERR_UNSUPPORTED),
     ("rms_eps", 0.0, dl.DL_ERR_UNSUPPORTED), ("rms_eps", float("inf"), dl.DL_ERR_UNSUPPORTED),
     ("score_fn", 1, dl.DL_ERR_UNSUPPORTED), ("renormalize", 0, dl.DL_ERR_UNSUPPORTED),
+    ("path", 3, dl.DL_ERR_UNSUPPORTED), ("path", -1, dl.DL_ERR_UNSUPPORTED),
 ])
 def test_config_validation(field, value, code):
     c = good()
@@ -62,6 +63,25 @@ def test_shared_expert_optional_and_scratch_size():
     c = dl.make_config(512, 768, 768, 8, 2, 256, 0, 1)
     assert dl.check_config(c) == dl.DL_OK
     assert dl.scratch_bytes(good()) > 0
+
+
+def test_single_launch_scratch_follows_the_plan():
+    """The single-launch hand-off arrays are sized by CU count and by the
+    largest batch that path takes (8 tokens here: 8 * top_k * F = 8192)."""
+    c = good()                       # TP16 shard shapes, max_batch 64
+    base = dl.scratch_bytes(c, 0)
+    with_single = dl.scratch_bytes(c, 256)
+    G, B, E, K, F, Fs = 256, 8, 384, 8, 128, 128
+    tagged = 8 * (G * B + B * E + B * K * F + B * Fs)
+    assert tagged <= with_single - base <= tagged + 8 * 256
+    c.path = dl.DL_PATH_MULTI        # multi-launch only: no single-launch arrays
+    assert dl.scratch_bytes(c, 256) == base
+    big_h = dl.make_config(16384, 512, 512, 384, 8, 128, 128, 8)   # hidden above 8192
+    assert dl.scratch_bytes(big_h, 256) == dl.scratch_bytes(big_h, 0)
+    many_e = dl.make_config(7168, 512, 512, 1024, 8, 128, 128, 8)  # more than 512 experts
+    assert dl.scratch_bytes(many_e, 256) == dl.scratch_bytes(many_e, 0)
+    odd_fs = dl.make_config(7168, 512, 512, 384, 8, 128, 256, 8)   # shared ffn != expert ffn
+    assert dl.scratch_bytes(odd_fs, 256) == dl.scratch_bytes(odd_fs, 0)
 
 
 def _io(batch=1, **kw):

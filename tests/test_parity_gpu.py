@@ -23,9 +23,18 @@ def need_gpu():
     import decode_step_moe_amd  # noqa: F401  (raises if the library was not built)
 
 
-def run_gpu(layer, with_h=True, max_batch=None, inplace=False, logits=True, layer_obj=None):
+AUTO, MULTI, SINGLE = 0, 1, 2
+PATH_NAMES = {AUTO: "auto", MULTI: "multi", SINGLE: "single"}
+
+
+def used_single(obj, batch, path):
+    return path != MULTI and batch <= obj.single_max_batch
+
+
+def run_gpu(layer, with_h=True, max_batch=None, inplace=False, logits=True, layer_obj=None,
+            path=AUTO):
     from decode_step_moe_amd import DecodeLayer
-    cfg = sdev.config_of(layer, max_batch)
+    cfg = sdev.config_of(layer, max_batch, path=path)
     if layer_obj is None:
         w = sdev.upload_weights(layer)
         layer_obj = DecodeLayer(cfg, w)
@@ -35,6 +44,7 @@ def run_gpu(layer, with_h=True, max_batch=None, inplace=False, logits=True, laye
         out.resid_out = resid
     layer_obj.step(x, attn, resid, out)
     torch.cuda.synchronize()
+    assert layer_obj.status() == 0, "a single-launch hand-off wait expired"
     got = {"qkv": out.qkv.cpu().numpy(), "resid_out": out.resid_out.cpu().numpy(),
            "logits": out.router_logits.cpu().numpy() if logits else None,
            "topk_idx": out.topk_idx.cpu().numpy(), "topk_w": out.topk_w.cpu().numpy(),
@@ -51,28 +61,35 @@ def check(layer, got, tag):
     return m
 
 
+@pytest.mark.parametrize("path", [AUTO, MULTI])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_workload_parity(cfg):
-    say(f"[workload cfg={cfg} {gen.SHAPES[cfg].name}] start")
+def test_workload_parity(cfg, path):
+    say(f"[workload cfg={cfg} {gen.SHAPES[cfg].name} path={PATH_NAMES[path]}] start")
     layer = workload.build(cfg, h_source="stored")
-    got, _ = run_gpu(layer)
-    check(layer, got, f"cfg{cfg}")
+    got, obj = run_gpu(layer, path=path)
+    single = used_single(obj, layer.shape.batch, path)
+    # batches up to 8 take the single-launch path under AUTO at these shapes
+    assert single == (path == AUTO and layer.shape.batch <= 8), (obj.single_max_batch, layer.shape.batch)
+    check(layer, got, f"cfg{cfg}_{'single' if single else 'multi'}")
 
 
+@pytest.mark.parametrize("path", [AUTO, MULTI])
 @pytest.mark.parametrize("batch", [2, 3, 5, 13, 64])
-def test_ragged_batches(batch):
-    say(f"[ragged cfg=2 shapes, batch={batch}] start")
+def test_ragged_batches(batch, path):
+    say(f"[ragged cfg=2 shapes, batch={batch} path={PATH_NAMES[path]}] start")
     layer = workload.build(2, batch=batch)
-    got, _ = run_gpu(layer, max_batch=64)
-    check(layer, got, f"ragged_b{batch}")
+    got, obj = run_gpu(layer, max_batch=64, path=path)
+    check(layer, got, f"ragged_b{batch}_{'single' if used_single(obj, batch, path) else 'multi'}")
 
 
+@pytest.mark.parametrize("path", [AUTO, MULTI])
 @pytest.mark.parametrize("top_k,shared", [(1, 256), (8, 256), (2, 0), (1, 0)])
-def test_topk_and_shared_edges(top_k, shared):
-    say(f"[tiny edges k={top_k} shared_ffn={shared}] start")
+def test_topk_and_shared_edges(top_k, shared, path):
+    say(f"[tiny edges k={top_k} shared_ffn={shared} path={PATH_NAMES[path]}] start")
     layer = workload.build(0, batch=3, top_k=top_k, shared_ffn=shared)
-    got, _ = run_gpu(layer)
-    m = check(layer, got, f"tiny_k{top_k}_fs{shared}")
+    got, obj = run_gpu(layer, path=path)
+    assert used_single(obj, 3, path) == (path == AUTO)
+    m = check(layer, got, f"tiny_k{top_k}_fs{shared}_{PATH_NAMES[path]}")
     if top_k == 1:
         assert np.all(got["topk_w"] == 1.0)
     if top_k == 8:   # k = E: every expert, weights s / sum s
@@ -90,11 +107,42 @@ def test_batch_zero_is_noop():
     torch.cuda.synchronize()
 
 
-def test_inplace_residual_and_null_logits():
-    say("[in-place residual, logits NULL] start")
+@pytest.mark.parametrize("path", [AUTO, MULTI])
+def test_inplace_residual_and_null_logits(path):
+    say(f"[in-place residual, logits NULL, path={PATH_NAMES[path]}] start")
     layer = workload.build(4, h_source="stored")
-    got, _ = run_gpu(layer, inplace=True, logits=False)
+    got, _ = run_gpu(layer, inplace=True, logits=False, path=path)
     check(layer, got, "inplace")
+
+
+def test_single_path_refuses_a_larger_batch():
+    """DL_PATH_SINGLE with a batch above its limit fails on the host; nothing runs."""
+    say("[forced single path, batch above its limit] start")
+    from decode_step_moe_amd import DecodeLayerError, DL_ERR_UNSUPPORTED
+    layer = workload.build(2, batch=13)
+    got, obj = run_gpu(workload.build(2, batch=5), max_batch=64, path=SINGLE)
+    assert obj.single_max_batch == 8
+    x, attn, resid = sdev.upload_inputs(layer)
+    with pytest.raises(DecodeLayerError) as ei:
+        obj.step(x, attn, resid)
+    assert ei.value.code == DL_ERR_UNSUPPORTED
+
+
+def test_single_path_alternating_batches():
+    """One handle, single-launch path, batch sizes changing from step to step:
+    every step's hand-off values carry a fresh tag, so values left by an
+    earlier (larger) step are never taken for this step's."""
+    say("[single path, batches 8,1,5,8,2,1 on one handle] start")
+    from decode_step_moe_amd import DecodeLayer
+    full = workload.build(2, batch=8)
+    obj = DecodeLayer(sdev.config_of(full, 8), sdev.upload_weights(full))
+    for b in (8, 1, 5, 8, 2, 1):
+        # the batch-8 router gives every prefix token its target logits exactly
+        layer = routing.RoutedLayer(gen.draw(2, batch=b), full.w_router, full.targets[:b],
+                                    full.target_logits[:b])
+        got, _ = run_gpu(layer, layer_obj=obj)
+        assert used_single(obj, b, AUTO)
+        check(layer, got, f"alternating_b{b}")
 
 
 def test_batch_equals_single_token_steps():
@@ -122,6 +170,7 @@ def test_repeated_steps_are_stable_under_concurrency():
     layer = workload.build(2, h_source="stored")
     cfg = sdev.config_of(layer)
     obj = DecodeLayer(cfg, sdev.upload_weights(layer))
+    assert used_single(obj, 8, AUTO)
     x, attn, resid = sdev.upload_inputs(layer)
     first = obj.step(x, attn, resid)
     torch.cuda.synchronize()
@@ -140,6 +189,7 @@ def test_repeated_steps_are_stable_under_concurrency():
                 for k, v in ref.items():
                     assert torch.equal(getattr(oo, k), v), (it, k)
     torch.cuda.synchronize()
+    assert obj.status() == 0
 
 
 def test_graph_replay_matches_eager():
@@ -170,6 +220,45 @@ def test_graph_replay_matches_eager():
             assert torch.equal(getattr(out, k), getattr(eager, k)), (rep, k)
         obj.step(x, attn, resid)   # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", [AUTO, MULTI])
+def test_graph_replay_many_steps(path):
+    """A graph holding two steps (different copies of the inputs), replayed
+    10 times with eager steps in between: the single-launch path's step
+    counter lives on the device, so replays use fresh tags."""
+    say(f"[graph of 2 steps x 10 replays, cfg 2, path={PATH_NAMES[path]}] start")
+    from decode_step_moe_amd import DecodeLayer
+    layer = workload.build(2, h_source="stored")
+    obj = DecodeLayer(sdev.config_of(layer, path=path), sdev.upload_weights(layer))
+    x, attn, resid = sdev.upload_inputs(layer)
+    eager = obj.step(x, attn, resid)
+    torch.cuda.synchronize()
+    outs = [obj.alloc_outputs(8) for _ in range(2)]
+    ios = [obj.make_io(x, attn, resid, o) for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        obj.step_io(ios[0], s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        obj.step_io(ios[0])
+        obj.step_io(ios[1])
+    for rep in range(10):
+        for o in outs:
+            o.moe_out.fill_(float("nan"))
+            o.topk_idx.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for o in outs:
+            for k in ("qkv", "resid_out", "topk_idx", "topk_w", "moe_out"):
+                assert torch.equal(getattr(o, k), getattr(eager, k)), (rep, k)
+        if rep % 3 == 0:
+            obj.step(x, attn, resid)
+            torch.cuda.synchronize()
+    assert obj.status() == 0
 
 
 @pytest.mark.parametrize("scale", [1e3, 1e-3])
