@@ -12,18 +12,22 @@
 // bullets 1-4).  Here the grid is one workgroup per CU, all resident at once,
 // and the dependencies are hand-offs between phases of the same kernel.
 //
-// Workgroup w owns the H-slice S_w = [w*slice, (w+1)*slice) of the hidden
-// dimension, router rows e = w and w + G, and shared-expert ffn row f = w.
-// Phases:
+// Work of workgroup w (G workgroups):
+//   * the H-slice S_w = [w*slice, (w+1)*slice) of the out-projection, the
+//     norm statistics and the down projection;
+//   * "units" u = w and w + G of the E + Fs row units: unit u < E is router
+//     row u (fp32), unit u >= E is the shared expert's gate/up row pair
+//     f = u - E (bf16); both are H*4 bytes, so the load is balanced;
+//   * its share of the routed gate/up rows and of the qkv rows.
 //
-//  A  out-projection rows i in S_w:  r1 = r + attn Wo^T     -> resid_out
-//     hg = g * r1 (global and LDS); per-token partial sum of r1^2 over S_w
-//     -> published.  Then the workgroup's router rows and shared-expert
-//     gate/up rows (static weights) are requested into registers.
+// Phases:
+//  A  r1 = r + attn Wo^T on S_w -> resid_out; hg = g * r1 (global and LDS);
+//     per-token partial sum of r1^2 over S_w -> published.
+//     The unit rows (static weights) are requested into LDS.
 //  B  1/rms(t) from the G partial sums (every workgroup, identical order);
-//     h = hg / rms is read back from global memory and
-//     l[t, e] = h[t] . Wr[e]                          -> published
-//     a_s[t, f] = silu(S1[f] . h[t]) * (S3[f] . h[t])  -> published
+//     with h = hg / rms read back from global memory:
+//     l[t, e] = h[t] . Wr[e] -> published;
+//     a_s[t, f] = silu(S1[f] . h[t]) * (S3[f] . h[t]) -> published.
 //  C  every workgroup reads all logits and takes the same top-k decision
 //     (descending logit, ties to the lower expert id; s = sigmoid(l),
 //     w = s / sum s over the k picks), builds the same per-expert token lists
@@ -33,11 +37,15 @@
 //  D  y[t, i] for i in S_w:  sum_f S2[i, f] a_s[t, f]
 //                           + sum over the k picks of t, in pick order, of
 //                             w_p sum_f W2[e_p, i, f] a[p, f].
-//     Each y element is produced by one thread in a fixed order.  The first
-//     down-projection weights are requested before waiting for a.
-//     Last, the attention input projection rows qkv[t, j] = x[t] . Wqkv[j] of
-//     this workgroup's share of j (independent of everything else; placed at
-//     the end so that its traffic never queues in front of a hand-off).
+//     Each y element is produced by one thread in a fixed order.
+//     qkv[t, j] = x[t] . Wqkv[j] for this workgroup's rows j is computed while
+//     the activations of phase C are in flight.
+//
+// Wave roles.  A wave's loads complete in issue order, so a poll issued after
+// a bulk weight request waits for that request.  Waves 0-3 (control) poll and
+// never have bulk requests outstanding when they do; waves 4-7 (stream)
+// request the static weights of later phases (unit rows, qkv rows, the first
+// down-projection rows) ahead of time.  All eight stream the routed rows.
 //
 // Hand-offs.  Values produced by one workgroup for another (partial sums,
 // logits, SwiGLU activations) are written as 64-bit pairs (value, tag) with
@@ -52,9 +60,6 @@
 // read before a wait (the ordering rule of wireai.ir, "Oversight and
 // validation for AI-generated kernels").  Every wait is bounded: on expiry the
 // kernel records an error in the handle's status word and runs to completion.
-//
-// Wave-wide reductions on the serial parts (top-k, lists) use DPP lane
-// permutes and readlane rather than LDS-routed shuffles.
 #include <type_traits>
 
 #include "common.h"
@@ -66,8 +71,12 @@ namespace {
 
 constexpr int kFT = kFusedThreads;          // 512 threads, 8 waves
 constexpr int kFWaves = kFT / kWave;
-constexpr int kRtrJ = kFusedMaxH / 4 / kFT; // float4 chunks per thread per router row (4)
-constexpr int kShJ = kFusedMaxH / 8 / kFT;  // 16-byte bf16 chunks per thread per shared row (2)
+constexpr int kCtl = 256;                   // control threads (waves 0-3); stream threads are kCtl..kFT-1
+constexpr int kStr = kFT - kCtl;
+constexpr int kUnitU4 = kFusedMaxH / 4;     // 16-byte words of one unit row (H*4 bytes)
+constexpr int kUnitJ = kUnitU4 / kStr;      // words per stream thread per unit (8)
+constexpr int kChunkJ = kFusedMaxH / 8 / kFT;  // 8-element chunks per thread in phase B (2)
+static_assert(kFusedW2Words % kStr == 0, "staging split");
 
 // ---- tagged hand-off values -------------------------------------------------
 __device__ __forceinline__ void put_tagged(uint64_t *p, float v, unsigned tag) {
@@ -92,33 +101,62 @@ __device__ __forceinline__ float finish_tagged(const uint64_t *p, uint64_t x, un
   }
   return __uint_as_float((unsigned)x);
 }
+// Polls n tagged values src[i], i = first, first + stride, ... into dst[i],
+// eight requests in flight per thread.
+__device__ __forceinline__ void gather_tagged(const uint64_t *src, float *dst, int first, int stride, int n,
+                                              unsigned tag, int limit, int *bad) {
+  for (int i0 = first; i0 < n; i0 += 8 * stride) {
+    uint64_t x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = i0 + r * stride;
+      if (i < n) x[r] = ld_tagged(src + i);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = i0 + r * stride;
+      if (i < n) dst[i] = finish_tagged(src + i, x[r], tag, limit, bad);
+    }
+  }
+}
 
 // ---- DPP wave arg-max ---------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+// (value, index) packed into one 64-bit key that orders like "larger value,
+// then smaller index": the float's bits mapped to an order-preserving
+// unsigned word in the high half, the inverted index in the low half.  The
+// wave maximum of the keys is taken with lane permutes (no branches).
+__device__ __forceinline__ uint64_t rank_key(float v, int i) {
+  unsigned u = __float_as_uint(v == 0.f ? 0.f : v);  // -0 ranks as +0 (they compare equal)
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)i);
 }
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+__device__ __forceinline__ void key_unpack(uint64_t k, float &v, int &i) {
+  unsigned u = (unsigned)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  v = __uint_as_float(u);
+  i = (int)(0xffffffffu - (unsigned)k);
 }
-__device__ __forceinline__ void amax(float &v, int &i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  // rows outside ROWS (and lanes with no source) compare against themselves
+  const int lo = (int)(unsigned)k, hi = (int)(unsigned)(k >> 32);
+  const unsigned olo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+  const unsigned ohi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > k ? o : k;
 }
-// Largest value over the wave, ties to the lower index; result uniform.
+// Largest (value, index) over the wave by the order above; result uniform.
 __device__ __forceinline__ void wave_argmax(float &v, int &i) {
-  amax(v, i, dpp_f<0xB1>(v), dpp_i<0xB1>(i));    // quad_perm [1,0,3,2]
-  amax(v, i, dpp_f<0x4E>(v), dpp_i<0x4E>(i));    // quad_perm [2,3,0,1]
-  amax(v, i, dpp_f<0x141>(v), dpp_i<0x141>(i));  // row_half_mirror
-  amax(v, i, dpp_f<0x140>(v), dpp_i<0x140>(i));  // row_mirror: rows of 16 uniform
-  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
-  int bi = __builtin_amdgcn_readlane(i, 15);
-#pragma unroll
-  for (int r = 1; r < 4; ++r)
-    amax(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r + 15)),
-         __builtin_amdgcn_readlane(i, 16 * r + 15));
-  v = bv;
-  i = bi;
+  uint64_t k = rank_key(v, i);
+  k = dpp_max_step<kDppXor1, 0xf>(k);
+  k = dpp_max_step<kDppXor2, 0xf>(k);
+  k = dpp_max_step<kDppHalfMirror, 0xf>(k);
+  k = dpp_max_step<kDppMirror, 0xf>(k);  // rows of 16 uniform
+  k = dpp_max_step<0x142, 0xa>(k);       // row_bcast:15 -> rows 1, 3
+  k = dpp_max_step<0x143, 0xc>(k);       // row_bcast:31 -> rows 2, 3
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)k, 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(k >> 32), 63);
+  key_unpack(((uint64_t)hi << 32) | lo, v, i);
 }
 
 // ---- activations ------------------------------------------------------------
@@ -192,11 +230,9 @@ __device__ __forceinline__ void wave_rows_dot(const uint16_t *const (&w)[NR], in
 
 __device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }
 
-__device__ __forceinline__ float dot4(const float4 &a, const float4 &b, float s) {
-  s = fmaf(a.x, b.x, s);
-  s = fmaf(a.y, b.y, s);
-  s = fmaf(a.z, b.z, s);
-  return fmaf(a.w, b.w, s);
+__device__ __forceinline__ void as8(const uint4 &a, const uint4 &b, float (&f)[8]) {
+  f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+  f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
 }
 
 // Phase trace (measurement only): thread 0 stamps the device wall clock.
@@ -206,12 +242,18 @@ __device__ __forceinline__ void stamp(const FusedArgs &a, int point) {
 
 struct Lds {
   float hg[kFusedMaxB][kFusedMaxSlice];
-  float sq[kFusedMaxB][kFusedMaxSlice];
-  float red[kFWaves * 4 * kFusedMaxB];
+  float red[kFWaves * kFusedMaxB * 4];
   float inv_rms[kFusedMaxB];
-  // logits for top-k, later the routed SwiGLU activations [pair][F]
-  float big[kFusedBig];
-  float act_s[kFusedActS];
+  union {
+    uint4 unit[2][kUnitU4];   // phase A/B: this workgroup's unit rows
+    float logits[kFusedBig];  // phase C: every logit
+    struct {                  // phase D
+      float act[kFusedBig];
+      float act_s[kFusedActS];
+      float contrib[(kFusedMaxB + kFusedMaxPairs) * kFusedMaxSlice];
+    } d;
+  } u;
+  uint4 w2[kFusedW2Words];    // phase D: the first down-projection rows of the slice
   // top-k and lists
   int sel[kFusedMaxPairs];
   float selw[kFusedMaxPairs];
@@ -223,27 +265,29 @@ struct Lds {
   int pair_exp[kFusedMaxPairs];
   float pair_w[kFusedMaxPairs];
   int n_active;
-  // gate/up partials: [wave][token]
-  float uv[kFWaves][kFusedMaxB];
-  // phase D contributions: [item = shared token t | B + pair p][row in slice]
-  float contrib[(kFusedMaxB + kFusedMaxPairs) * kFusedMaxSlice];
+  // gate/up sums of a round: [item][W1 | W3][token]
+  float uv[8][2][kFusedMaxB];
+  float sqw[kFWaves][kFusedMaxB];  // per-wave partial sums of r1^2
+  int arrive;
   int bad;
 };
 
-// ---- phase A: out-projection rows of the slice ------------------------------
+// ---- phase A: out-projection rows of the slice -------------------------------
+// Wave v owns rows il = v + 8r (r < 4) of the slice.  Lane t < B keeps token
+// t: r1 -> resid_out, hg -> global (device-scope stores, written through) and
+// LDS, and returns its partial sum of r1^2 over the wave's rows.
 template <int NT>
-__device__ void oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
+__device__ float oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
+  constexpr int NR = kFusedMaxSlice / kFWaves;  // 4
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int B = a.B;
   const ActBf16Rows act{a.attn, a.Do, B - 1};
   const int nch = a.Do >> 3;
-  // up to kFusedMaxSlice / 8 = 4 rows per wave, all issued together; the
-  // residual and gain of lane t's (row, token t) are requested up front too
-  const uint16_t *rows[4];
-  int il[4];
-  float res[4], gn[4];
+  const uint16_t *rows[NR];
+  int il[NR];
+  float res[NR], gn[NR];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < NR; ++r) {
     il[r] = wv + kFWaves * r;
     const int i = i0 + min(il[r], ni - 1);
     rows[r] = a.w_o + (size_t)i * a.Do;
@@ -251,10 +295,11 @@ __device__ void oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
     res[r] = mine ? a.resid_in[(size_t)lane * a.H + i] : 0.f;
     gn[r] = mine ? bf16_lo(a.gain[i]) : 0.f;
   }
-  float o[4][NT];
-  wave_rows_dot<4, NT, 2>(rows, 0, nch, act, o);
+  float o[NR][NT];
+  wave_rows_dot<NR, NT, 2>(rows, 0, nch, act, o);
+  float sq = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < NR; ++r) {
     float mine = 0.f;  // lane t keeps token t's sum
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -265,95 +310,175 @@ __device__ void oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
       const float r1 = res[r] + mine;
       a.resid_out[ix] = r1;
       const float hgv = gn[r] * r1;
-      a.hg[ix] = hgv;
+      __hip_atomic_store(a.hg + ix, hgv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       L.hg[lane][il[r]] = hgv;
-      L.sq[lane][il[r]] = r1 * r1;
+      sq += r1 * r1;
     }
   }
+  return sq;
 }
 
 // 16-byte weight chunks per lane in flight per row, by token count
 template <int NT>
 constexpr int cpb_for() { return NT <= 2 ? 16 : NT <= 4 ? 8 : 4; }
 
-template <int NT>
-__device__ void qkv_rows(const FusedArgs &a, int j0, int nj) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const ActBf16Rows act{a.x, a.H, a.B - 1};
-  const int nch = a.H >> 3;
-  for (int jl = wv; jl < nj; jl += kFWaves) {
-    const uint16_t *row[1] = {a.w_qkv + (size_t)(j0 + jl) * a.H};
-    float s[1][NT];
-    wave_rows_dot<1, NT, cpb_for<NT>()>(row, 0, nch, act, s);
+// ---- phase C: gate/up rows --------------------------------------------------
+// One bf16 row (16-byte chunks c = lane + 64u, u < CPB, of [c0, cend)) dotted
+// with NT gathered fp32 hg rows, split into a load step and a use step so that
+// a wave can have the loads of several rows in flight before it uses any.
+template <int NT, int CPB>
+struct RowDot {
+  uint4 wv[CPB];
+  __device__ __forceinline__ void issue(const uint16_t *row, int c0, int cend) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (lane == t && t < a.B) a.qkv[(size_t)t * a.Dq + j0 + jl] = s[0][t];
+    for (int u = 0; u < CPB; ++u) {
+      const int c = c0 + lane + kWave * u;
+      wv[u] = c < cend ? ld_stream16(row + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+    }
   }
-}
+  __device__ __forceinline__ void use(const HgGather<NT> &act, int c0, int cend, float (&acc)[NT]) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int c = c0 + lane + kWave * u;
+      if (c < cend) {
+        float wf[8];
+        unpack8(wv[u], wf);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float hv[8];
+          act.load8(t, c * 8, hv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[t] = fmaf(wf[e], hv[e], acc[t]);
+        }
+      }
+    }
+  }
+};
 
-// ---- phase C: routed gate/up, one (expert, ffn row) pair per two waves ------
+// A gate/up row: row f of W1/W3 of a routed expert over its tokens, or row f
+// of S1/S3 of the shared expert over all B tokens.
+struct GuRow {
+  const uint16_t *row = nullptr;
+  const int *toks = nullptr;  // LDS token list, or nullptr for tokens 0..cnt-1
+  int cnt = 0;
+  __device__ __forceinline__ int tok(int t) const {
+    const int tt = t < cnt ? t : cnt - 1;
+    return toks ? toks[tt] : tt;
+  }
+};
+
+// One wave: rows A and (if B.row) B, with every weight load of both issued
+// before any is used.  Sums per token come back in every lane.
 template <int NT>
-__device__ void routed_gateup_row(const FusedArgs &a, Lds &L, int slot, int f) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int e = L.act_exp[slot], cnt = L.act_cnt[slot], off = L.act_off[slot];
-  HgGather<NT> act;
-  act.base = a.hg;
-  act.ld = a.H;
+__device__ void gateup_two(const FusedArgs &a, const GuRow &A, const GuRow &Bw, float (&sa)[NT], float (&sb)[NT]) {
+  constexpr int CPB = NT <= 2 ? 16 : NT <= 4 ? 8 : 4;
+  HgGather<NT> ga, gb;
+  ga.base = gb.base = a.hg;
+  ga.ld = gb.ld = a.H;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) act.tok[t] = L.pair_tok[off + (t < cnt ? t : cnt - 1)];
-  const uint16_t *row[1] = {((wv & 1) ? a.w3 : a.w1) + ((size_t)e * a.F + f) * a.H};
-  float s[1][NT];
-  wave_rows_dot<1, NT, cpb_for<NT>()>(row, 0, a.H >> 3, act, s);
+  for (int t = 0; t < NT; ++t) {
+    ga.tok[t] = A.tok(t);
+    gb.tok[t] = Bw.row ? Bw.tok(t) : 0;
+  }
+  float acc_a[NT], acc_b[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    if (lane == t) L.uv[wv][t] = s[0][t];
+  for (int t = 0; t < NT; ++t) acc_a[t] = acc_b[t] = 0.f;
+  const int nch = a.H >> 3;
+  for (int c0 = 0; c0 < nch; c0 += CPB * kWave) {
+    RowDot<NT, CPB> da, db;
+    da.issue(A.row, c0, nch);
+    if (Bw.row) db.issue(Bw.row, c0, nch);
+    da.use(ga, c0, nch, acc_a);
+    if (Bw.row) db.use(gb, c0, nch, acc_b);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    sa[t] = wave_sum(acc_a[t]);
+    sb[t] = wave_sum(acc_b[t]);
+  }
 }
 
 // ---- phase D: one (item, row) unit per group of LPG lanes --------------------
 // Items 0..B-1 are the shared expert's tokens (weights S2, activations
 // act_s), items B..B+P-1 the routed pairs (weights W2 of the pair's expert,
 // activations act, scaled by the pair's weight); F = 8 * LPG for both.
-// Without a shared expert the items start at B.
+// Without a shared expert the items start at B.  Unit u = (item0 + u / ni,
+// row u % ni).  The weights of units [0, U0) are staged in LDS by the stream
+// threads while the activations are awaited; the rest are streamed.
 template <int LPG>
 struct Down {
   static constexpr int NG = kFT / LPG;  // lane groups
-  static constexpr int R = 8;           // units per group whose weights are in flight together
+  static constexpr int R = 8;
   const FusedArgs &a;
   Lds &L;
   int i0, ni, item0, n_units;
-  __device__ void issue(int round, uint4 (&wv)[R]) const {
-    const int g = threadIdx.x / LPG, lg = threadIdx.x % LPG;
+  __device__ int u0_end() const { return min(n_units, kFusedW2Words / LPG); }
+  __device__ const uint16_t *row(int u) const {
+    const int item = item0 + u / ni, il = u % ni;
+    return item < a.B ? a.s2 + (size_t)(i0 + il) * a.F
+                      : a.w2 + ((size_t)L.pair_exp[item - a.B] * a.H + i0 + il) * a.F;
+  }
+  // stream threads: word k of the staged range is unit k / LPG, lane k % LPG
+  __device__ void stage() const {
+    const int n = u0_end() * LPG;
+    constexpr int J = kFusedW2Words / kStr;  // 16
+    uint4 v[J];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int u = g + NG * (round * R + r);
-      wv[r] = make_uint4(0, 0, 0, 0);
-      if (u < n_units) {
-        const int item = item0 + u / ni, il = u % ni;
-        const uint16_t *row = item < a.B ? a.s2 + (size_t)(i0 + il) * a.F
-                                         : a.w2 + ((size_t)L.pair_exp[item - a.B] * a.H + i0 + il) * a.F;
-        wv[r] = ld_stream16(row + lg * 8);
+    for (int j = 0; j < J; ++j) {
+      const int k = (threadIdx.x - kCtl) + kStr * j;
+      v[j] = k < n ? ld_stream16(row(k / LPG) + (k % LPG) * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = (threadIdx.x - kCtl) + kStr * j;
+      if (k < n) L.w2[k] = v[j];
+    }
+  }
+  __device__ void use(int u, const uint4 &wv) const {
+    const int lg = threadIdx.x % LPG;
+    const int item = item0 + u / ni, il = u % ni;
+    const float *ap = item < a.B ? L.u.d.act_s + item * a.F + lg * 8 : L.u.d.act + (item - a.B) * a.F + lg * 8;
+    float wf[8];
+    unpack8(wv, wf);
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s = fmaf(wf[q], ap[q], s);
+    s = group_sum(s, LPG);
+    if (lg == 0) L.u.d.contrib[item * kFusedMaxSlice + il] = item < a.B ? s : s * L.pair_w[item - a.B];
+  }
+  // all threads: staged units from LDS, then the rest streamed
+  __device__ void compute() const {
+    const int g = threadIdx.x / LPG, lg = threadIdx.x % LPG;
+    const int ue = u0_end();
+    for (int ub = 0; ub < ue; ub += NG * R) {
+      uint4 wv[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int u = ub + g + NG * r;
+        wv[r] = u < ue ? L.w2[u * LPG + lg] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int u = ub + g + NG * r;
+        if (u < ue) use(u, wv[r]);
+      }
+    }
+    for (int ub = ue; ub < n_units; ub += NG * R) {
+      uint4 wv[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int u = ub + g + NG * r;
+        wv[r] = u < n_units ? ld_stream16(row(u) + lg * 8) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int u = ub + g + NG * r;
+        if (u < n_units) use(u, wv[r]);
       }
     }
   }
-  __device__ void consume(int round, const uint4 (&wv)[R]) const {
-    const int g = threadIdx.x / LPG, lg = threadIdx.x % LPG;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int u = g + NG * (round * R + r);
-      if (u < n_units) {
-        const int item = item0 + u / ni, il = u % ni;
-        const float *ap = item < a.B ? L.act_s + item * a.F + lg * 8 : L.big + (item - a.B) * a.F + lg * 8;
-        float wf[8];
-        unpack8(wv[r], wf);
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s = fmaf(wf[q], ap[q], s);
-        s = group_sum(s, LPG);
-        if (lg == 0) L.contrib[item * kFusedMaxSlice + il] = item < a.B ? s : s * L.pair_w[item - a.B];
-      }
-    }
-  }
-  __device__ int rounds() const { return (n_units + NG * R - 1) / (NG * R); }
 };
 
 template <class Fn>
@@ -379,6 +504,8 @@ __device__ __forceinline__ void by_lpg(int F, Fn fn) {
 __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   __shared__ Lds L;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool ctl = tid < kCtl;
+  const int st = tid - kCtl;  // stream-thread index (valid when !ctl)
   const int w = blockIdx.x, G = gridDim.x;
   const int B = a.B, E = a.E, K = a.K, H = a.H;
   const unsigned epoch = *a.epoch;
@@ -387,49 +514,59 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     return;
   }
   const unsigned tag = epoch + 1;
-  if (tid == 0) L.bad = 0;
+  if (tid == 0) {
+    L.bad = 0;
+    L.arrive = 0;
+  }
+  __syncthreads();
   const int i0 = w * a.slice;
   const int ni = max(0, min(a.slice, H - i0));
   stamp(a, 0);
 
   // ================= phase A =================
-  if (ni > 0) by_tokens(B, [&](auto nt) { oproj_rows<decltype(nt)::value>(a, L, i0, ni); });
-  __syncthreads();
-  stamp(a, 1);
-  // release hg (ordinary stores) before the hand-off values that announce it
-  if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid < B) {
-    float s = 0.f;
-    for (int il = 0; il < ni; ++il) s += L.sq[tid][il];
-    put_tagged(a.pss + (size_t)w * B + tid, s, tag);
-  }
-  // static weights for phase B, requested now: router rows e0 = w, e1 = w + G
-  // (fp32, float4 chunk c = tid + kFT*j of H/4) and shared gate/up row f = w
-  // (bf16, 16-byte chunk c = tid + kFT*j of H/8)
-  const int e0 = w, e1 = w + G;
-  const bool has_e0 = e0 < E, has_e1 = e1 < E, has_f = w < a.Fs;
-  float4 rt[2][kRtrJ];
-  uint4 sh[2][kShJ];
-#pragma unroll
-  for (int j = 0; j < kRtrJ; ++j) {
-    const int c = tid + kFT * j;
-    const bool in = c < (H >> 2);
-    rt[0][j] = has_e0 && in ? ld_stream16f(a.w_router + (size_t)e0 * H + 4 * c) : make_float4(0, 0, 0, 0);
-    rt[1][j] = has_e1 && in ? ld_stream16f(a.w_router + (size_t)e1 * H + 4 * c) : make_float4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < kShJ; ++j) {
-    const int c = tid + kFT * j;
-    const bool in = has_f && c < (H >> 3);
-    sh[0][j] = in ? ld_stream16(a.s1 + (size_t)w * H + 8 * c) : make_uint4(0, 0, 0, 0);
-    sh[1][j] = in ? ld_stream16(a.s3 + (size_t)w * H + 8 * c) : make_uint4(0, 0, 0, 0);
-  }
-  stamp(a, 2);
-
-  // ================= phase B =================
   {
-    // poll all G partial sums of every token at once, then reduce per token
+    // out-projection rows.  Each wave leaves its partial sums of r1^2 in LDS
+    // once its hg values are written through; the last wave to arrive adds
+    // the 8 partials in wave order and publishes them (no workgroup barrier).
+    float sq = 0.f;
+    if (ni > 0) by_tokens(B, [&](auto nt) { sq = oproj_rows<decltype(nt)::value>(a, L, i0, ni); });
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's device-scope hg stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane < B) L.sqw[wv][lane] = sq;
+    int arrived = 0;
+    if (lane == 0) arrived = __hip_atomic_fetch_add(&L.arrive, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    arrived = __builtin_amdgcn_readfirstlane(arrived);
+    if (arrived == kFWaves - 1 && lane < B) {
+      float s8 = 0.f;
+#pragma unroll
+      for (int v = 0; v < kFWaves; ++v) s8 += __hip_atomic_load(&L.sqw[v][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      put_tagged(a.pss + (size_t)w * B + lane, s8, tag);
+    }
+  }
+  stamp(a, 1);
+  const int er[2] = {w, w + G};  // this workgroup's router rows
+  if (!ctl) {
+    // stream threads: the router rows (static weights) -> LDS
+    uint4 v[2][kUnitJ];
+    const int nw = H >> 2;  // 16-byte words per fp32 row
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < kUnitJ; ++j) {
+        const int i = st + kStr * j;
+        v[q][j] = er[q] < E && i < nw ? ld_stream16(reinterpret_cast<const uint4 *>(a.w_router + (size_t)er[q] * H) + i)
+                                      : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < kUnitJ; ++j) {
+        const int i = st + kStr * j;
+        if (er[q] < E && i < nw) L.u.unit[q][i] = v[q][j];
+      }
+  } else {
+    // control threads: every workgroup's partial sums (thread q: workgroup q)
     uint64_t x[kFusedMaxB];
 #pragma unroll
     for (int t = 0; t < kFusedMaxB; ++t)
@@ -442,114 +579,85 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         if (lane == 0) L.red[wv * kFusedMaxB + t] = v;
       }
     }
-    __syncthreads();
-    if (tid < B) {
-      float s = 0.f;
-      for (int q = 0; q < kFWaves; ++q) s += L.red[q * kFusedMaxB + tid];
-      L.inv_rms[tid] = 1.0f / sqrtf(s / (float)H + a.eps);
-    }
-    __syncthreads();
   }
-  // every workgroup's hg is now announced: acquire before reading it
+  __syncthreads();
+  if (tid < B) {
+    float s = 0.f;
+    for (int q = 0; q < kCtl / kWave; ++q) s += L.red[q * kFusedMaxB + tid];
+    L.inv_rms[tid] = 1.0f / sqrtf(s / (float)H + a.eps);
+  }
+  // every workgroup's hg is now announced: acquire before reading it (drops
+  // any line of an earlier step's hg from this XCD's caches)
   if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   stamp(a, 4);
+
+  // ================= phase B: router logits =================
   if (a.h_out && ni > 0)
     for (int q = tid; q < B * ni; q += kFT) {
       const int t = q / ni, il = q % ni;
       a.h_out[(size_t)t * H + i0 + il] = L.hg[t][il] * L.inv_rms[t];
     }
-  if (has_e0 || has_f) {  // uniform over the workgroup
-    // per token: this thread's partial dots [router row 0, row 1, S1, S3],
-    // wave-reduced, then the 8 wave totals summed in order
+  if (er[0] < E) {  // uniform over the workgroup
+    const bool two = er[1] < E;
+    const int nc = H >> 3;  // 8-element chunks c = tid + kFT*j
     for (int t = 0; t < B; ++t) {
       const float *hrow = a.hg + (size_t)t * H;
-      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+      float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < kRtrJ; ++j) {
+      for (int j = 0; j < kChunkJ; ++j) {
         const int c = tid + kFT * j;
-        if (c < (H >> 2)) {
-          const float4 hv = ld16f(hrow + 4 * c);
-          p0 = dot4(rt[0][j], hv, p0);
-          p1 = dot4(rt[1][j], hv, p1);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kShJ; ++j) {
-        const int c = tid + kFT * j;
-        if (has_f && c < (H >> 3)) {
+        if (c < nc) {
           const float4 h0 = ld16f(hrow + 8 * c), h1 = ld16f(hrow + 8 * c + 4);
           const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-          float w1f[8], w3f[8];
-          unpack8(sh[0][j], w1f);
-          unpack8(sh[1][j], w3f);
+          float wa[8];
+          as8(L.u.unit[0][2 * c], L.u.unit[0][2 * c + 1], wa);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            p2 = fmaf(w1f[q], hv[q], p2);
-            p3 = fmaf(w3f[q], hv[q], p3);
+          for (int k2 = 0; k2 < 8; ++k2) p0 = fmaf(wa[k2], hv[k2], p0);
+          if (two) {
+            as8(L.u.unit[1][2 * c], L.u.unit[1][2 * c + 1], wa);
+#pragma unroll
+            for (int k2 = 0; k2 < 8; ++k2) p1 = fmaf(wa[k2], hv[k2], p1);
           }
         }
       }
       p0 = wave_sum(p0);
       p1 = wave_sum(p1);
-      p2 = wave_sum(p2);
-      p3 = wave_sum(p3);
       if (lane == 0) {
-        float *r = L.red + (wv * kFusedMaxB + t) * 4;
-        r[0] = p0; r[1] = p1; r[2] = p2; r[3] = p3;
+        L.red[(wv * kFusedMaxB + t) * 2 + 0] = p0;
+        L.red[(wv * kFusedMaxB + t) * 2 + 1] = p1;
       }
     }
     __syncthreads();
-    if (tid < B) {
-      float q4[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q < kFWaves; ++q)
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) q4[k2] += L.red[(q * kFusedMaxB + tid) * 4 + k2];
-      const float inv = L.inv_rms[tid];
-      if (has_e0) {
-        const float l = q4[0] * inv;
-        put_tagged(a.logit + (size_t)tid * E + e0, l, tag);
-        if (a.logits_out) a.logits_out[(size_t)tid * E + e0] = l;
+    if (tid < 2 * B) {
+      const int q = tid & 1, t = tid >> 1;
+      if (q == 0 || two) {
+        float s = 0.f;
+        for (int v = 0; v < kFWaves; ++v) s += L.red[(v * kFusedMaxB + t) * 2 + q];
+        const float l = s * L.inv_rms[t];
+        put_tagged(a.logit + (size_t)t * E + er[q], l, tag);
+        if (a.logits_out) a.logits_out[(size_t)t * E + er[q]] = l;
       }
-      if (has_e1) {
-        const float l = q4[1] * inv;
-        put_tagged(a.logit + (size_t)tid * E + e1, l, tag);
-        if (a.logits_out) a.logits_out[(size_t)tid * E + e1] = l;
-      }
-      if (has_f) put_tagged(a.act_s + (size_t)tid * a.Fs + w, silu_mul(q4[2] * inv, q4[3] * inv), tag);
     }
   }
+  __syncthreads();   // the router rows in LDS are dead from here on
   stamp(a, 5);
 
   // ================= phase C =================
-  {
-    const int n = B * E;
-    constexpr int PER = kFusedBig / kFT;
-    uint64_t x[PER];
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int q = tid + r * kFT;
-      if (q < n) x[r] = ld_tagged(a.logit + q);
-    }
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int q = tid + r * kFT;
-      if (q < n) L.big[q] = finish_tagged(a.logit + q, x[r], tag, a.spin_limit, &L.bad);
-    }
-  }
+  if (ctl) gather_tagged(a.logit, L.u.logits, tid, kCtl, B * E, tag, a.spin_limit, &L.bad);
   __syncthreads();
   stamp(a, 7);
-  // top-k per token, one wave per token: lane l holds experts l, l+64, ...
-  for (int t = wv; t < B; t += kFWaves) {
+  // top-k per token on the control waves: lane l holds experts l, l+64, ...
+  for (int t = wv; ctl && t < B; t += kCtl / kWave) {
     constexpr int NC = kFusedMaxE / 64;
     float lv[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = lane + 64 * c;
-      lv[c] = e < E ? L.big[t * E + e] : -INFINITY;
+      lv[c] = e < E ? L.u.logits[t * E + e] : -INFINITY;
     }
     int my_idx = 0;
-    float my_s = 0.f, ssum = 0.f;
+    float my_l = 0.f;
     for (int j = 0; j < K; ++j) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
@@ -560,12 +668,13 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         if (bi == lane + 64 * c) lv[c] = -INFINITY;
-      const float s = 1.0f / (1.0f + expf(-bv));
-      ssum += s;
-      if (lane == j) { my_idx = bi; my_s = s; }
+      if (lane == j) { my_idx = bi; my_l = bv; }
     }
+    // scores of the k picks, renormalised (lane j holds pick j)
+    const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
+    const float ssum = wave_sum(s);
     if (lane < K) {
-      const float wgt = my_s / ssum;
+      const float wgt = s / ssum;
       L.sel[t * K + lane] = my_idx;
       L.selw[t * K + lane] = wgt;
       if (w == 0) {
@@ -610,28 +719,64 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   }
   __syncthreads();
   stamp(a, 8);
-  // routed gate/up: row pairs (active slot, ffn row) in contiguous blocks per workgroup
+  // gate/up items: routed (active slot, ffn row) pairs, then the shared
+  // expert's ffn rows; workgroup w takes items w, w + G, ... (so the heavier
+  // shared items, which carry every token, spread over the grid).  Rounds of
+  // 8 items: wave v takes the W1 (v even) or W3 (v odd) rows of items
+  // v/2 and 4 + v/2 of the round.
   {
-    const int n_act = L.n_active;
-    const int total = n_act * a.F;
-    const int per = (total + G - 1) / G;
-    const int rp0 = w * per, nrp = max(0, min(per, total - rp0));
-    for (int m = 0; m < nrp; m += kFWaves / 2) {
-      const int mm = m + (wv >> 1);
-      if (mm < nrp) {
-        const int slot = (rp0 + mm) / a.F, f = (rp0 + mm) % a.F;
-        by_tokens(L.act_cnt[slot], [&](auto nt) { routed_gateup_row<decltype(nt)::value>(a, L, slot, f); });
+    const int n_rt = L.n_active * a.F;
+    const int total = n_rt + a.Fs;
+    const int nit = w < total ? (total - w + G - 1) / G : 0;
+    auto item_row = [&](int k, int mat, GuRow &r) {
+      const int it = w + G * k;
+      if (it < n_rt) {
+        const int slot = it / a.F, f = it % a.F;
+        r.row = (mat ? a.w3 : a.w1) + ((size_t)L.act_exp[slot] * a.F + f) * H;
+        r.toks = L.pair_tok + L.act_off[slot];
+        r.cnt = L.act_cnt[slot];
+      } else {
+        r.row = (mat ? a.s3 : a.s1) + (size_t)(it - n_rt) * H;
+        r.toks = nullptr;
+        r.cnt = B;
+      }
+    };
+    for (int k0 = 0; k0 < nit; k0 += 8) {
+      const int ka = k0 + (wv >> 1), kb = k0 + 4 + (wv >> 1), mat = wv & 1;
+      GuRow ra, rb;
+      if (ka < nit) item_row(ka, mat, ra);
+      if (kb < nit) item_row(kb, mat, rb);
+      if (ka < nit) {
+        const int nt = max(ra.cnt, rb.row ? rb.cnt : 0);
+        by_tokens(nt, [&](auto ntc) {
+          constexpr int NT = decltype(ntc)::value;
+          float sa[NT], sb[NT];
+          gateup_two<NT>(a, ra, rb, sa, sb);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (lane == t) {
+              L.uv[wv >> 1][mat][t] = sa[t];
+              L.uv[4 + (wv >> 1)][mat][t] = sb[t];
+            }
+          }
+        });
       }
       __syncthreads();
-      // combine: thread (pair-in-round pp, token j)
-      const int pp = tid >> 3, j = tid & 7;
-      if (pp < kFWaves / 2 && m + pp < nrp) {
-        const int s2 = (rp0 + m + pp) / a.F, f2 = (rp0 + m + pp) % a.F;
-        const int c2 = L.act_cnt[s2], o2 = L.act_off[s2];
-        if (j < c2) {
-          const int t = L.pair_tok[o2 + j];
-          const float u = L.uv[2 * pp][j] * L.inv_rms[t], v = L.uv[2 * pp + 1][j] * L.inv_rms[t];
-          put_tagged(a.act + (size_t)(o2 + j) * a.F + f2, silu_mul(u, v), tag);
+      // combine: thread (item-in-round is, token j)
+      const int is = tid >> 3, j = tid & 7;
+      if (is < 8 && k0 + is < nit) {
+        const int it = w + G * (k0 + is);
+        if (it < n_rt) {
+          const int s2 = it / a.F, f2 = it % a.F;
+          const int c2 = L.act_cnt[s2], o2 = L.act_off[s2];
+          if (j < c2) {
+            const int t = L.pair_tok[o2 + j];
+            const float u = L.uv[is][0][j] * L.inv_rms[t], v = L.uv[is][1][j] * L.inv_rms[t];
+            put_tagged(a.act + (size_t)(o2 + j) * a.F + f2, silu_mul(u, v), tag);
+          }
+        } else if (j < B) {
+          const float u = L.uv[is][0][j] * L.inv_rms[j], v = L.uv[is][1][j] * L.inv_rms[j];
+          put_tagged(a.act_s + (size_t)j * a.Fs + (it - n_rt), silu_mul(u, v), tag);
         }
       }
       __syncthreads();
@@ -646,66 +791,61 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     by_lpg(a.F, [&](auto lpg) {
       constexpr int LPG = decltype(lpg)::value;
       const Down<LPG> d{a, L, i0, ni, item0, ni > 0 ? (B + P - item0) * ni : 0};
-      uint4 wq[Down<LPG>::R];
-      d.issue(0, wq);  // static weights: requested before the wait
-      // gather every SwiGLU activation into LDS (routed [P][F], shared [B][Fs])
-      {
-        constexpr int PER = kFusedBig / kFT;
-        const int n = P * a.F;
-        uint64_t x[PER];
-#pragma unroll
-        for (int r = 0; r < PER; ++r) {
-          const int q = tid + r * kFT;
-          if (q < n) x[r] = ld_tagged(a.act + q);
-        }
-        const int ns = B * a.Fs;
-        constexpr int PERS = kFusedActS / kFT;
-        uint64_t xs[PERS];
-#pragma unroll
-        for (int r = 0; r < PERS; ++r) {
-          const int q = tid + r * kFT;
-          if (q < ns) xs[r] = ld_tagged(a.act_s + q);
-        }
-#pragma unroll
-        for (int r = 0; r < PER; ++r) {
-          const int q = tid + r * kFT;
-          if (q < n) L.big[q] = finish_tagged(a.act + q, x[r], tag, a.spin_limit, &L.bad);
-        }
-#pragma unroll
-        for (int r = 0; r < PERS; ++r) {
-          const int q = tid + r * kFT;
-          if (q < ns) L.act_s[q] = finish_tagged(a.act_s + q, xs[r], tag, a.spin_limit, &L.bad);
-        }
+      if (!ctl) {
+        d.stage();   // the first down-projection rows (static weights) -> LDS
+      } else {
+        // every SwiGLU activation -> LDS
+        gather_tagged(a.act, L.u.d.act, tid, kCtl, P * a.F, tag, a.spin_limit, &L.bad);
+        gather_tagged(a.act_s, L.u.d.act_s, tid, kCtl, B * a.Fs, tag, a.spin_limit, &L.bad);
       }
       __syncthreads();
       stamp(a, 10);
-      const int nr = d.rounds();
-      for (int r = 0; r < nr; ++r) {
-        if (r > 0) d.issue(r, wq);
-        d.consume(r, wq);
-      }
+      d.compute();
     });
     __syncthreads();
     for (int q = tid; q < B * ni; q += kFT) {
       const int t = q / ni, il = q % ni;
-      float y = a.Fs > 0 ? L.contrib[t * kFusedMaxSlice + il] : 0.f;
-      for (int r = 0; r < K; ++r) y += L.contrib[(B + L.pos[t * K + r]) * kFusedMaxSlice + il];
+      float y = a.Fs > 0 ? L.u.d.contrib[t * kFusedMaxSlice + il] : 0.f;
+      for (int r = 0; r < K; ++r) y += L.u.d.contrib[(B + L.pos[t * K + r]) * kFusedMaxSlice + il];
       a.moe_out[(size_t)t * H + i0 + il] = y;
     }
   }
   stamp(a, 11);
-  // attention input projection (independent of everything else)
-  {
-    const int rq = (a.Dq + G - 1) / G;
-    const int j0 = w * rq, nj = max(0, min(rq, a.Dq - j0));
-    if (nj > 0) by_tokens(B, [&](auto nt) { qkv_rows<decltype(nt)::value>(a, j0, nj); });
-  }
   __syncthreads();
   stamp(a, 3);
   if (tid == 0) {
     if (L.bad) atomicOr(a.status, 1u);
     if (w == 0) *a.epoch = tag;   // every workgroup has read this step's epoch (all pss seen)
   }
+}
+
+// The attention input projection of the single-launch path, as its own small
+// kernel on the handle's second stream: it depends on nothing else in the
+// step, uses the registers and LDS the persistent kernel leaves free on each
+// CU, and fills HBM time the persistent kernel spends waiting on hand-offs
+// (wireai.ir, "Four key changes behind the jump": the small-batch
+// projection of bullet 1, run on a side stream as bullet 3 runs the shared
+// expert).
+// One wave per row of Wqkv.
+template <int NT>
+__global__ void __launch_bounds__(64) qkv_side_kernel(FusedArgs a) {
+  const int j = blockIdx.x, lane = threadIdx.x;
+  const ActBf16Rows act{a.x, a.H, a.B - 1};
+  const uint16_t *row[1] = {a.w_qkv + (size_t)j * a.H};
+  float s[1][NT];
+  wave_rows_dot<1, NT, 4>(row, 0, a.H >> 3, act, s);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (lane == t && t < a.B) a.qkv[(size_t)t * a.Dq + j] = s[0][t];
+}
+
+hipError_t launch_qkv_side(const FusedArgs &a, hipStream_t s) {
+  const dim3 grid(a.Dq), block(64);
+  if (a.B <= 1) hipLaunchKernelGGL(qkv_side_kernel<1>, grid, block, 0, s, a);
+  else if (a.B <= 2) hipLaunchKernelGGL(qkv_side_kernel<2>, grid, block, 0, s, a);
+  else if (a.B <= 4) hipLaunchKernelGGL(qkv_side_kernel<4>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(qkv_side_kernel<8>, grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s) {

@@ -31,7 +31,9 @@ constexpr int kFusedMaxPairs = 64;    // B * k
 constexpr int kFusedBig = 8192;       // B * E logits, then B * k * F activations
 constexpr int kFusedActS = 4096;      // B * Fs shared activations
 constexpr int kFusedMaxH = 8192;      // router / shared rows held in registers
-constexpr int kFusedMaxE = 512;       // at most 2 router rows per workgroup (with 256 CUs)
+constexpr int kFusedMaxE = 512;       // experts (top-k candidates per lane)
+constexpr int kFusedMaxGrid = 256;    // workgroups (one poll per control thread)
+constexpr int kFusedW2Words = 4096;   // 16-byte words of down-projection rows staged in LDS (64 KB)
 
 struct FusedArgs {
   const uint16_t *x, *w_qkv;
@@ -106,6 +108,7 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t s);
 hipError_t launch_gateup(const GateUpArgs &a, int grid, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s);
+hipError_t launch_qkv_side(const FusedArgs &a, hipStream_t s);
 // Resident workgroups of the single-launch kernel per CU (0 if it cannot run).
 int fused_blocks_per_cu();
 

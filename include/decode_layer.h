@@ -77,9 +77,12 @@ enum {
  *                   resident, phases handing data to each other through
  *                   device memory (the shared expert's and the router's
  *                   weights stream while the norm is being exchanged).
- *                   Available when hidden <= 8192 and <= 32 * (number of
- *                   CUs), n_experts <= 512 and <= 2 * CUs, shared_ffn == 0 or
- *                   == expert_ffn and <= CUs; for batches up to
+ *                   The attention input projection runs beside it as a
+ *                   small kernel on the handle's second stream.
+ *                   Available on devices with at most 256 CUs when
+ *                   hidden <= 8192 and <= 32 * CUs, n_experts <= 512 and
+ *                   <= 2 * CUs, and shared_ffn == 0 or == expert_ffn; for
+ *                   batches up to
  *                   decode_layer_single_max_batch(), which is at most 8 and
  *                   also bounded by B*k <= 64, B*E <= 8192, B*k*F <= 8192 and
  *                   B*Fs <= 4096.
@@ -153,7 +156,8 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
 
 /* Enqueue one layer-step on `hip_stream` (a hipStream_t; NULL = the null
  * stream) and return without synchronising.  Device work: on the single-launch
- * path one kernel on `hip_stream`; on the multi-launch path up to five kernel
+ * path one persistent kernel on `hip_stream` and the attention input
+ * projection on the handle's second stream; on the multi-launch path up to five kernel
  * launches, four on `hip_stream` and one (the shared expert's gate/up
  * projection) on the handle's second stream, which is forked from and joined
  * back into `hip_stream` with events.  Either can be captured in a HIP graph.
@@ -216,11 +220,10 @@ int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
  * device buffer of decode_layer_grid(h) * decode_layer_trace_points() uint64
  * values (caller-owned, 16-byte aligned), every later single-launch step has
  * thread 0 of each workgroup w write the device wall clock (100 MHz) into
- * buffer[w * points + p] at these points: 0 start, 1 out-projection done,
- * 2 norm partials published and phase-B weights requested, 4 norm known,
- * 5 logits and shared activations published, 7 all logits read, 13 top-k
- * done, 8 expert lists built, 9 routed activations published,
- * 10 activations read, 11 y written, 3 end (after qkv); others unused.
+ * buffer[w * points + p] at these points: 0 start, 1 out-projection done and
+ * norm partials published, 4 norm known, 5 logits published, 7 all logits
+ * read, 13 top-k done, 8 expert lists built, 9 SwiGLU activations
+ * published, 10 activations read, 11 y written, 3 end; others unused.
  * NULL turns it off.  Returns DL_OK or DL_ERR_INVALID_ARG. */
 int decode_layer_set_trace(decode_layer *h, void *device_buffer);
 int decode_layer_trace_points(void);
