@@ -68,7 +68,15 @@ def algorithmic_bytes(layer) -> dict:
     weights = 2 * (Dq * H + H * Do + H) + 4 * E * H + n_act * 3 * 2 * F * H + 3 * 2 * Fs * H
     io = 2 * B * (H + Do) + 4 * B * H * 2 + 4 * B * Dq + 4 * B * E + 8 * pairs + 4 * B * H
     b["step"] = weights + io
-    b["single_launch_step"] = b["step"]
+    # the single-launch kernel does all but the attention input projection,
+    # which runs beside it on the second stream
+    b["qkv_side"] = 2 * Dq * H + 2 * B * H + 4 * B * Dq
+    b["single_launch_step"] = b["step"] - b["qkv_side"]
+    b["batched_proj"] = 2 * (Dq * H + H * Do + H) + 2 * B * (H + Do) + 4 * B * H * 3
+    b["batched_router"] = 4 * E * H + 4 * B * H + 4 * B * Dq
+    b["batched_topk_permute"] = 4 * B * H * 2 + 4 * B * E + 8 * pairs
+    b["batched_gateup"] = b["shared_gateup"] + b["expert_gateup"] - 4 * B * H
+    b["batched_down"] = b["expert_down_combine"]
     b["step_flops"] = 2 * B * (Dq * H + H * Do + E * H) + 2 * pairs * 3 * F * H + 2 * B * 3 * Fs * H
     return b
 
@@ -110,7 +118,9 @@ def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True, path=0):
     copies = make_copies(layer, n_copies)
     cfg = sdev.config_of(layer, path=path)
     handles = [DecodeLayer(cfg, w) for w in copies]
-    single = path != 1 and layer.shape.batch <= handles[0].single_max_batch
+    single = path in (0, 2) and layer.shape.batch <= handles[0].single_max_batch
+    batched = not single and any(k.startswith("batched") for k in _launch_probe(handles[0], layer))
+    path_name = "single" if single else ("batched" if batched else "multi")
     x, attn, resid = sdev.upload_inputs(layer)
     outs = [h.alloc_outputs(layer.shape.batch) for h in handles]
     ios = [h.make_io(x, attn, resid, o) for h, o in zip(handles, outs)]
@@ -169,18 +179,19 @@ def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True, path=0):
 
     kern = {}
     if want_kernels:
-        for h in handles:
-            h.set_profiling(True)
+        # each profiled step is queued behind an unprofiled one, so its first
+        # event is taken as the previous step ends, not on an idle GPU
         acc = {}
-        for i in range(warmup):
+        for i in range(warmup + steps):
             run(i)
-        torch.cuda.synchronize()
-        for i in range(steps):
-            run(i)
-            for k_, v in handles[i % n_copies].kernel_times_ms().items():
-                acc.setdefault(k_, []).append(v)
-        for h in handles:
-            h.set_profiling(False)
+            hp = handles[(i + 1) % n_copies]
+            hp.set_profiling(True)
+            run(i + 1)
+            times = hp.kernel_times_ms()
+            hp.set_profiling(False)
+            if i >= warmup:
+                for k_, v in times.items():
+                    acc.setdefault(k_, []).append(v)
         kern = {k_: float(np.mean(v)) for k_, v in acc.items()}
     for h in handles:
         assert h.status() == 0, "a single-launch hand-off wait expired"
@@ -188,11 +199,24 @@ def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True, path=0):
            "copies": n_copies, "eager_us": eager_ms * 1e3, "graph_us": graph_ms * 1e3,
            "bytes": nbytes, "kernel_us": {k_: v * 1e3 for k_, v in kern.items()},
            "active_experts": int(len(layer.touched_experts())),
-           "path": "single" if single else "multi", "launches": 1 if single else 5}
+           "path": path_name, "launches": 1 if single else 5}
     del handles, copies
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res, layer
+
+
+def _launch_probe(h, layer):
+    """Names of the launches one step of this batch makes on handle `h`."""
+    import torch
+    from synth import device as sdev
+    x, attn, resid = sdev.upload_inputs(layer)
+    h.set_profiling(True)
+    h.step(x, attn, resid)
+    names = list(h.kernel_times_ms())
+    h.set_profiling(False)
+    torch.cuda.synchronize()
+    return names
 
 
 # ----------------------------------------------------------------- CPU baseline
@@ -242,6 +266,9 @@ def main():
     ap.add_argument("--no-batches", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="run a few eager headline steps and a 1 GiB negate of known size "
+                         "(for hardware-counter runs under rocprofv3 --pmc), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -253,6 +280,9 @@ def main():
         sys.exit(1)
     import decode_step_moe_amd  # noqa: F401  (fails loudly without the built library)
 
+    if args.counter_pass:
+        counter_pass(args.steps)
+        return
     head, layer = time_config(HEADLINE_CFG, args.steps, args.warmup, args.copies)
     multi, _ = time_config(HEADLINE_CFG, args.steps, args.warmup, args.copies, want_kernels=False,
                            path=1)
@@ -293,7 +323,7 @@ def main():
                               "eager_us": round(multi["eager_us"], 3), "launches_per_step": 5},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": b[dom],
+                     "traffic": counted_traffic(dom, head["workload"]), "bytes_per_launch": b[dom],
                      "avg_launch_us": round(kern[dom], 3)},
         "kernels_us": {k_: round(v, 3) for k_, v in kern.items()},
         "batches": batches,
@@ -301,6 +331,79 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def counter_pass(steps):
+    """Eager steps of the batch-1 and batch-64 workloads, then a plain
+    elementwise pass of known size.
+
+    Under `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE) the negate reads and
+    writes exactly COPY_BYTES each; the ratio of its counter to that size is
+    the factor that turns a layer-step kernel's counter into HBM bytes."""
+    import torch
+    from decode_step_moe_amd import DecodeLayer
+    from synth import device as sdev, routing, gen
+
+    for cfg_id in (HEADLINE_CFG, 3):
+        raw = gen.draw(cfg_id)
+        layer = routing.shape_router(raw, routing.stored_h(cfg_id))
+        n_copies = max(4, int(np.ceil(1.0e9 / algorithmic_bytes(layer)["step"])))
+        copies = make_copies(layer, n_copies)
+        handles = [DecodeLayer(sdev.config_of(layer), w) for w in copies]
+        x, attn, resid = sdev.upload_inputs(layer)
+        outs = [h.alloc_outputs(layer.shape.batch) for h in handles]
+        ios = [h.make_io(x, attn, resid, o) for h, o in zip(handles, outs)]
+        stream = torch.cuda.current_stream()
+        for i in range(max(steps, n_copies)):
+            handles[i % n_copies].step_io(ios[i % n_copies], stream)
+        torch.cuda.synchronize()
+        for h in handles:
+            assert h.status() == 0
+        log(f"[counter-pass] {layer.shape.name}: {max(steps, n_copies)} layer-steps over {n_copies} copies")
+        del handles, copies, outs, ios
+        torch.cuda.empty_cache()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[counter-pass] 3 negates of {COPY_BYTES} bytes")
+
+
+COPY_BYTES = 1 << 30
+
+# Sources each measured kernel is built from: a counter summary applies to
+# the kernel only while these files are unchanged.
+KERNEL_SOURCES = {
+    "single_launch_step": ("fused.hip", "common.h", "kernels.h"),
+    "batched_gateup": ("batched.hip", "common.h", "kernels.h"),
+    "batched_down": ("batched.hip", "common.h", "kernels.h"),
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "decode_step_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(kernel, workload):
+    """HBM bytes per launch from the committed hardware-counter summary of this
+    kernel and workload, or None if there is none or the kernel has changed."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.txt")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return int(fields["hbm_bytes_per_launch"])
 
 
 def _summary(r):
@@ -311,7 +414,9 @@ def _summary(r):
             "tok_per_s_per_shard": round(r["batch"] / (us * 1e-6), 1),
             "active_experts": r["active_experts"], "copies": r["copies"],
             "path": r["path"], "launches_per_step": r["launches"],
-            "kernels_us": {k_: round(v, 3) for k_, v in r["kernel_us"].items()}}
+            "kernels_us": {k_: round(v, 3) for k_, v in r["kernel_us"].items()},
+            "kernels_gbps": {k_: round(r["bytes"][k_] / (v * 1e-6) / 1e9, 1)
+                             for k_, v in r["kernel_us"].items() if k_ in r["bytes"]}}
 
 
 if __name__ == "__main__":

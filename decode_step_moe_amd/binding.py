@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdecode_layer.so")
 
 DL_OK, DL_ERR_INVALID_ARG, DL_ERR_UNSUPPORTED, DL_ERR_HIP, DL_ERR_OOM = 0, -1, -2, -3, -4
-DL_PATH_AUTO, DL_PATH_MULTI, DL_PATH_SINGLE = 0, 1, 2
+DL_PATH_AUTO, DL_PATH_MULTI, DL_PATH_SINGLE, DL_PATH_BATCHED = 0, 1, 2, 3
 _ERR_NAMES = {0: "DL_OK", -1: "DL_ERR_INVALID_ARG", -2: "DL_ERR_UNSUPPORTED", -3: "DL_ERR_HIP",
               -4: "DL_ERR_OOM"}
 
@@ -182,7 +182,9 @@ class DecodeLayer:
             pass
 
     LAUNCH_NAMES = ("proj_out_in", "shared_gateup", "router_topk_permute", "expert_gateup",
-                    "expert_down_combine", "single_launch_step")
+                    "expert_down_combine", "single_launch_step",
+                    "batched_proj", "batched_router", "batched_topk_permute", "batched_gateup",
+                    "batched_down")
 
     @property
     def single_max_batch(self) -> int:

@@ -169,6 +169,139 @@ __device__ __forceinline__ void stream_rows_bf16(const uint16_t *const (&w)[NR],
   }
 }
 
+// ---- row GEMV building blocks -------------------------------------------------
+struct ActBf16Rows {  // bf16 [tokens][ld], token index clamped to tmax
+  const uint16_t *base;
+  int ld, tmax;
+  __device__ __forceinline__ void load8(int t, int k, float (&v)[8]) const {
+    int tt = t < tmax ? t : tmax;
+    unpack8(ld16(base + (size_t)tt * ld + k), v);
+  }
+};
+
+template <int NT>
+struct HgGather {  // fp32 hg rows of a token list
+  const float *base;
+  int ld;
+  int tok[NT];
+  __device__ __forceinline__ void load8(int t, int k, float (&v)[8]) const {
+    const float *p = base + (size_t)tok[t] * ld + k;
+    float4 u = ld16f(p), w = ld16f(p + 4);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+  }
+};
+
+// One wave: dot products of NR bf16 weight rows (16-byte chunks [cbeg, cend)
+// of each, i.e. elements [8 cbeg, 8 cend)) with NT activation rows.  Lane l
+// takes chunks cbeg + l, cbeg + l + 64, ...; up to CPB chunks of every row are
+// loaded before any is consumed.  The sums come back in every lane.
+template <int NR, int NT, int CPB, class Act>
+__device__ __forceinline__ void wave_rows_dot(const uint16_t *const (&w)[NR], int cbeg, int cend,
+                                              const Act &act, float (&out)[NR][NT]) {
+  const int lane = threadIdx.x & 63;
+  float acc[NR][NT];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
+  for (int c0 = cbeg; c0 < cend; c0 += CPB * kWave) {
+    uint4 wv[CPB][NR];
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int c = c0 + lane + kWave * u;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) wv[u][r] = c < cend ? ld_stream16(w[r] + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int c = c0 + lane + kWave * u;
+      if (c < cend) {
+        float a[NT][8];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) act.load8(t, c * 8, a[t]);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          float wf[8];
+          unpack8(wv[u][r], wf);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][t] = fmaf(wf[e], a[t][e], acc[r][t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) out[r][t] = wave_sum(acc[r][t]);
+}
+
+// ---- DPP wave arg-max ---------------------------------------------------------
+// (value, index) packed into one 64-bit key that orders like "larger value,
+// then smaller index": the float's bits mapped to an order-preserving
+// unsigned word in the high half, the inverted index in the low half.  The
+// wave maximum of the keys is taken with lane permutes (no branches).
+__device__ __forceinline__ uint64_t rank_key(float v, int i) {
+  unsigned u = __float_as_uint(v == 0.f ? 0.f : v);  // -0 ranks as +0 (they compare equal)
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)i);
+}
+__device__ __forceinline__ void key_unpack(uint64_t k, float &v, int &i) {
+  unsigned u = (unsigned)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  v = __uint_as_float(u);
+  i = (int)(0xffffffffu - (unsigned)k);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  // rows outside ROWS (and lanes with no source) compare against themselves
+  const int lo = (int)(unsigned)k, hi = (int)(unsigned)(k >> 32);
+  const unsigned olo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+  const unsigned ohi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > k ? o : k;
+}
+// Largest key over the wave; result uniform.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max_step<kDppXor1, 0xf>(k);
+  k = dpp_max_step<kDppXor2, 0xf>(k);
+  k = dpp_max_step<kDppHalfMirror, 0xf>(k);
+  k = dpp_max_step<kDppMirror, 0xf>(k);  // rows of 16 uniform
+  k = dpp_max_step<0x142, 0xa>(k);       // row_bcast:15 -> rows 1, 3
+  k = dpp_max_step<0x143, 0xc>(k);       // row_bcast:31 -> rows 2, 3
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)k, 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Top-k over one wave.  Lane l offers the candidates e = l + 64 c (c < NC,
+// e < E) with values lv[c]; lane j < K receives the j-th pick in the order
+// "larger value first, then smaller index".  The picks are K distinct
+// indices below E whatever the values (NaN ranks above +inf), because a key
+// never equals 0, the mark of an absent or taken candidate.  Needs K <= E.
+template <int NC>
+__device__ __forceinline__ void wave_topk(const float (&lv)[NC], int E, int K, int &my_idx, float &my_v) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) key[c] = lane + 64 * c < E ? rank_key(lv[c], lane + 64 * c) : 0ull;
+  uint64_t mine = 0;
+  for (int j = 0; j < K; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) best = key[c] > best ? key[c] : best;
+    best = wave_max_key(best);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) key[c] = key[c] == best ? 0ull : key[c];
+    mine = lane == j ? best : mine;
+  }
+  key_unpack(mine, my_v, my_idx);
+}
+
+__device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }
+
 // ---- cross-workgroup hand-off ------------------------------------------------
 // Every workgroup of a phase publishes its partial results, then counts
 // itself in `counter`; the workgroup that arrives last sees every other

@@ -120,116 +120,6 @@ __device__ __forceinline__ void gather_tagged(const uint64_t *src, float *dst, i
   }
 }
 
-// ---- DPP wave arg-max ---------------------------------------------------------
-// (value, index) packed into one 64-bit key that orders like "larger value,
-// then smaller index": the float's bits mapped to an order-preserving
-// unsigned word in the high half, the inverted index in the low half.  The
-// wave maximum of the keys is taken with lane permutes (no branches).
-__device__ __forceinline__ uint64_t rank_key(float v, int i) {
-  unsigned u = __float_as_uint(v == 0.f ? 0.f : v);  // -0 ranks as +0 (they compare equal)
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)i);
-}
-__device__ __forceinline__ void key_unpack(uint64_t k, float &v, int &i) {
-  unsigned u = (unsigned)(k >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-  v = __uint_as_float(u);
-  i = (int)(0xffffffffu - (unsigned)k);
-}
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
-  // rows outside ROWS (and lanes with no source) compare against themselves
-  const int lo = (int)(unsigned)k, hi = (int)(unsigned)(k >> 32);
-  const unsigned olo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
-  const unsigned ohi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > k ? o : k;
-}
-// Largest (value, index) over the wave by the order above; result uniform.
-__device__ __forceinline__ void wave_argmax(float &v, int &i) {
-  uint64_t k = rank_key(v, i);
-  k = dpp_max_step<kDppXor1, 0xf>(k);
-  k = dpp_max_step<kDppXor2, 0xf>(k);
-  k = dpp_max_step<kDppHalfMirror, 0xf>(k);
-  k = dpp_max_step<kDppMirror, 0xf>(k);  // rows of 16 uniform
-  k = dpp_max_step<0x142, 0xa>(k);       // row_bcast:15 -> rows 1, 3
-  k = dpp_max_step<0x143, 0xc>(k);       // row_bcast:31 -> rows 2, 3
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)k, 63);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(k >> 32), 63);
-  key_unpack(((uint64_t)hi << 32) | lo, v, i);
-}
-
-// ---- activations ------------------------------------------------------------
-struct ActBf16Rows {  // bf16 [tokens][ld], token index clamped to tmax
-  const uint16_t *base;
-  int ld, tmax;
-  __device__ __forceinline__ void load8(int t, int k, float (&v)[8]) const {
-    int tt = t < tmax ? t : tmax;
-    unpack8(ld16(base + (size_t)tt * ld + k), v);
-  }
-};
-
-template <int NT>
-struct HgGather {  // fp32 hg rows of a token list
-  const float *base;
-  int ld;
-  int tok[NT];
-  __device__ __forceinline__ void load8(int t, int k, float (&v)[8]) const {
-    const float *p = base + (size_t)tok[t] * ld + k;
-    float4 u = ld16f(p), w = ld16f(p + 4);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-    v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
-  }
-};
-
-// One wave: dot products of NR bf16 weight rows (16-byte chunks [cbeg, cend)
-// of each, i.e. elements [8 cbeg, 8 cend)) with NT activation rows.  Lane l
-// takes chunks cbeg + l, cbeg + l + 64, ...; up to CPB chunks of every row are
-// loaded before any is consumed.  The sums come back in every lane.
-template <int NR, int NT, int CPB, class Act>
-__device__ __forceinline__ void wave_rows_dot(const uint16_t *const (&w)[NR], int cbeg, int cend,
-                                              const Act &act, float (&out)[NR][NT]) {
-  const int lane = threadIdx.x & 63;
-  float acc[NR][NT];
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
-  for (int c0 = cbeg; c0 < cend; c0 += CPB * kWave) {
-    uint4 wv[CPB][NR];
-#pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int c = c0 + lane + kWave * u;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) wv[u][r] = c < cend ? ld_stream16(w[r] + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int c = c0 + lane + kWave * u;
-      if (c < cend) {
-        float a[NT][8];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) act.load8(t, c * 8, a[t]);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          float wf[8];
-          unpack8(wv[u][r], wf);
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][t] = fmaf(wf[e], a[t][e], acc[r][t]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) out[r][t] = wave_sum(acc[r][t]);
-}
-
-__device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }
-
 __device__ __forceinline__ void as8(const uint4 &a, const uint4 &b, float (&f)[8]) {
   f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
   f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
@@ -654,22 +544,11 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = lane + 64 * c;
-      lv[c] = e < E ? L.u.logits[t * E + e] : -INFINITY;
+      lv[c] = e < E ? L.u.logits[t * E + e] : 0.f;
     }
-    int my_idx = 0;
-    float my_l = 0.f;
-    for (int j = 0; j < K; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        if (lv[c] > bv) { bv = lv[c]; bi = lane + 64 * c; }   // c ascending: ties keep the lower id
-      wave_argmax(bv, bi);
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        if (bi == lane + 64 * c) lv[c] = -INFINITY;
-      if (lane == j) { my_idx = bi; my_l = bv; }
-    }
+    int my_idx;
+    float my_l;
+    wave_topk<NC>(lv, E, K, my_idx, my_l);
     // scores of the k picks, renormalised (lane j holds pick j)
     const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
     const float ssum = wave_sum(s);

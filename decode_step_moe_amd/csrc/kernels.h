@@ -63,6 +63,46 @@ struct FusedArgs {
 };
 constexpr int kTracePoints = 16;
 
+// Batched path (batched.hip): five launches for batches the single-launch
+// path does not take (up to 64 tokens); MFMA wherever 16 or more tokens share
+// a weight matrix.  Needs H % 512 == 0 and Do % 128 == 0.
+constexpr int kBatchQkvSplit = 4;     // K splits of the attention input projection
+constexpr int kBatchRtrExperts = 32;  // router experts per workgroup
+constexpr int kBatchRtrK = 256;       // router K per workgroup
+constexpr int kBatchMfmaMin = 16;     // an expert with at least this many tokens uses MFMA
+constexpr int kBatchGateupGrid = 1024;
+constexpr int kBatchLaunches = 5;
+
+struct BatchArgs {
+  const uint16_t *x, *w_qkv;
+  float *qkv;
+  const uint16_t *attn, *w_o, *gain;
+  const float *resid_in;
+  float *resid_out;
+  const float *w_router;
+  float *logits_out;
+  int32_t *topk_idx;
+  float *topk_w;
+  const uint16_t *w1, *w3, *w2, *s1, *s3, *s2;
+  float *moe_out, *h_out;
+  // scratch
+  float *hg;          // [B][H]        g * r1
+  float *ss_part;     // [H/16][B]     partial sums of r1^2 per out-projection workgroup
+  float *qkv_part;    // [kBatchQkvSplit][B][Dq]
+  float *rlog_part;   // [H/kBatchRtrK][B][E]  router dot products per K chunk
+  float *hn;          // [B][H]        normalised h (fp32)
+  uint16_t *hp;       // [2][B][H]     h as bf16 hi + lo planes (MFMA operands)
+  float *act;         // [B*k][F]      routed SwiGLU activations, pairs grouped by expert
+  float *act_s;       // [B][Fs]
+  int *n_active;      // [1]
+  int *act_exp, *act_cnt, *act_off;  // [E] per active slot
+  int *pair_tok;      // [B*k]
+  float *pair_w;      // [B*k]
+  unsigned *counter;  // [1] arrivals of the top-k workgroups (re-armed by the last)
+  int B, H, Dq, Do, E, K, F, Fs;
+  float eps;
+};
+
 struct ProjArgs {
   const uint16_t *x, *w_qkv;
   float *qkv;
@@ -109,6 +149,8 @@ hipError_t launch_gateup(const GateUpArgs &a, int grid, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s);
 hipError_t launch_qkv_side(const FusedArgs &a, hipStream_t s);
+// ev: kBatchLaunches event pairs recorded around the launches, or nullptr.
+hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]);
 // Resident workgroups of the single-launch kernel per CU (0 if it cannot run).
 int fused_blocks_per_cu();
 

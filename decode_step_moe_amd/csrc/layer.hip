@@ -44,12 +44,22 @@ int single_max_batch_for(const decode_layer_config &c, int grid, int slice) {
 
 SinglePlan plan_single(const decode_layer_config &c, int n_cu) {
   SinglePlan p;
-  if (c.path == DL_PATH_MULTI || n_cu < 1) return p;
+  if (c.path == DL_PATH_MULTI || c.path == DL_PATH_BATCHED || n_cu < 1) return p;
   p.grid = n_cu;
   int sl = (c.hidden + n_cu - 1) / n_cu;
   p.slice = (sl + 3) & ~3;
   p.max_batch = single_max_batch_for(c, p.grid, p.slice);
   return p;
+}
+
+// Batched path: shape requirements of its tilings (K splits of 4 waves x 32
+// for the projections and gate/up, 256-wide router K chunks).
+bool batched_ok(const decode_layer_config &c) { return c.hidden % 512 == 0 && c.attn_dim % 128 == 0; }
+
+// Whether some step of this configuration takes the batched path.
+bool batched_used(const decode_layer_config &c, const SinglePlan &sp) {
+  if (c.path == DL_PATH_BATCHED) return true;
+  return c.path == DL_PATH_AUTO && batched_ok(c) && c.max_batch > sp.max_batch;
 }
 
 struct Scratch {
@@ -65,16 +75,21 @@ struct Scratch {
   int *n_active = nullptr;    // [1]
   float *act = nullptr;       // [maxB*k][F]
   float *act_s = nullptr;     // [maxB][Fs]
-  unsigned *counters = nullptr;  // [2]: out-projection, router
+  unsigned *counters = nullptr;  // [3]: out-projection, router, batched top-k
   // single-launch hand-off arrays (tagged 64-bit values)
   uint64_t *pss = nullptr, *logit = nullptr, *act64 = nullptr, *act_s64 = nullptr;
   unsigned *epoch = nullptr;     // [1] steps completed
   unsigned *status = nullptr;    // [1]
+  // batched path (empty when no step can take it)
+  float *qkv_part = nullptr;     // [kBatchQkvSplit][maxB][Dq]
+  float *rlog_part = nullptr;    // [H/kBatchRtrK][maxB][E]
+  float *hn = nullptr;           // [maxB][H]
+  uint16_t *hp = nullptr;        // [2][maxB][H]
 };
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-constexpr int kNumBuf = 19;
+constexpr int kNumBuf = 23;
 struct Layout {
   size_t off[kNumBuf];
   size_t total;
@@ -85,13 +100,16 @@ int nblk_o_of(const decode_layer_config &c) { return (c.hidden + kORowsPerBlock 
 Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
   const size_t B = c.max_batch, H = c.hidden, E = c.n_experts, K = c.top_k;
   const size_t Bs = sp.max_batch, G = sp.grid;
+  const size_t Bb = batched_used(c, sp) ? B : 0;
   const size_t sizes[kNumBuf] = {
       B * H * 4, (size_t)nblk_o_of(c) * B * 4, B * 4, B * E * 4, B * K * 4, B * K * 4,
       E * 4, E * 4, E * 4, 4, B * K * (size_t)c.expert_ffn * 4, B * (size_t)(c.shared_ffn > 0 ? c.shared_ffn : 1) * 4,
-      2 * 4,
+      3 * 4,
       // single-launch arrays (empty when the path is unavailable)
       G * Bs * 8, Bs * E * 8, Bs * K * (size_t)c.expert_ffn * 8, Bs * (size_t)c.shared_ffn * 8,
-      4, 4};
+      4, 4,
+      // batched arrays
+      (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2};
   Layout L;
   size_t o = 0;
   for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
@@ -174,8 +192,9 @@ static int check_config(const decode_layer_config *c, decode_layer *h) {
   if (c->score_fn != 0) return fail(h, DL_ERR_UNSUPPORTED, "score_fn=%d: only 0 (sigmoid) is supported", c->score_fn);
   if (c->renormalize != 1)
     return fail(h, DL_ERR_UNSUPPORTED, "renormalize=%d: only 1 is supported", c->renormalize);
-  if (c->path != DL_PATH_AUTO && c->path != DL_PATH_MULTI && c->path != DL_PATH_SINGLE)
-    return fail(h, DL_ERR_UNSUPPORTED, "path=%d: need DL_PATH_AUTO, DL_PATH_MULTI or DL_PATH_SINGLE", c->path);
+  if (c->path < DL_PATH_AUTO || c->path > DL_PATH_BATCHED)
+    return fail(h, DL_ERR_UNSUPPORTED, "path=%d: need DL_PATH_AUTO, DL_PATH_MULTI, DL_PATH_SINGLE or DL_PATH_BATCHED",
+                c->path);
   return DL_OK;
 }
 
@@ -272,6 +291,10 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
   if (h->single.max_batch > 0 && fused_blocks_per_cu() < 1) h->single = SinglePlan{};
   if (cfg->path == DL_PATH_SINGLE && h->single.max_batch == 0)
     return cleanup(fail(h, DL_ERR_UNSUPPORTED, "the single-launch path cannot run this configuration on this device"));
+  if (cfg->path == DL_PATH_BATCHED && !batched_ok(*cfg))
+    return cleanup(fail(h, DL_ERR_UNSUPPORTED,
+                        "the batched path needs hidden %% 512 == 0 and attn_dim %% 128 == 0 (hidden=%d, attn_dim=%d)",
+                        cfg->hidden, cfg->attn_dim));
   Layout L = layout_of(*cfg, h->single);
   if (hipMalloc(&h->scratch_base, L.total) != hipSuccess) {
     h->scratch_base = nullptr;
@@ -297,6 +320,10 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
   h->s.act_s64 = (uint64_t *)(b + L.off[16]);
   h->s.epoch = (unsigned *)(b + L.off[17]);
   h->s.status = (unsigned *)(b + L.off[18]);
+  h->s.qkv_part = (float *)(b + L.off[19]);
+  h->s.rlog_part = (float *)(b + L.off[20]);
+  h->s.hn = (float *)(b + L.off[21]);
+  h->s.hp = (uint16_t *)(b + L.off[22]);
   // The hand-off counters start at zero and are re-armed by the kernels
   // themselves, and the tagged hand-off values start with tag 0, which no
   // step uses (tags are the step counter + 1), so no step ever needs a memset.
@@ -326,9 +353,10 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
   const decode_layer_config &c = h->cfg;
   hipStream_t st = (hipStream_t)hip_stream;
   const int B = io->batch;
-  const bool single = c.path != DL_PATH_MULTI && B <= h->single.max_batch;
+  const bool single = (c.path == DL_PATH_AUTO || c.path == DL_PATH_SINGLE) && B <= h->single.max_batch;
   if (c.path == DL_PATH_SINGLE && !single)
     return fail(h, DL_ERR_UNSUPPORTED, "batch=%d exceeds the single-launch limit %d", B, h->single.max_batch);
+  const bool batched = !single && batched_used(c, h->single);
   HIP_TRY(h, hipSetDevice(h->device));
   if (h->profiling)
     for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i) h->launched[i] = false;
@@ -384,6 +412,58 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
     HIP_TRY(h, launch_qkv_side(fa, h->side));
     HIP_TRY(h, hipEventRecord(h->ev_join, h->side));
     HIP_TRY(h, hipStreamWaitEvent(st, h->ev_join, 0));
+    if (h->profiling) h->profiled_step = true;
+    return DL_OK;
+  }
+  if (batched) {
+    BatchArgs ba{};
+    ba.x = (const uint16_t *)io->x;
+    ba.w_qkv = (const uint16_t *)h->w.w_qkv;
+    ba.qkv = io->qkv;
+    ba.attn = (const uint16_t *)io->attn;
+    ba.w_o = (const uint16_t *)h->w.w_o;
+    ba.gain = (const uint16_t *)h->w.norm_gain;
+    ba.resid_in = io->resid_in;
+    ba.resid_out = io->resid_out;
+    ba.w_router = h->w.w_router;
+    ba.logits_out = io->router_logits;
+    ba.topk_idx = io->topk_idx;
+    ba.topk_w = io->topk_w;
+    ba.w1 = (const uint16_t *)h->w.w1;
+    ba.w3 = (const uint16_t *)h->w.w3;
+    ba.w2 = (const uint16_t *)h->w.w2;
+    ba.s1 = (const uint16_t *)h->w.s1;
+    ba.s3 = (const uint16_t *)h->w.s3;
+    ba.s2 = (const uint16_t *)h->w.s2;
+    ba.moe_out = io->moe_out;
+    ba.h_out = io->h_out;
+    ba.hg = h->s.hg;
+    ba.ss_part = h->s.ss_part;
+    ba.qkv_part = h->s.qkv_part;
+    ba.rlog_part = h->s.rlog_part;
+    ba.hn = h->s.hn;
+    ba.hp = h->s.hp;
+    ba.act = h->s.act;
+    ba.act_s = h->s.act_s;
+    ba.n_active = h->s.n_active;
+    ba.act_exp = h->s.act_exp;
+    ba.act_cnt = h->s.act_cnt;
+    ba.act_off = h->s.act_off;
+    ba.pair_tok = h->s.pair_tok;
+    ba.pair_w = h->s.pair_w;
+    ba.counter = h->s.counters + 2;
+    ba.B = B;
+    ba.H = c.hidden;
+    ba.Dq = c.qkv_out;
+    ba.Do = c.attn_dim;
+    ba.E = c.n_experts;
+    ba.K = c.top_k;
+    ba.F = c.expert_ffn;
+    ba.Fs = c.shared_ffn;
+    ba.eps = c.rms_eps;
+    if (h->profiling)
+      for (int i = 0; i < kBatchLaunches; ++i) h->launched[6 + i] = true;
+    HIP_TRY(h, launch_batched(ba, st, h->profiling ? &h->ev_prof[6] : nullptr));
     if (h->profiling) h->profiled_step = true;
     return DL_OK;
   }

@@ -74,36 +74,23 @@ __device__ void router_chunk(const RouterArgs &a, int e, int t0, int nt, float (
   __syncthreads();
 }
 
-// Per-token top-k by repeated wave arg-max; candidates of lane L are the
-// experts L, L+64, ... (at most 16 with E <= 1024), tracked with a bit mask.
+// Per-token top-k over the logits in global memory (wave_topk in common.h:
+// descending, ties to the lower expert id, always k distinct valid ids).
 __device__ void topk_token(const RouterArgs &a, int t, int *s_sel, float *s_w) {
   const int lane = threadIdx.x & 63;
-  const int ncand = (a.E + 63) >> 6;
+  constexpr int NC = kMaxExperts / 64;
   const float *lg = a.logits + (size_t)t * a.E;
-  unsigned taken = 0;
-  int my_idx = 0;
-  float my_s = 0.f, ssum = 0.f;
-  for (int j = 0; j < a.K; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int c = 0; c < ncand; ++c) {
-      int e = lane + 64 * c;
-      if (e < a.E && !((taken >> c) & 1u)) {
-        float v = lg[e];
-        if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
-      }
-    }
+  float lv[NC];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    float s = 1.0f / (1.0f + expf(-bv));
-    ssum += s;
-    if (lane == j) { my_idx = bi; my_s = s; }
+  for (int c = 0; c < NC; ++c) {
+    const int e = lane + 64 * c;
+    lv[c] = e < a.E ? lg[e] : 0.f;
   }
+  int my_idx;
+  float my_l;
+  wave_topk<NC>(lv, a.E, a.K, my_idx, my_l);
+  const float my_s = lane < a.K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
+  const float ssum = wave_sum(my_s);
   if (lane < a.K) {
     float w = my_s / ssum;
     a.topk_idx[(size_t)t * a.K + lane] = my_idx;

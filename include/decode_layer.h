@@ -67,12 +67,12 @@ enum {
  *   rms_eps       : > 0 and finite
  *   score_fn      : 0 = sigmoid (the only value supported)
  *   renormalize   : 1 = top-k weights divided by their sum (the only value supported)
- *   path          : DL_PATH_AUTO, DL_PATH_MULTI or DL_PATH_SINGLE (below)
+ *   path          : DL_PATH_AUTO, DL_PATH_MULTI, DL_PATH_SINGLE or DL_PATH_BATCHED (below)
  *
  * Execution paths.  The pages' backend is shape-aware: small-batch kernels at
  * one or two tokens, split-K kernels beyond (wireai.ir "vLLM's speed jump on
  * NVIDIA Blackwell servers; record 842 tokens/s for Kimi K3", section "Four
- * key changes behind the jump", bullet 1).  This library has two:
+ * key changes behind the jump", bullet 1).  This library has three:
  *   DL_PATH_SINGLE  the whole step in ONE launch: one workgroup per CU, all
  *                   resident, phases handing data to each other through
  *                   device memory (the shared expert's and the router's
@@ -86,15 +86,25 @@ enum {
  *                   decode_layer_single_max_batch(), which is at most 8 and
  *                   also bounded by B*k <= 64, B*E <= 8192, B*k*F <= 8192 and
  *                   B*Fs <= 4096.
- *   DL_PATH_MULTI   five launches (input/out-projection, router + top-k +
- *                   permutation, routed gate/up, down + combine) with the
- *                   shared expert's gate/up on the handle's second stream.
- *                   Any batch in the envelope.
- *   DL_PATH_AUTO    SINGLE when the step's batch allows it, else MULTI.
+ *   DL_PATH_BATCHED five launches on the caller's stream (projections,
+ *                   router dot products, top-k + permutation, gate/up,
+ *                   down + combine) that run every contraction whose
+ *                   weights 16 or more tokens share on the matrix cores
+ *                   (fp32 activations as bf16 hi + lo pairs) and the rest
+ *                   as VALU GEMVs.  Available when hidden % 512 == 0 and
+ *                   attn_dim % 128 == 0; any batch up to max_batch.
+ *   DL_PATH_MULTI   five launches of VALU GEMVs (input/out-projection,
+ *                   router + top-k + permutation, routed gate/up, down +
+ *                   combine) with the shared expert's gate/up on the
+ *                   handle's second stream.  Any configuration and batch
+ *                   in the envelope.
+ *   DL_PATH_AUTO    SINGLE when the step's batch allows it, else BATCHED
+ *                   when available, else MULTI.
  * Forcing DL_PATH_SINGLE makes a step with a larger batch fail with
- * DL_ERR_UNSUPPORTED.
+ * DL_ERR_UNSUPPORTED; forcing DL_PATH_BATCHED (or SINGLE) on a configuration
+ * the path cannot run makes decode_layer_init fail with DL_ERR_UNSUPPORTED.
  */
-enum { DL_PATH_AUTO = 0, DL_PATH_MULTI = 1, DL_PATH_SINGLE = 2 };
+enum { DL_PATH_AUTO = 0, DL_PATH_MULTI = 1, DL_PATH_SINGLE = 2, DL_PATH_BATCHED = 3 };
 typedef struct {
   int32_t hidden;
   int32_t qkv_out;
@@ -207,12 +217,14 @@ const char *decode_layer_last_error(const decode_layer *h);
  * the launches' durations in milliseconds, in the fixed order
  *   0 out-projection + input projection, 1 shared expert gate/up,
  *   2 router + top-k + permute, 3 routed expert gate/up, 4 expert down + combine,
- *   5 single-launch step
+ *   5 single-launch step,
+ *   6 batched projections, 7 batched router, 8 batched top-k + permute,
+ *   9 batched gate/up, 10 batched down + combine
  * (0 for a launch the last step did not make).  It returns the number of
  * entries written (<= capacity) or a negative DL_ERR_* code (DL_ERR_INVALID_ARG
  * if profiling is off or no step ran since it was enabled).  Enabling creates
  * the events (DL_ERR_HIP on failure); do not enable it while capturing a graph. */
-#define DECODE_LAYER_N_LAUNCHES 6
+#define DECODE_LAYER_N_LAUNCHES 11
 int decode_layer_set_profiling(decode_layer *h, int enable);
 int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
 
@@ -233,7 +245,8 @@ int decode_layer_grid(const decode_layer *h);
 /* Bytes of device scratch a handle with this configuration allocates on a
  * device with `n_cu` compute units (0 if the configuration is invalid).  The
  * single-launch path's hand-off arrays grow with n_cu; n_cu = 0 gives the size
- * without them (the multi-launch path alone).  Host-only. */
+ * without them.  The batched path's arrays are included when a step of this
+ * configuration can take that path.  Host-only. */
 size_t decode_layer_scratch_bytes(const decode_layer_config *cfg, int n_cu);
 
 #ifdef __cplusplus

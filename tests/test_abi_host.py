@@ -43,7 +43,7 @@ def good():
     ("max_batch", 65, dl.DL_ERR_UNSUPPORTED), ("max_batch", 0, dl.DL_ERR_UNSUPPORTED),
     ("rms_eps", 0.0, dl.DL_ERR_UNSUPPORTED), ("rms_eps", float("inf"), dl.DL_ERR_UNSUPPORTED),
     ("score_fn", 1, dl.DL_ERR_UNSUPPORTED), ("renormalize", 0, dl.DL_ERR_UNSUPPORTED),
-    ("path", 3, dl.DL_ERR_UNSUPPORTED), ("path", -1, dl.DL_ERR_UNSUPPORTED),
+    ("path", 4, dl.DL_ERR_UNSUPPORTED), ("path", -1, dl.DL_ERR_UNSUPPORTED),
 ])
 def test_config_validation(field, value, code):
     c = good()
@@ -75,13 +75,47 @@ def test_single_launch_scratch_follows_the_plan():
     tagged = 8 * (G * B + B * E + B * K * F + B * Fs)
     assert tagged <= with_single - base <= tagged + 8 * 256
     c.path = dl.DL_PATH_MULTI        # multi-launch only: no single-launch arrays
-    assert dl.scratch_bytes(c, 256) == base
+    assert dl.scratch_bytes(c, 256) == dl.scratch_bytes(c, 0)
     big_h = dl.make_config(16384, 512, 512, 384, 8, 128, 128, 8)   # hidden above 8192
     assert dl.scratch_bytes(big_h, 256) == dl.scratch_bytes(big_h, 0)
     many_e = dl.make_config(7168, 512, 512, 1024, 8, 128, 128, 8)  # more than 512 experts
     assert dl.scratch_bytes(many_e, 256) == dl.scratch_bytes(many_e, 0)
     odd_fs = dl.make_config(7168, 512, 512, 384, 8, 128, 256, 8)   # shared ffn != expert ffn
     assert dl.scratch_bytes(odd_fs, 256) == dl.scratch_bytes(odd_fs, 0)
+
+
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_batched_scratch_follows_the_path():
+    """The batched path's arrays (qkv and router partial sums, h in fp32 and
+    as bf16 hi + lo planes) exist exactly when some step can take that path."""
+    c = good()                       # TP16 shard shapes, max_batch 64
+    B, H, Dq, E = 64, 7168, 512, 384
+    batched = (_a256(4 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
+               + _a256(2 * 2 * B * H))
+    auto = dl.scratch_bytes(c, 256)
+    c.path = dl.DL_PATH_MULTI
+    multi = dl.scratch_bytes(c, 256)
+    c.path = dl.DL_PATH_BATCHED
+    forced = dl.scratch_bytes(c, 256)
+    assert forced == dl.scratch_bytes(c, 0)     # no single-launch arrays when forced
+    assert auto - batched > multi               # AUTO: single-launch arrays on top
+    assert forced - batched == multi
+    # a batch the single-launch path covers entirely: no batched arrays under AUTO
+    small = dl.make_config(7168, 512, 512, 384, 8, 128, 128, 8)
+    small_multi = dl.make_config(7168, 512, 512, 384, 8, 128, 128, 8, path=dl.DL_PATH_MULTI)
+    G, Bs, K, F, Fs = 256, 8, 8, 128, 128
+    tagged = 8 * (G * Bs + Bs * E + Bs * K * F + Bs * Fs)
+    assert tagged <= dl.scratch_bytes(small, 256) - dl.scratch_bytes(small_multi, 256) <= tagged + 8 * 256
+    # shapes the batched tiling cannot take: AUTO never allocates its arrays
+    odd_h = dl.make_config(7168 + 256, 512, 512, 384, 8, 128, 128, 64)
+    odd_h_multi = dl.make_config(7168 + 256, 512, 512, 384, 8, 128, 128, 64, path=dl.DL_PATH_MULTI)
+    assert dl.scratch_bytes(odd_h, 0) == dl.scratch_bytes(odd_h_multi, 0)
+    odd_do = dl.make_config(7168, 512, 520, 384, 8, 128, 128, 64)
+    odd_do_multi = dl.make_config(7168, 512, 520, 384, 8, 128, 128, 64, path=dl.DL_PATH_MULTI)
+    assert dl.scratch_bytes(odd_do, 0) == dl.scratch_bytes(odd_do_multi, 0)
 
 
 def _io(batch=1, **kw):

@@ -23,12 +23,19 @@ def need_gpu():
     import decode_step_moe_amd  # noqa: F401  (raises if the library was not built)
 
 
-AUTO, MULTI, SINGLE = 0, 1, 2
-PATH_NAMES = {AUTO: "auto", MULTI: "multi", SINGLE: "single"}
+AUTO, MULTI, SINGLE, BATCHED = 0, 1, 2, 3
+PATH_NAMES = {AUTO: "auto", MULTI: "multi", SINGLE: "single", BATCHED: "batched"}
+PATHS = [AUTO, MULTI, BATCHED]
 
 
 def used_single(obj, batch, path):
-    return path != MULTI and batch <= obj.single_max_batch
+    return path in (AUTO, SINGLE) and batch <= obj.single_max_batch
+
+
+def used_name(obj, batch, path):
+    if used_single(obj, batch, path):
+        return "single"
+    return "multi" if path == MULTI else "batched"
 
 
 def run_gpu(layer, with_h=True, max_batch=None, inplace=False, logits=True, layer_obj=None,
@@ -61,7 +68,7 @@ def check(layer, got, tag):
     return m
 
 
-@pytest.mark.parametrize("path", [AUTO, MULTI])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_workload_parity(cfg, path):
     say(f"[workload cfg={cfg} {gen.SHAPES[cfg].name} path={PATH_NAMES[path]}] start")
@@ -70,19 +77,19 @@ def test_workload_parity(cfg, path):
     single = used_single(obj, layer.shape.batch, path)
     # batches up to 8 take the single-launch path under AUTO at these shapes
     assert single == (path == AUTO and layer.shape.batch <= 8), (obj.single_max_batch, layer.shape.batch)
-    check(layer, got, f"cfg{cfg}_{'single' if single else 'multi'}")
+    check(layer, got, f"cfg{cfg}_{used_name(obj, layer.shape.batch, path)}")
 
 
-@pytest.mark.parametrize("path", [AUTO, MULTI])
-@pytest.mark.parametrize("batch", [2, 3, 5, 13, 64])
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("batch", [2, 3, 5, 13, 17, 64])
 def test_ragged_batches(batch, path):
     say(f"[ragged cfg=2 shapes, batch={batch} path={PATH_NAMES[path]}] start")
     layer = workload.build(2, batch=batch)
     got, obj = run_gpu(layer, max_batch=64, path=path)
-    check(layer, got, f"ragged_b{batch}_{'single' if used_single(obj, batch, path) else 'multi'}")
+    check(layer, got, f"ragged_b{batch}_{used_name(obj, batch, path)}")
 
 
-@pytest.mark.parametrize("path", [AUTO, MULTI])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("top_k,shared", [(1, 256), (8, 256), (2, 0), (1, 0)])
 def test_topk_and_shared_edges(top_k, shared, path):
     say(f"[tiny edges k={top_k} shared_ffn={shared} path={PATH_NAMES[path]}] start")
@@ -107,7 +114,7 @@ def test_batch_zero_is_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("path", [AUTO, MULTI])
+@pytest.mark.parametrize("path", PATHS)
 def test_inplace_residual_and_null_logits(path):
     say(f"[in-place residual, logits NULL, path={PATH_NAMES[path]}] start")
     layer = workload.build(4, h_source="stored")
@@ -222,7 +229,7 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("path", [AUTO, MULTI])
+@pytest.mark.parametrize("path", PATHS)
 def test_graph_replay_many_steps(path):
     """A graph holding two steps (different copies of the inputs), replayed
     10 times with eager steps in between: the single-launch path's step
@@ -259,6 +266,59 @@ def test_graph_replay_many_steps(path):
             obj.step(x, attn, resid)
             torch.cuda.synchronize()
     assert obj.status() == 0
+
+
+def test_batched_graph_replay_hot_experts():
+    """The batched path at batch 64 (hot experts, every routed contraction on
+    MFMA) captured in a graph with another step, replayed with eager steps
+    in between: every replay equals the eager result bit for bit."""
+    say("[graph of 2 batched steps x 6 replays, cfg 3] start")
+    from decode_step_moe_amd import DecodeLayer
+    layer = workload.build(3, h_source="stored")
+    obj = DecodeLayer(sdev.config_of(layer), sdev.upload_weights(layer))
+    assert not used_single(obj, 64, AUTO)
+    x, attn, resid = sdev.upload_inputs(layer)
+    eager = obj.step(x, attn, resid)
+    torch.cuda.synchronize()
+    outs = [obj.alloc_outputs(64) for _ in range(2)]
+    ios = [obj.make_io(x, attn, resid, o) for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        obj.step_io(ios[0], s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        obj.step_io(ios[0])
+        obj.step_io(ios[1])
+    for rep in range(6):
+        for o in outs:
+            o.moe_out.fill_(float("nan"))
+            o.qkv.fill_(float("nan"))
+            o.topk_idx.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for o in outs:
+            for k in ("qkv", "resid_out", "topk_idx", "topk_w", "moe_out"):
+                assert torch.equal(getattr(o, k), getattr(eager, k)), (rep, k)
+        if rep % 2 == 0:
+            obj.step(x, attn, resid)
+            torch.cuda.synchronize()
+
+
+def test_batched_path_batches_change_on_one_handle():
+    """One batched-path handle stepping batches 64, 9, 33, 1, 64: the lists
+    and partial sums of a larger step never leak into a smaller one."""
+    say("[batched path, batches 64,9,33,1,64 on one handle] start")
+    from decode_step_moe_amd import DecodeLayer
+    full = workload.build(2, batch=64)
+    obj = DecodeLayer(sdev.config_of(full, 64, path=BATCHED), sdev.upload_weights(full))
+    for b in (64, 9, 33, 1, 64):
+        layer = routing.RoutedLayer(gen.draw(2, batch=b), full.w_router, full.targets[:b],
+                                    full.target_logits[:b])
+        got, _ = run_gpu(layer, layer_obj=obj)
+        check(layer, got, f"batched_b{b}")
 
 
 @pytest.mark.parametrize("scale", [1e3, 1e-3])
