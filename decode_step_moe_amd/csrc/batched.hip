@@ -86,30 +86,41 @@ __device__ __forceinline__ void load8f(const float *p, float (&x)[8]) {
   x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
 }
 
+__device__ __forceinline__ uint4 zero_unless(bool keep, const uint4 &v) {
+  const unsigned m = keep ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// Loads are issued in batches and kept apart from the MFMAs that consume
+// them by a scheduling barrier: left to itself the compiler interleaves each
+// load with its first use, which leaves one load in flight per wave.
+// A wave's loads complete in issue order, so a batch's first MFMA waits only
+// for the batch's first loads.
+#define DL_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 // One wave: acc[c] += A_c (16 x 32 nks) . W^T (32 nks x 16) with bf16 A rows
 // at ap[c] and weight rows at wp (both already offset by this lane's row and
-// its 8g K position).  U K-steps of loads are issued before their MFMAs.
+// its 8g K position).  U K-steps of loads per batch; the K-steps of the last
+// batch beyond nks re-read step nks-1 and multiply zero weights.
 template <int NC, int U>
 __device__ __forceinline__ void mfma_rows(const uint16_t *wp, const uint16_t *const (&ap)[NC], int nks,
                                           f32x4 (&acc)[NC]) {
-  int ks = 0;
-  for (; ks + U <= nks; ks += U) {
+  for (int ks = 0; ks < nks; ks += U) {
     uint4 wv[U], av[U][NC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wv[u] = ld_stream16(wp + (ks + u) * 32);
+    for (int u = 0; u < U; ++u) {
+      const int k = min(ks + u, nks - 1) * 32;
+      wv[u] = ld_stream16(wp + k);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int c = 0; c < NC; ++c) av[u][c] = ld16(ap[c] + k);
+    }
+    DL_SCHED_FENCE();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) av[u][c] = ld16(ap[c] + (ks + u) * 32);
+    for (int u = 0; u < U; ++u) {
+      const uint4 w = zero_unless(ks + u < nks, wv[u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = mfma_bf16(av[u][c], wv[u], acc[c]);
-  }
-  for (; ks < nks; ++ks) {
-    const uint4 wv = ld_stream16(wp + ks * 32);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = mfma_bf16(ld16(ap[c] + ks * 32), wv, acc[c]);
+      for (int c = 0; c < NC; ++c) acc[c] = mfma_bf16(av[u][c], w, acc[c]);
+    }
   }
 }
 
@@ -219,6 +230,7 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) av[it][c] = ld16f(ap + 16 * it);
     }
+    DL_SCHED_FENCE();
     f32x4 acc[NC][2];
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -267,6 +279,7 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __shared__ int cnt[kMaxExperts], off[kMaxExperts];
   __shared__ unsigned msk[kMaxExperts][2];
   __shared__ int sa[kBlock], sc[kBlock];
+  __shared__ int slot_nch[kMaxExperts];
   __shared__ int last_flag;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int B = a.B, H = a.H, E = a.E, K = a.K, t = blockIdx.x;
@@ -299,7 +312,15 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   // logits: K chunks summed in ascending order, then scaled
   for (int e = tid; e < E; e += kBlock) {
     float d = 0.f;
-    for (int ky = 0; ky < n_rk; ++ky) d += a.rlog_part[((size_t)ky * B + t) * E + e];
+    const float *p = a.rlog_part + (size_t)t * E + e;
+    const size_t stride = (size_t)B * E;
+    for (int ky0 = 0; ky0 < n_rk; ky0 += 8) {  // 8 independent loads per batch
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p[min(ky0 + j, n_rk - 1) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d += ky0 + j < n_rk ? v[j] : 0.f;
+    }
     const float l = d * inv;
     lg[e] = l;
     if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
@@ -361,11 +382,34 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
       a.act_exp[pa] = q;
       a.act_cnt[pa] = c;
       a.act_off[pa] = pc;
+      // gate/up work per slot: 16-token chunks on the matrix cores, else one VALU item
+      slot_nch[pa] = c >= kBatchMfmaMin ? (c + 15) >> 4 : 1;
       ++pa;
       pc += c;
     }
   }
-  if (tid == kBlock - 1) *a.n_active = sa[kBlock - 1];
+  const int n_act = sa[kBlock - 1];
+  if (tid == kBlock - 1) *a.n_active = n_act;
+  __syncthreads();
+  // gate/up work list: (slot, chunk) pairs, slots ascending
+  {
+    const int seg2 = (n_act + kBlock - 1) / kBlock;
+    const int s0 = tid * seg2, s1 = min(n_act, s0 + seg2);
+    int lq = 0;
+    for (int q = s0; q < s1; ++q) lq += slot_nch[q];
+    sa[tid] = lq;
+    __syncthreads();
+    for (int o = 1; o < kBlock; o <<= 1) {
+      const int v = tid >= o ? sa[tid - o] : 0;
+      __syncthreads();
+      sa[tid] += v;
+      __syncthreads();
+    }
+    int pq = sa[tid] - lq;
+    for (int q = s0; q < s1; ++q)
+      for (int c = 0; c < slot_nch[q]; ++c) a.gu_q[pq++] = q | (c << 16);
+    if (tid == kBlock - 1) *a.n_q = sa[kBlock - 1];
+  }
   __syncthreads();
   // a pair's place inside its expert = number of lower tokens with that expert
   for (int i = tid; i < P; i += kBlock) {
@@ -381,73 +425,50 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
 // ================================================================ launch 4
 struct GuItem {
   const uint16_t *w1, *w3;  // first of the item's 16 rows, row stride H
-  const int *toks;          // token of row m (nullptr: m itself)
+  const int *toks;          // token of row m (nullptr: tok0 + m)
+  int tok0;
   float *out;               // row m of the output at out + m * ld, 16 columns
-  int ld, cnt;
-  __device__ int tok(int m) const { return toks ? toks[m] : m; }
+  int ld, cnt;              // cnt <= 16 rows on the matrix cores, < 16 on the VALU
+  __device__ int tok(int m) const { return toks ? toks[m] : tok0 + m; }
 };
 
-// 16 tokens per chunk on the matrix cores; the 4 waves split K.
-template <int NC>
-__device__ void gateup_mfma(const BatchArgs &a, const GuItem &it, float (*red)[4 * 2 * 256]) {
+// Up to 16 tokens on the matrix cores; the 4 waves split K.
+__device__ void gateup_mfma(const BatchArgs &a, const GuItem &it, float (*red)[2 * 256]) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int H = a.H, kw = wv * (H / 4) + 8 * g, nks = H / 128;
   const uint16_t *p1 = it.w1 + (size_t)n * H + kw, *p3 = it.w3 + (size_t)n * H + kw;
-  const uint16_t *ph[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) ph[c] = a.hp + (size_t)it.tok(min(16 * c + n, it.cnt - 1)) * H + kw;
+  const uint16_t *ph = a.hp + (size_t)it.tok(min(n, it.cnt - 1)) * H + kw;
   const size_t plane = (size_t)a.B * H;
-  f32x4 acc1[NC], acc3[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) acc1[c] = acc3[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = NC <= 2 ? 4 : 2;
-  int ks = 0;
-  for (; ks + U <= nks; ks += U) {
-    uint4 w1v[U], w3v[U], hv[U][NC], lv[U][NC];
+  f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = acc1;
+  constexpr int U = 7;   // 28 loads per batch; H = 7168 gives 8 batches of 7 K-steps
+  for (int ks = 0; ks < nks; ks += U) {
+    uint4 w1v[U], w3v[U], hv[U], lv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      w1v[u] = ld_stream16(p1 + (ks + u) * 32);
-      w3v[u] = ld_stream16(p3 + (ks + u) * 32);
+      const int k = min(ks + u, nks - 1) * 32;
+      w1v[u] = ld_stream16(p1 + k);
+      w3v[u] = ld_stream16(p3 + k);
+      hv[u] = ld16(ph + k);
+      lv[u] = ld16(ph + plane + k);
     }
+    DL_SCHED_FENCE();
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        hv[u][c] = ld16(ph[c] + (ks + u) * 32);
-        lv[u][c] = ld16(ph[c] + plane + (ks + u) * 32);
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        acc1[c] = mfma_bf16(hv[u][c], w1v[u], acc1[c]);
-        acc1[c] = mfma_bf16(lv[u][c], w1v[u], acc1[c]);
-        acc3[c] = mfma_bf16(hv[u][c], w3v[u], acc3[c]);
-        acc3[c] = mfma_bf16(lv[u][c], w3v[u], acc3[c]);
-      }
-  }
-  for (; ks < nks; ++ks) {
-    const uint4 w1v = ld_stream16(p1 + ks * 32), w3v = ld_stream16(p3 + ks * 32);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint4 hv = ld16(ph[c] + ks * 32), lv = ld16(ph[c] + plane + ks * 32);
-      acc1[c] = mfma_bf16(hv, w1v, acc1[c]);
-      acc1[c] = mfma_bf16(lv, w1v, acc1[c]);
-      acc3[c] = mfma_bf16(hv, w3v, acc3[c]);
-      acc3[c] = mfma_bf16(lv, w3v, acc3[c]);
+    for (int u = 0; u < U; ++u) {
+      const uint4 a1 = zero_unless(ks + u < nks, w1v[u]), a3 = zero_unless(ks + u < nks, w3v[u]);
+      acc1 = mfma_bf16(hv[u], a1, acc1);
+      acc3 = mfma_bf16(hv[u], a3, acc3);
+      acc1 = mfma_bf16(lv[u], a1, acc1);
+      acc3 = mfma_bf16(lv[u], a3, acc3);
     }
   }
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      red[wv][(c * 2) * 256 + (4 * g + i) * 16 + n] = acc1[c][i];
-      red[wv][(c * 2 + 1) * 256 + (4 * g + i) * 16 + n] = acc3[c][i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    red[wv][(4 * g + i) * 16 + n] = acc1[i];
+    red[wv][256 + (4 * g + i) * 16 + n] = acc3[i];
+  }
   __syncthreads();
   for (int q = tid; q < it.cnt * 16; q += kBlock) {
-    const int m = q >> 4, nn = q & 15;
-    const int i1 = ((m >> 4) * 2) * 256 + (m & 15) * 16 + nn;
+    const int m = q >> 4, nn = q & 15, i1 = m * 16 + nn;
     const float u = ((red[0][i1] + red[1][i1]) + red[2][i1]) + red[3][i1];
     const float v = ((red[0][i1 + 256] + red[1][i1 + 256]) + red[2][i1 + 256]) + red[3][i1 + 256];
     it.out[(size_t)m * it.ld + nn] = silu_mul(u, v);
@@ -486,150 +507,250 @@ __device__ void gateup_valu(const BatchArgs &a, const GuItem &it) {
   }
 }
 
-// Items: (active slot, 16-row tile) for the routed experts, then the shared
-// expert's tiles.  Block b runs on XCD b % 8; each XCD takes a contiguous
-// range of items, so an expert's tiles (which read the same token rows of h)
-// mostly share one L2.
-__global__ void __launch_bounds__(kBlock) gateup_b(BatchArgs a) {
-  __shared__ float red[kWavesPerBlock][4 * 2 * 256];
-  const int n_act = *a.n_active;
+// Items: (work-list entry, 16-row tile) for the routed experts, where a
+// work-list entry is an active slot and, for an expert with 16 or more
+// tokens, one 16-token chunk of it; then (16-row tile, chunk) of the shared
+// expert.  Every matrix-core item is thus 16 rows x at most 16 tokens.
+// Block b runs on XCD b % 8; each XCD takes a contiguous range of items, so
+// the items that read the same token rows of h (or the same shared-expert
+// rows) mostly share one L2.
+__global__ void __launch_bounds__(kBlock, 3) gateup_b(BatchArgs a) {
+  __shared__ float red[kWavesPerBlock][2 * 256];
+  const int n_q = *a.n_q;
   const int ntr = a.F / 16, nts = a.Fs / 16;
-  const int n_items = n_act * ntr + nts;
+  const bool s_mfma = a.B >= kBatchMfmaMin;
+  const int nch_s = s_mfma ? (a.B + 15) >> 4 : 1;
+  const int n_rt = n_q * ntr;
+  const int n_items = n_rt + nch_s * nts;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, nloc = gridDim.x >> 3;
   const int per = (n_items + 7) >> 3;
   const int beg = xcd * per, end = min(beg + per, n_items);
   for (int i = beg + loc; i < end; i += nloc) {
     GuItem it;
-    if (i < n_act * ntr) {
-      const int slot = i / ntr, tile = i % ntr;
-      const int e = a.act_exp[slot], off = a.act_off[slot];
+    bool mfma;
+    if (i < n_rt) {
+      const int q = a.gu_q[i / ntr], tile = i % ntr;
+      const int slot = q & 0xffff, c0 = 16 * (q >> 16);
+      const int e = a.act_exp[slot], off = a.act_off[slot] + c0, cnt = a.act_cnt[slot];
       it.w1 = a.w1 + ((size_t)e * a.F + tile * 16) * a.H;
       it.w3 = a.w3 + ((size_t)e * a.F + tile * 16) * a.H;
       it.toks = a.pair_tok + off;
+      it.tok0 = 0;
       it.out = a.act + (size_t)off * a.F + tile * 16;
       it.ld = a.F;
-      it.cnt = a.act_cnt[slot];
+      mfma = cnt >= kBatchMfmaMin;
+      it.cnt = mfma ? min(16, cnt - c0) : cnt;
     } else {
-      const int tile = i - n_act * ntr;
+      const int j = i - n_rt, tile = j / nch_s, c0 = 16 * (j % nch_s);
       it.w1 = a.s1 + (size_t)tile * 16 * a.H;
       it.w3 = a.s3 + (size_t)tile * 16 * a.H;
       it.toks = nullptr;
-      it.out = a.act_s + tile * 16;
+      it.tok0 = c0;
+      it.out = a.act_s + (size_t)c0 * a.Fs + tile * 16;
       it.ld = a.Fs;
-      it.cnt = a.B;
+      mfma = s_mfma;
+      it.cnt = mfma ? min(16, a.B - c0) : a.B;
     }
-    if (it.cnt >= kBatchMfmaMin)
-      by_chunks((it.cnt + 15) >> 4, [&](auto ncc) { gateup_mfma<decltype(ncc)::value>(a, it, red); });
-    else
-      gateup_valu(a, it);
+    if (mfma) gateup_mfma(a, it, red);
+    else gateup_valu(a, it);
     __syncthreads();  // red is reused by the next item
   }
 }
 
 // ================================================================ launch 5
+// Weights of one item for this lane: row n = lane % 16 of the 16-row tile,
+// K positions 32 s + 8 g (g = lane / 16) for s < NKS = Fd / 32.  MFMA items
+// use them as the B operand; VALU items reduce the four g lanes of a row.
+template <int NKS>
+__device__ __forceinline__ void down_load_w(const uint16_t *tile, uint4 (&wv)[NKS]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const uint16_t *p = tile + (size_t)n * (32 * NKS) + 8 * g;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) wv[s] = ld_stream16(p + 32 * s);
+}
+
 struct DnItem {
-  const uint16_t *w;  // row r0 of the item's [H][Fd] matrix
   const float *act;   // row m at act + m * Fd
   const int *toks;    // token of row m (nullptr: m itself)
   const float *wts;   // weight of row m (nullptr: 1)
-  int Fd, cnt;
+  int cnt;
+  __device__ int tok(int m) const { return toks ? toks[m] : m; }
+  __device__ float wt(int m) const { return wts ? wts[m] : 1.f; }
 };
 
-__device__ void down_mfma(const DnItem &it, float (*y)[16]) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int nks = it.Fd / 32;
-  uint4 wv[8];
+// Rows [c0, c0 + 16) of an item on the matrix cores: load, then compute.
+template <int NKS>
+struct MfmaChunk {
+  float4 xv[NKS][2];
+  __device__ __forceinline__ void load(const DnItem &it, int c0) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const float *ap = it.act + (size_t)min(c0 + n, it.cnt - 1) * (32 * NKS) + 8 * g;
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    if (s < nks) wv[s] = ld_stream16(it.w + (size_t)n * it.Fd + 32 * s + 8 * g);
-  for (int c0 = 0; c0 < it.cnt; c0 += 16) {
-    const float *ap = it.act + (size_t)min(c0 + n, it.cnt - 1) * it.Fd + 8 * g;
+    for (int s = 0; s < NKS; ++s) {
+      xv[s][0] = ld16f(ap + 32 * s);
+      xv[s][1] = ld16f(ap + 32 * s + 4);
+    }
+  }
+  __device__ __forceinline__ void compute(const DnItem &it, int c0, const uint4 (&wv)[NKS], float (*y)[16]) const {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s < nks) {
-        float x[8];
-        load8f(ap + 32 * s, x);
-        uint4 hi, lo;
-        split8(x, hi, lo);
-        acc = mfma_bf16(hi, wv[s], acc);
-        acc = mfma_bf16(lo, wv[s], acc);
-      }
+    for (int s = 0; s < NKS; ++s) {
+      const float x[8] = {xv[s][0].x, xv[s][0].y, xv[s][0].z, xv[s][0].w,
+                          xv[s][1].x, xv[s][1].y, xv[s][1].z, xv[s][1].w};
+      uint4 hi, lo;
+      split8(x, hi, lo);
+      acc = mfma_bf16(hi, wv[s], acc);
+      acc = mfma_bf16(lo, wv[s], acc);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = c0 + 4 * g + i;
-      if (m < it.cnt) {
-        const int t = it.toks ? it.toks[m] : m;
-        const float w = it.wts ? it.wts[m] : 1.f;
-        y[t][n] += w * acc[i];
+      if (m < it.cnt) y[it.tok(m)][n] += it.wt(m) * acc[i];
+    }
+  }
+};
+
+// Rows m0 .. m0 + TB - 1 (below cnt) of an item on the VALU.
+template <int NKS>
+struct ValuRows {
+  static constexpr int TB = 8 / NKS;   // 64 VGPRs of activations per batch
+  float4 xv[TB][NKS][2];
+  __device__ __forceinline__ void load(const DnItem &it, int m0) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const float *ap = it.act + (size_t)min(m0 + tb, it.cnt - 1) * (32 * NKS) + 8 * g;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        xv[tb][s][0] = ld16f(ap + 32 * s);
+        xv[tb][s][1] = ld16f(ap + 32 * s + 4);
       }
     }
   }
-}
-
-// Lane l: row l / 4 of the tile, K chunks (l % 4) + 4j of 8 values; the 4
-// lanes of a row reduce with quad permutes.
-__device__ void down_valu(const DnItem &it, float (*y)[16]) {
-  const int lane = threadIdx.x & 63, r = lane >> 2, q = lane & 3;
-  const int nch = it.Fd / 32;
-  uint4 wv[8];
+  __device__ __forceinline__ void compute(const DnItem &it, int m0, const uint4 (&wv)[NKS], float (*y)[16]) const {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < nch) wv[j] = ld_stream16(it.w + (size_t)r * it.Fd + 8 * q + 32 * j);
-  for (int m = 0; m < it.cnt; ++m) {
-    const float *ap = it.act + (size_t)m * it.Fd + 8 * q;
-    float acc = 0.f;
+    for (int tb = 0; tb < TB; ++tb) {
+      float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < nch) {
-        float x[8], wf[8];
-        load8f(ap + 32 * j, x);
-        unpack8(wv[j], wf);
+      for (int s = 0; s < NKS; ++s) {
+        float wf[8];
+        unpack8(wv[s], wf);
+        const float x[8] = {xv[tb][s][0].x, xv[tb][s][0].y, xv[tb][s][0].z, xv[tb][s][0].w,
+                            xv[tb][s][1].x, xv[tb][s][1].y, xv[tb][s][1].z, xv[tb][s][1].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(wf[e], x[e], acc);
       }
-    acc += dpp_mov<kDppXor1>(acc);
-    acc += dpp_mov<kDppXor2>(acc);
-    if (q == 0) {
-      const int t = it.toks ? it.toks[m] : m;
-      const float w = it.wts ? it.wts[m] : 1.f;
-      y[t][r] += w * acc;
+      acc += __shfl_xor(acc, 16, kWave);   // lanes g, g ^ 1
+      acc += __shfl_xor(acc, 32, kWave);   // (v0 + v1) + (v2 + v3)
+      const int m = m0 + tb;
+      if (g == 0 && m < it.cnt) y[it.tok(m)][n] += it.wt(m) * acc;
+    }
+  }
+};
+
+// One item with weights wv; if `next` is set, the next item's weights are
+// requested right after this item's first activation batch, so the wait
+// for those activations does not include them (a wave's loads complete in
+// issue order).
+template <int NKS>
+__device__ __forceinline__ void down_item(const DnItem &it, const uint4 (&wv)[NKS], float (*y)[16],
+                                          const uint16_t *next, uint4 (&wn)[NKS]) {
+  if (it.cnt >= kBatchMfmaMin) {
+    for (int c0 = 0; c0 < it.cnt; c0 += 16) {
+      MfmaChunk<NKS> ch;
+      ch.load(it, c0);
+      if (c0 == 0 && next) down_load_w<NKS>(next, wn);
+      DL_SCHED_FENCE();
+      ch.compute(it, c0, wv, y);
+    }
+  } else {
+    for (int m0 = 0; m0 < it.cnt; m0 += ValuRows<NKS>::TB) {
+      ValuRows<NKS> rw;
+      rw.load(it, m0);
+      if (m0 == 0 && next) down_load_w<NKS>(next, wn);
+      DL_SCHED_FENCE();
+      rw.compute(it, m0, wv, y);
     }
   }
 }
 
-// Workgroup: rows [16 b, 16 b + 16) of y for every token.  Wave w takes items
-// w, w + 4, ... (active slots, then the shared expert) into its own LDS
-// accumulator; the four accumulators are added in wave order at the end.
+// Routed items of this wave: active slots wv, wv + 4, ... (metadata in LDS).
+template <int NKS>
+__device__ void down_routed(const BatchArgs &a, int i0, int n_act, const int *exp_, const int *cnt_,
+                            const int *off_, float (*y)[16]) {
+  constexpr int Fd = 32 * NKS;
+  const int wv = threadIdx.x >> 6;
+  if (wv >= n_act) return;
+  auto tile = [&](int slot) { return a.w2 + ((size_t)exp_[slot] * a.H + i0) * Fd; };
+  uint4 wc[NKS], wn[NKS];
+  down_load_w<NKS>(tile(wv), wc);
+  for (int i = wv; i < n_act; i += kWavesPerBlock) {
+    const int off = off_[i];
+    const DnItem it{a.act + (size_t)off * Fd, a.pair_tok + off, a.pair_w + off, cnt_[i]};
+    const int nx = i + kWavesPerBlock;
+    down_item<NKS>(it, wc, y, nx < n_act ? tile(nx) : nullptr, wn);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) wc[s] = wn[s];
+  }
+}
+
+// The shared expert (weight 1, every token): with 16 or more tokens wave w
+// takes the 16-token chunk w on the matrix cores; below that one wave takes
+// all tokens on the VALU.
+template <int NKS>
+__device__ void down_shared(const BatchArgs &a, int i0, int n_act, float (*y)[16]) {
+  const int wv = threadIdx.x >> 6, B = a.B;
+  const DnItem it{a.act_s, nullptr, nullptr, B};
+  const uint16_t *tile = a.s2 + (size_t)i0 * (32 * NKS);
+  uint4 wv_[NKS];
+  if (B >= kBatchMfmaMin) {
+    if (16 * wv < B) {
+      down_load_w<NKS>(tile, wv_);
+      MfmaChunk<NKS> ch;
+      ch.load(it, 16 * wv);
+      DL_SCHED_FENCE();
+      ch.compute(it, 16 * wv, wv_, y);
+    }
+  } else if (wv == n_act % kWavesPerBlock) {
+    down_load_w<NKS>(tile, wv_);
+    for (int m0 = 0; m0 < B; m0 += ValuRows<NKS>::TB) {
+      ValuRows<NKS> rw;
+      rw.load(it, m0);
+      DL_SCHED_FENCE();
+      rw.compute(it, m0, wv_, y);
+    }
+  }
+}
+
+template <class Fn>
+__device__ __forceinline__ void by_nks(int Fd, Fn fn) {
+  switch (Fd) {
+    case 32: fn(std::integral_constant<int, 1>{}); break;
+    case 64: fn(std::integral_constant<int, 2>{}); break;
+    case 128: fn(std::integral_constant<int, 4>{}); break;
+    default: fn(std::integral_constant<int, 8>{}); break;
+  }
+}
+
+// Workgroup: rows [16 b, 16 b + 16) of y for every token.  Each wave adds its
+// items into its own LDS accumulator; the four are added in wave order.
 __global__ void __launch_bounds__(kBlock) down_b(BatchArgs a) {
   __shared__ float yw[kWavesPerBlock][kMaxBatch][16];
+  __shared__ int s_exp[kMaxExperts], s_cnt[kMaxExperts], s_off[kMaxExperts];
   const int tid = threadIdx.x, wv = tid >> 6;
   const int B = a.B, H = a.H, i0 = blockIdx.x * 16;
-  for (int q = tid; q < kWavesPerBlock * kMaxBatch * 16; q += kBlock) (&yw[0][0][0])[q] = 0.f;
-  __syncthreads();
   const int n_act = *a.n_active;
-  const int n_items = n_act + (a.Fs > 0 ? 1 : 0);
-  for (int i = wv; i < n_items; i += kWavesPerBlock) {
-    DnItem it;
-    if (i < n_act) {
-      const int e = a.act_exp[i], off = a.act_off[i];
-      it.w = a.w2 + ((size_t)e * H + i0) * a.F;
-      it.act = a.act + (size_t)off * a.F;
-      it.toks = a.pair_tok + off;
-      it.wts = a.pair_w + off;
-      it.Fd = a.F;
-      it.cnt = a.act_cnt[i];
-    } else {
-      it.w = a.s2 + (size_t)i0 * a.Fs;
-      it.act = a.act_s;
-      it.toks = nullptr;
-      it.wts = nullptr;
-      it.Fd = a.Fs;
-      it.cnt = B;
-    }
-    if (it.cnt >= kBatchMfmaMin) down_mfma(it, yw[wv]);
-    else down_valu(it, yw[wv]);
+  for (int q = tid; q < kWavesPerBlock * kMaxBatch * 16; q += kBlock) (&yw[0][0][0])[q] = 0.f;
+  for (int q = tid; q < n_act; q += kBlock) {
+    s_exp[q] = a.act_exp[q];
+    s_cnt[q] = a.act_cnt[q];
+    s_off[q] = a.act_off[q];
   }
+  __syncthreads();
+  by_nks(a.F, [&](auto k) { down_routed<decltype(k)::value>(a, i0, n_act, s_exp, s_cnt, s_off, yw[wv]); });
+  if (a.Fs > 0) by_nks(a.Fs, [&](auto k) { down_shared<decltype(k)::value>(a, i0, n_act, yw[wv]); });
   __syncthreads();
   for (int q = tid; q < B * 16; q += kBlock) {
     const int t = q >> 4, nn = q & 15;
@@ -643,7 +764,8 @@ hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]
   const int n_wo = a.H / 16;
   const int n_q = (a.Dq + 15) / 16 * kBatchQkvSplit;
   const int n_rk = a.H / kBatchRtrK;
-  const int max_items = min(a.E, a.B * a.K) * (a.F / 16) + a.Fs / 16;
+  const int max_q = min(a.E, a.B * a.K) * ((a.B + 15) / 16);
+  const int max_items = max_q * (a.F / 16) + ((a.B + 15) / 16) * (a.Fs / 16);
   const int g4 = min(kBatchGateupGrid, (max_items + 7) & ~7);
   hipError_t e;
   auto rec = [&](int i, int j) { return ev ? hipEventRecord(ev[i][j], s) : hipSuccess; };

@@ -98,6 +98,8 @@ struct BatchArgs {
   int *act_exp, *act_cnt, *act_off;  // [E] per active slot
   int *pair_tok;      // [B*k]
   float *pair_w;      // [B*k]
+  int *gu_q;          // [4 E] gate/up work list: slot | (16-token chunk << 16)
+  int *n_q;           // [1]   its length
   unsigned *counter;  // [1] arrivals of the top-k workgroups (re-armed by the last)
   int B, H, Dq, Do, E, K, F, Fs;
   float eps;

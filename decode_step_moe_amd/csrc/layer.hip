@@ -85,11 +85,13 @@ struct Scratch {
   float *rlog_part = nullptr;    // [H/kBatchRtrK][maxB][E]
   float *hn = nullptr;           // [maxB][H]
   uint16_t *hp = nullptr;        // [2][maxB][H]
+  int *gu_q = nullptr;           // [4 E] gate/up work list
+  int *n_q = nullptr;            // [1]
 };
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-constexpr int kNumBuf = 23;
+constexpr int kNumBuf = 25;
 struct Layout {
   size_t off[kNumBuf];
   size_t total;
@@ -109,7 +111,8 @@ Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
       G * Bs * 8, Bs * E * 8, Bs * K * (size_t)c.expert_ffn * 8, Bs * (size_t)c.shared_ffn * 8,
       4, 4,
       // batched arrays
-      (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2};
+      (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2,
+      Bb ? 4 * E * 4 : size_t(0), Bb ? size_t(4) : size_t(0)};
   Layout L;
   size_t o = 0;
   for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
@@ -324,6 +327,8 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
   h->s.rlog_part = (float *)(b + L.off[20]);
   h->s.hn = (float *)(b + L.off[21]);
   h->s.hp = (uint16_t *)(b + L.off[22]);
+  h->s.gu_q = (int *)(b + L.off[23]);
+  h->s.n_q = (int *)(b + L.off[24]);
   // The hand-off counters start at zero and are re-armed by the kernels
   // themselves, and the tagged hand-off values start with tag 0, which no
   // step uses (tags are the step counter + 1), so no step ever needs a memset.
@@ -451,6 +456,8 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
     ba.act_off = h->s.act_off;
     ba.pair_tok = h->s.pair_tok;
     ba.pair_w = h->s.pair_w;
+    ba.gu_q = h->s.gu_q;
+    ba.n_q = h->s.n_q;
     ba.counter = h->s.counters + 2;
     ba.B = B;
     ba.H = c.hidden;

@@ -94,7 +94,7 @@ def test_batched_scratch_follows_the_path():
     c = good()                       # TP16 shard shapes, max_batch 64
     B, H, Dq, E = 64, 7168, 512, 384
     batched = (_a256(4 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
-               + _a256(2 * 2 * B * H))
+               + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(4))
     auto = dl.scratch_bytes(c, 256)
     c.path = dl.DL_PATH_MULTI
     multi = dl.scratch_bytes(c, 256)
