@@ -86,18 +86,6 @@ __device__ __forceinline__ void load8f(const float *p, float (&x)[8]) {
   x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
 }
 
-__device__ __forceinline__ uint4 zero_unless(bool keep, const uint4 &v) {
-  const unsigned m = keep ? 0xffffffffu : 0u;
-  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-}
-
-// Loads are issued in batches and kept apart from the MFMAs that consume
-// them by a scheduling barrier: left to itself the compiler interleaves each
-// load with its first use, which leaves one load in flight per wave.
-// A wave's loads complete in issue order, so a batch's first MFMA waits only
-// for the batch's first loads.
-#define DL_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
 // One wave: acc[c] += A_c (16 x 32 nks) . W^T (32 nks x 16) with bf16 A rows
 // at ap[c] and weight rows at wp (both already offset by this lane's row and
 // its 8g K position).  U K-steps of loads per batch; the K-steps of the last

@@ -169,6 +169,18 @@ __device__ __forceinline__ void stream_rows_bf16(const uint16_t *const (&w)[NR],
   }
 }
 
+__device__ __forceinline__ uint4 zero_unless(bool keep, const uint4 &v) {
+  const unsigned m = keep ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// Loads are issued in batches and kept apart from the arithmetic that
+// consumes them by a scheduling barrier: left to itself the compiler
+// interleaves each load with its first use, which leaves one load in flight
+// per wave.  A wave's loads complete in issue order, so a batch's first use
+// waits only for the batch's first loads.
+#define DL_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 // ---- row GEMV building blocks -------------------------------------------------
 struct ActBf16Rows {  // bf16 [tokens][ld], token index clamped to tmax
   const uint16_t *base;
@@ -238,66 +250,75 @@ __device__ __forceinline__ void wave_rows_dot(const uint16_t *const (&w)[NR], in
     for (int t = 0; t < NT; ++t) out[r][t] = wave_sum(acc[r][t]);
 }
 
-// ---- DPP wave arg-max ---------------------------------------------------------
-// (value, index) packed into one 64-bit key that orders like "larger value,
-// then smaller index": the float's bits mapped to an order-preserving
-// unsigned word in the high half, the inverted index in the low half.  The
-// wave maximum of the keys is taken with lane permutes (no branches).
-__device__ __forceinline__ uint64_t rank_key(float v, int i) {
-  unsigned u = __float_as_uint(v == 0.f ? 0.f : v);  // -0 ranks as +0 (they compare equal)
+// ---- wave top-k ---------------------------------------------------------------
+// A float mapped to an unsigned word that orders like the float (-0 ranks as
+// +0, the two compare equal); the result is at least 1, so that 0 can mark an
+// absent or taken candidate.
+__device__ __forceinline__ unsigned rank_bits(float v) {
+  unsigned u = __float_as_uint(v == 0.f ? 0.f : v);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (unsigned)i);
+  return u > 1u ? u : 1u;
 }
-__device__ __forceinline__ void key_unpack(uint64_t k, float &v, int &i) {
-  unsigned u = (unsigned)(k >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-  v = __uint_as_float(u);
-  i = (int)(0xffffffffu - (unsigned)k);
+__device__ __forceinline__ float unrank_bits(unsigned u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+__device__ __forceinline__ unsigned dpp_umax(unsigned v) {
   // rows outside ROWS (and lanes with no source) compare against themselves
-  const int lo = (int)(unsigned)k, hi = (int)(unsigned)(k >> 32);
-  const unsigned olo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
-  const unsigned ohi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > k ? o : k;
+  const unsigned o = (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xf, false);
+  return o > v ? o : v;
 }
-// Largest key over the wave; result uniform.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-  k = dpp_max_step<kDppXor1, 0xf>(k);
-  k = dpp_max_step<kDppXor2, 0xf>(k);
-  k = dpp_max_step<kDppHalfMirror, 0xf>(k);
-  k = dpp_max_step<kDppMirror, 0xf>(k);  // rows of 16 uniform
-  k = dpp_max_step<0x142, 0xa>(k);       // row_bcast:15 -> rows 1, 3
-  k = dpp_max_step<0x143, 0xc>(k);       // row_bcast:31 -> rows 2, 3
-  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)k, 63);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(k >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Largest word over the wave; result uniform.
+__device__ __forceinline__ unsigned wave_umax(unsigned v) {
+  v = dpp_umax<kDppXor1, 0xf>(v);
+  v = dpp_umax<kDppXor2, 0xf>(v);
+  v = dpp_umax<kDppHalfMirror, 0xf>(v);
+  v = dpp_umax<kDppMirror, 0xf>(v);  // rows of 16 uniform
+  v = dpp_umax<0x142, 0xa>(v);       // row_bcast:15 -> rows 1, 3
+  v = dpp_umax<0x143, 0xc>(v);       // row_bcast:31 -> rows 2, 3
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Top-k over one wave.  Lane l offers the candidates e = l + 64 c (c < NC,
 // e < E) with values lv[c]; lane j < K receives the j-th pick in the order
 // "larger value first, then smaller index".  The picks are K distinct
-// indices below E whatever the values (NaN ranks above +inf), because a key
-// never equals 0, the mark of an absent or taken candidate.  Needs K <= E.
+// indices below E whatever the values (a NaN ranks above +inf).  Needs K <= E.
+// Each round takes the wave maximum of the 32-bit value keys; the lowest
+// index holding that key is found through a ballot (a second maximum, over
+// inverted indices, only when several lanes hold it).
 template <int NC>
 __device__ __forceinline__ void wave_topk(const float (&lv)[NC], int E, int K, int &my_idx, float &my_v) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[NC];
+  unsigned key[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) key[c] = lane + 64 * c < E ? rank_key(lv[c], lane + 64 * c) : 0ull;
-  uint64_t mine = 0;
+  for (int c = 0; c < NC; ++c) key[c] = lane + 64 * c < E ? rank_bits(lv[c]) : 0u;
+  int mine_idx = 0;
+  unsigned mine_key = 1u;
   for (int j = 0; j < K; ++j) {
-    uint64_t best = 0;
+    unsigned m = key[0];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) best = key[c] > best ? key[c] : best;
-    best = wave_max_key(best);
+    for (int c = 1; c < NC; ++c) m = key[c] > m ? key[c] : m;
+    const unsigned g = wave_umax(m);
+    // this lane's lowest index holding g, as 0xffffffff - index (0: none)
+    unsigned inv = 0u;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) key[c] = key[c] == best ? 0ull : key[c];
-    mine = lane == j ? best : mine;
+    for (int c = NC - 1; c >= 0; --c) inv = key[c] == g ? 0xffffffffu - (unsigned)(lane + 64 * c) : inv;
+    const unsigned long long holders = __ballot(inv != 0u);
+    unsigned best;
+    if (__popcll(holders) == 1)
+      best = (unsigned)__builtin_amdgcn_readlane((int)inv, __ffsll((long long)holders) - 1);
+    else
+      best = wave_umax(inv);
+    const int id = (int)(0xffffffffu - best);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) key[c] = id == lane + 64 * c ? 0u : key[c];
+    if (lane == j) {
+      mine_idx = id;
+      mine_key = g;
+    }
   }
-  key_unpack(mine, my_v, my_idx);
+  my_idx = mine_idx;
+  my_v = unrank_bits(mine_key);
 }
 
 __device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }

@@ -155,8 +155,8 @@ struct Lds {
   int pair_exp[kFusedMaxPairs];
   float pair_w[kFusedMaxPairs];
   int n_active;
-  // gate/up sums of a round: [item][W1 | W3][token]
-  float uv[8][2][kFusedMaxB];
+  // gate/up sums of a round: [item][K half][W1 | W3][token]
+  float uv[4][2][2][kFusedMaxB];
   float sqw[kFWaves][kFusedMaxB];  // per-wave partial sums of r1^2
   int arrive;
   int bad;
@@ -208,49 +208,10 @@ __device__ float oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
   return sq;
 }
 
-// 16-byte weight chunks per lane in flight per row, by token count
-template <int NT>
-constexpr int cpb_for() { return NT <= 2 ? 16 : NT <= 4 ? 8 : 4; }
-
 // ---- phase C: gate/up rows --------------------------------------------------
-// One bf16 row (16-byte chunks c = lane + 64u, u < CPB, of [c0, cend)) dotted
-// with NT gathered fp32 hg rows, split into a load step and a use step so that
-// a wave can have the loads of several rows in flight before it uses any.
-template <int NT, int CPB>
-struct RowDot {
-  uint4 wv[CPB];
-  __device__ __forceinline__ void issue(const uint16_t *row, int c0, int cend) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int c = c0 + lane + kWave * u;
-      wv[u] = c < cend ? ld_stream16(row + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void use(const HgGather<NT> &act, int c0, int cend, float (&acc)[NT]) const {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int c = c0 + lane + kWave * u;
-      if (c < cend) {
-        float wf[8];
-        unpack8(wv[u], wf);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          float hv[8];
-          act.load8(t, c * 8, hv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[t] = fmaf(wf[e], hv[e], acc[t]);
-        }
-      }
-    }
-  }
-};
-
-// A gate/up row: row f of W1/W3 of a routed expert over its tokens, or row f
-// of S1/S3 of the shared expert over all B tokens.
+// A gate/up item's tokens: a routed expert's LDS token list, or all B tokens
+// of the shared expert.
 struct GuRow {
-  const uint16_t *row = nullptr;
   const int *toks = nullptr;  // LDS token list, or nullptr for tokens 0..cnt-1
   int cnt = 0;
   __device__ __forceinline__ int tok(int t) const {
@@ -259,34 +220,63 @@ struct GuRow {
   }
 };
 
-// One wave: rows A and (if B.row) B, with every weight load of both issued
-// before any is used.  Sums per token come back in every lane.
+// 16-byte chunks per lane per load batch: 2 weight words and NT activation
+// octets each, about 100 VGPRs in flight.
 template <int NT>
-__device__ void gateup_two(const FusedArgs &a, const GuRow &A, const GuRow &Bw, float (&sa)[NT], float (&sb)[NT]) {
-  constexpr int CPB = NT <= 2 ? 16 : NT <= 4 ? 8 : 4;
-  HgGather<NT> ga, gb;
-  ga.base = gb.base = a.hg;
-  ga.ld = gb.ld = a.H;
+constexpr int gu_cpb() { return NT <= 1 ? 7 : NT <= 2 ? 4 : NT <= 4 ? 2 : 1; }
+
+// One wave: the W1 and W3 rows of one item over 16-byte chunks [cbeg, cend)
+// (8 elements each), dotted with the hg rows of the item's tokens.  Every
+// load of a batch - weights and activations - is issued before any is used,
+// so a batch costs one memory round trip.  Sums come back in every lane.
+template <int NT>
+__device__ void gateup_pair(const GuRow &r, const uint16_t *row1, const uint16_t *row3, const float *hg, int H,
+                            int cbeg, int cend, float (&su)[NT], float (&sv)[NT]) {
+  constexpr int CPB = gu_cpb<NT>();
+  const int lane = threadIdx.x & 63;
+  const float *hrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) hrow[t] = hg + (size_t)r.tok(t) * H;
+  float au[NT], av[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) au[t] = av[t] = 0.f;
+  for (int c0 = cbeg; c0 < cend; c0 += CPB * kWave) {
+    uint4 w1[CPB], w3[CPB];
+    float4 x[CPB][NT][2];
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int cc = min(c0 + lane + kWave * u, cend - 1);
+      w1[u] = ld_stream16(row1 + (size_t)cc * 8);
+      w3[u] = ld_stream16(row3 + (size_t)cc * 8);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        x[u][t][0] = ld16f(hrow[t] + (size_t)cc * 8);
+        x[u][t][1] = ld16f(hrow[t] + (size_t)cc * 8 + 4);
+      }
+    }
+    DL_SCHED_FENCE();
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const bool on = c0 + lane + kWave * u < cend;
+      float f1[8], f3[8];
+      unpack8(zero_unless(on, w1[u]), f1);
+      unpack8(zero_unless(on, w3[u]), f3);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float hv[8] = {x[u][t][0].x, x[u][t][0].y, x[u][t][0].z, x[u][t][0].w,
+                             x[u][t][1].x, x[u][t][1].y, x[u][t][1].z, x[u][t][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          au[t] = fmaf(f1[e], hv[e], au[t]);
+          av[t] = fmaf(f3[e], hv[e], av[t]);
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    ga.tok[t] = A.tok(t);
-    gb.tok[t] = Bw.row ? Bw.tok(t) : 0;
-  }
-  float acc_a[NT], acc_b[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc_a[t] = acc_b[t] = 0.f;
-  const int nch = a.H >> 3;
-  for (int c0 = 0; c0 < nch; c0 += CPB * kWave) {
-    RowDot<NT, CPB> da, db;
-    da.issue(A.row, c0, nch);
-    if (Bw.row) db.issue(Bw.row, c0, nch);
-    da.use(ga, c0, nch, acc_a);
-    if (Bw.row) db.use(gb, c0, nch, acc_b);
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    sa[t] = wave_sum(acc_a[t]);
-    sb[t] = wave_sum(acc_b[t]);
+    su[t] = wave_sum(au[t]);
+    sv[t] = wave_sum(av[t]);
   }
 }
 
@@ -435,25 +425,44 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     }
   }
   stamp(a, 1);
-  const int er[2] = {w, w + G};  // this workgroup's router rows
+  // Units u = w and w + G of this workgroup: u < E is router row u (fp32,
+  // H * 4 bytes); E <= u < E + fs_b is the shared expert's row pair
+  // f = u - E (S1 row f then S3 row f, bf16, also H * 4 bytes).  Shared rows
+  // f >= fs_b join the routed gate/up items of phase C.
+  const int fs_b = max(0, min(a.Fs, 2 * G - E));
+  const int er[2] = {w, w + G};
+  int kind[2];  // 0 none, 1 router row, 2 shared row pair
+#pragma unroll
+  for (int q = 0; q < 2; ++q) kind[q] = er[q] < E ? 1 : er[q] < E + fs_b ? 2 : 0;
   if (!ctl) {
-    // stream threads: the router rows (static weights) -> LDS
+    // stream threads: the unit rows (static weights) -> LDS
     uint4 v[2][kUnitJ];
-    const int nw = H >> 2;  // 16-byte words per fp32 row
+    const int nw = H >> 2;  // 16-byte words per unit
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int j = 0; j < kUnitJ; ++j) {
-        const int i = st + kStr * j;
-        v[q][j] = er[q] < E && i < nw ? ld_stream16(reinterpret_cast<const uint4 *>(a.w_router + (size_t)er[q] * H) + i)
-                                      : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      // router: words [0, nw) of the fp32 row; shared: S1 row f in words
+      // [0, nw/2) and S3 row f in words [nw/2, nw)
+      const int half = nw >> 1;
+      const uint4 *src0, *src1;
+      if (kind[q] == 2) {
+        src0 = reinterpret_cast<const uint4 *>(a.s1 + (size_t)(er[q] - E) * H);
+        src1 = reinterpret_cast<const uint4 *>(a.s3 + (size_t)(er[q] - E) * H);
+      } else {
+        src0 = reinterpret_cast<const uint4 *>(a.w_router + (size_t)min(er[q], E - 1) * H);
+        src1 = src0 + half;
       }
 #pragma unroll
+      for (int j = 0; j < kUnitJ; ++j) {
+        const int i = st + kStr * j;
+        v[q][j] = kind[q] && i < nw ? ld_stream16(i < half ? src0 + i : src1 + (i - half)) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int j = 0; j < kUnitJ; ++j) {
         const int i = st + kStr * j;
-        if (er[q] < E && i < nw) L.u.unit[q][i] = v[q][j];
+        if (kind[q] && i < nw) L.u.unit[q][i] = v[q][j];
       }
   } else {
     // control threads: every workgroup's partial sums (thread q: workgroup q)
@@ -482,55 +491,75 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   __syncthreads();
   stamp(a, 4);
 
-  // ================= phase B: router logits =================
+  // ================= phase B: router logits and shared-expert rows ==========
   if (a.h_out && ni > 0)
     for (int q = tid; q < B * ni; q += kFT) {
       const int t = q / ni, il = q % ni;
       a.h_out[(size_t)t * H + i0 + il] = L.hg[t][il] * L.inv_rms[t];
     }
-  if (er[0] < E) {  // uniform over the workgroup
-    const bool two = er[1] < E;
-    const int nc = H >> 3;  // 8-element chunks c = tid + kFT*j
+  if (kind[0] || kind[1]) {  // uniform over the workgroup
+    const int nc = H >> 3;    // 8-element chunks c = tid + kFT*j
     for (int t = 0; t < B; ++t) {
       const float *hrow = a.hg + (size_t)t * H;
-      float p0 = 0.f, p1 = 0.f;
+      float p[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [unit][router or S1 | S3]
+      float4 hx[kChunkJ][2];
+#pragma unroll
+      for (int j = 0; j < kChunkJ; ++j) {
+        const int c = min(tid + kFT * j, nc - 1);
+        hx[j][0] = ld16f(hrow + 8 * c);
+        hx[j][1] = ld16f(hrow + 8 * c + 4);
+      }
 #pragma unroll
       for (int j = 0; j < kChunkJ; ++j) {
         const int c = tid + kFT * j;
         if (c < nc) {
-          const float4 h0 = ld16f(hrow + 8 * c), h1 = ld16f(hrow + 8 * c + 4);
-          const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-          float wa[8];
-          as8(L.u.unit[0][2 * c], L.u.unit[0][2 * c + 1], wa);
+          const float hv[8] = {hx[j][0].x, hx[j][0].y, hx[j][0].z, hx[j][0].w,
+                               hx[j][1].x, hx[j][1].y, hx[j][1].z, hx[j][1].w};
 #pragma unroll
-          for (int k2 = 0; k2 < 8; ++k2) p0 = fmaf(wa[k2], hv[k2], p0);
-          if (two) {
-            as8(L.u.unit[1][2 * c], L.u.unit[1][2 * c + 1], wa);
+          for (int q = 0; q < 2; ++q) {
+            float wa[8];
+            if (kind[q] == 1) {
+              as8(L.u.unit[q][2 * c], L.u.unit[q][2 * c + 1], wa);
 #pragma unroll
-            for (int k2 = 0; k2 < 8; ++k2) p1 = fmaf(wa[k2], hv[k2], p1);
+              for (int k2 = 0; k2 < 8; ++k2) p[q][0] = fmaf(wa[k2], hv[k2], p[q][0]);
+            } else if (kind[q] == 2) {
+              unpack8(L.u.unit[q][c], wa);
+#pragma unroll
+              for (int k2 = 0; k2 < 8; ++k2) p[q][0] = fmaf(wa[k2], hv[k2], p[q][0]);
+              unpack8(L.u.unit[q][nc + c], wa);
+#pragma unroll
+              for (int k2 = 0; k2 < 8; ++k2) p[q][1] = fmaf(wa[k2], hv[k2], p[q][1]);
+            }
           }
         }
       }
-      p0 = wave_sum(p0);
-      p1 = wave_sum(p1);
-      if (lane == 0) {
-        L.red[(wv * kFusedMaxB + t) * 2 + 0] = p0;
-        L.red[(wv * kFusedMaxB + t) * 2 + 1] = p1;
-      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float v = wave_sum(p[q][m]);
+          if (lane == 0) L.red[((wv * kFusedMaxB + t) * 2 + q) * 2 + m] = v;
+        }
     }
     __syncthreads();
     if (tid < 2 * B) {
       const int q = tid & 1, t = tid >> 1;
-      if (q == 0 || two) {
-        float s = 0.f;
-        for (int v = 0; v < kFWaves; ++v) s += L.red[(v * kFusedMaxB + t) * 2 + q];
-        const float l = s * L.inv_rms[t];
+      float sp[2] = {0.f, 0.f};
+      for (int v = 0; v < kFWaves; ++v) {
+        sp[0] += L.red[((v * kFusedMaxB + t) * 2 + q) * 2 + 0];
+        sp[1] += L.red[((v * kFusedMaxB + t) * 2 + q) * 2 + 1];
+      }
+      if (kind[q] == 1) {
+        const float l = sp[0] * L.inv_rms[t];
         put_tagged(a.logit + (size_t)t * E + er[q], l, tag);
         if (a.logits_out) a.logits_out[(size_t)t * E + er[q]] = l;
+      } else if (kind[q] == 2) {
+        const int f = er[q] - E;
+        put_tagged(a.act_s + (size_t)t * a.Fs + f, silu_mul(sp[0] * L.inv_rms[t], sp[1] * L.inv_rms[t]), tag);
       }
     }
   }
-  __syncthreads();   // the router rows in LDS are dead from here on
+  __syncthreads();   // the unit rows in LDS are dead from here on
   stamp(a, 5);
 
   // ================= phase C =================
@@ -599,43 +628,44 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   __syncthreads();
   stamp(a, 8);
   // gate/up items: routed (active slot, ffn row) pairs, then the shared
-  // expert's ffn rows; workgroup w takes items w, w + G, ... (so the heavier
-  // shared items, which carry every token, spread over the grid).  Rounds of
-  // 8 items: wave v takes the W1 (v even) or W3 (v odd) rows of items
-  // v/2 and 4 + v/2 of the round.
+  // expert's rows f >= fs_b that phase B did not take; workgroup w takes
+  // items w, w + G, ...  Rounds of 4 items: waves 2i and 2i + 1 take both
+  // rows (W1 and W3) of item i of the round over the two halves of K, so the
+  // item's activation loads serve both rows.
   {
     const int n_rt = L.n_active * a.F;
-    const int total = n_rt + a.Fs;
+    const int total = n_rt + (a.Fs - fs_b);
     const int nit = w < total ? (total - w + G - 1) / G : 0;
-    auto item_row = [&](int k, int mat, GuRow &r) {
-      const int it = w + G * k;
-      if (it < n_rt) {
-        const int slot = it / a.F, f = it % a.F;
-        r.row = (mat ? a.w3 : a.w1) + ((size_t)L.act_exp[slot] * a.F + f) * H;
-        r.toks = L.pair_tok + L.act_off[slot];
-        r.cnt = L.act_cnt[slot];
-      } else {
-        r.row = (mat ? a.s3 : a.s1) + (size_t)(it - n_rt) * H;
-        r.toks = nullptr;
-        r.cnt = B;
-      }
-    };
-    for (int k0 = 0; k0 < nit; k0 += 8) {
-      const int ka = k0 + (wv >> 1), kb = k0 + 4 + (wv >> 1), mat = wv & 1;
-      GuRow ra, rb;
-      if (ka < nit) item_row(ka, mat, ra);
-      if (kb < nit) item_row(kb, mat, rb);
-      if (ka < nit) {
-        const int nt = max(ra.cnt, rb.row ? rb.cnt : 0);
-        by_tokens(nt, [&](auto ntc) {
+    const int nc = H >> 3, cmid = nc >> 1;
+    for (int k0 = 0; k0 < nit; k0 += 4) {
+      const int ki = k0 + (wv >> 1), hf = wv & 1;
+      if (ki < nit) {
+        const int it = w + G * ki;
+        GuRow r;
+        const uint16_t *row1, *row3;
+        if (it < n_rt) {
+          const int slot = it / a.F, f = it % a.F;
+          const size_t ro = ((size_t)L.act_exp[slot] * a.F + f) * H;
+          row1 = a.w1 + ro;
+          row3 = a.w3 + ro;
+          r.toks = L.pair_tok + L.act_off[slot];
+          r.cnt = L.act_cnt[slot];
+        } else {
+          const size_t ro = (size_t)(fs_b + it - n_rt) * H;
+          row1 = a.s1 + ro;
+          row3 = a.s3 + ro;
+          r.toks = nullptr;
+          r.cnt = B;
+        }
+        by_tokens(r.cnt, [&](auto ntc) {
           constexpr int NT = decltype(ntc)::value;
-          float sa[NT], sb[NT];
-          gateup_two<NT>(a, ra, rb, sa, sb);
+          float su[NT], sv[NT];
+          gateup_pair<NT>(r, row1, row3, a.hg, H, hf ? cmid : 0, hf ? nc : cmid, su, sv);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             if (lane == t) {
-              L.uv[wv >> 1][mat][t] = sa[t];
-              L.uv[4 + (wv >> 1)][mat][t] = sb[t];
+              L.uv[wv >> 1][hf][0][t] = su[t];
+              L.uv[wv >> 1][hf][1][t] = sv[t];
             }
           }
         });
@@ -643,19 +673,20 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       __syncthreads();
       // combine: thread (item-in-round is, token j)
       const int is = tid >> 3, j = tid & 7;
-      if (is < 8 && k0 + is < nit) {
+      if (is < 4 && k0 + is < nit) {
         const int it = w + G * (k0 + is);
+        const float su = L.uv[is][0][0][j] + L.uv[is][1][0][j];
+        const float sv = L.uv[is][0][1][j] + L.uv[is][1][1][j];
         if (it < n_rt) {
           const int s2 = it / a.F, f2 = it % a.F;
           const int c2 = L.act_cnt[s2], o2 = L.act_off[s2];
           if (j < c2) {
             const int t = L.pair_tok[o2 + j];
-            const float u = L.uv[is][0][j] * L.inv_rms[t], v = L.uv[is][1][j] * L.inv_rms[t];
-            put_tagged(a.act + (size_t)(o2 + j) * a.F + f2, silu_mul(u, v), tag);
+            put_tagged(a.act + (size_t)(o2 + j) * a.F + f2, silu_mul(su * L.inv_rms[t], sv * L.inv_rms[t]), tag);
           }
         } else if (j < B) {
-          const float u = L.uv[is][0][j] * L.inv_rms[j], v = L.uv[is][1][j] * L.inv_rms[j];
-          put_tagged(a.act_s + (size_t)j * a.Fs + (it - n_rt), silu_mul(u, v), tag);
+          put_tagged(a.act_s + (size_t)j * a.Fs + (fs_b + it - n_rt),
+                     silu_mul(su * L.inv_rms[j], sv * L.inv_rms[j]), tag);
         }
       }
       __syncthreads();
