@@ -264,6 +264,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-batches", action="store_true", help="headline workload only")
+    ap.add_argument("--batches", default=",".join(str(c) for c in BATCH_CFGS),
+                    help="workload ids measured under \"batches\" (comma-separated)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--counter-pass", action="store_true",
@@ -288,7 +290,7 @@ def main():
                            path=1)
     batches = {}
     if not args.no_batches:
-        for c in BATCH_CFGS:
+        for c in [int(v) for v in args.batches.split(",") if v.strip()]:
             r, _ = time_config(c, max(20, args.steps // 2), args.warmup, None)
             batches[r["workload"]] = _summary(r)
     us = head["graph_us"]

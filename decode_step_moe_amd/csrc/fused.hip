@@ -577,7 +577,9 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     }
     int my_idx;
     float my_l;
+    stamp(a, 14);
     wave_topk<NC>(lv, E, K, my_idx, my_l);
+    stamp(a, 15);
     // scores of the k picks, renormalised (lane j holds pick j)
     const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
     const float ssum = wave_sum(s);
@@ -625,6 +627,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     }
     if (lane == 0) L.n_active = __popcll(fm);
   }
+  stamp(a, 12);
   __syncthreads();
   stamp(a, 8);
   // gate/up items: routed (active slot, ffn row) pairs, then the shared
