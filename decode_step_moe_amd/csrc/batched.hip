@@ -472,7 +472,7 @@ __device__ void gateup_valu(const BatchArgs &a, const GuItem &it) {
     const int nt = min(8, it.cnt - t0);
     auto pass = [&](auto ntc) {
       constexpr int NT = decltype(ntc)::value;
-      constexpr int CPB = NT <= 4 ? 4 : 2;
+      constexpr int CPB = NT <= 2 ? 4 : NT <= 4 ? 2 : 1;
       HgGather<NT> act;
       act.base = a.hn;
       act.ld = H;

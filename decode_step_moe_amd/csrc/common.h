@@ -182,32 +182,41 @@ __device__ __forceinline__ uint4 zero_unless(bool keep, const uint4 &v) {
 #define DL_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // ---- row GEMV building blocks -------------------------------------------------
+// Activation sources for wave_rows_dot: raw() requests 8 consecutive values
+// of token t at element k (no use yet), unpack() turns them into fp32.
 struct ActBf16Rows {  // bf16 [tokens][ld], token index clamped to tmax
   const uint16_t *base;
   int ld, tmax;
-  __device__ __forceinline__ void load8(int t, int k, float (&v)[8]) const {
-    int tt = t < tmax ? t : tmax;
-    unpack8(ld16(base + (size_t)tt * ld + k), v);
+  typedef uint4 Raw;
+  __device__ __forceinline__ Raw raw(int t, int k) const {
+    const int tt = t < tmax ? t : tmax;
+    return ld16(base + (size_t)tt * ld + k);
   }
+  __device__ __forceinline__ void unpack(const Raw &r, float (&v)[8]) const { unpack8(r, v); }
 };
 
 template <int NT>
-struct HgGather {  // fp32 hg rows of a token list
+struct HgGather {  // fp32 rows of a token list
   const float *base;
   int ld;
   int tok[NT];
-  __device__ __forceinline__ void load8(int t, int k, float (&v)[8]) const {
+  struct Raw { float4 a, b; };
+  __device__ __forceinline__ Raw raw(int t, int k) const {
     const float *p = base + (size_t)tok[t] * ld + k;
-    float4 u = ld16f(p), w = ld16f(p + 4);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-    v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+    return Raw{ld16f(p), ld16f(p + 4)};
+  }
+  __device__ __forceinline__ void unpack(const Raw &r, float (&v)[8]) const {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
   }
 };
 
 // One wave: dot products of NR bf16 weight rows (16-byte chunks [cbeg, cend)
 // of each, i.e. elements [8 cbeg, 8 cend)) with NT activation rows.  Lane l
-// takes chunks cbeg + l, cbeg + l + 64, ...; up to CPB chunks of every row are
-// loaded before any is consumed.  The sums come back in every lane.
+// takes chunks cbeg + l, cbeg + l + 64, ...; the weight and activation loads
+// of CPB chunks are issued together (addresses clamped to the last chunk,
+// weights of chunks beyond it zeroed afterwards), so a batch is one memory
+// round trip.  The sums come back in every lane.
 template <int NR, int NT, int CPB, class Act>
 __device__ __forceinline__ void wave_rows_dot(const uint16_t *const (&w)[NR], int cbeg, int cend,
                                               const Act &act, float (&out)[NR][NT]) {
@@ -219,28 +228,30 @@ __device__ __forceinline__ void wave_rows_dot(const uint16_t *const (&w)[NR], in
     for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
   for (int c0 = cbeg; c0 < cend; c0 += CPB * kWave) {
     uint4 wv[CPB][NR];
+    typename Act::Raw ar[CPB][NT];
 #pragma unroll
     for (int u = 0; u < CPB; ++u) {
-      const int c = c0 + lane + kWave * u;
+      const int c = min(c0 + lane + kWave * u, cend - 1);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) wv[u][r] = c < cend ? ld_stream16(w[r] + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+      for (int r = 0; r < NR; ++r) wv[u][r] = ld_stream16(w[r] + (size_t)c * 8);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) ar[u][t] = act.raw(t, c * 8);
     }
+    DL_SCHED_FENCE();
 #pragma unroll
     for (int u = 0; u < CPB; ++u) {
-      const int c = c0 + lane + kWave * u;
-      if (c < cend) {
-        float a[NT][8];
+      const bool on = c0 + lane + kWave * u < cend;
+      float a[NT][8];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) act.load8(t, c * 8, a[t]);
+      for (int t = 0; t < NT; ++t) act.unpack(ar[u][t], a[t]);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          float wf[8];
-          unpack8(wv[u][r], wf);
+      for (int r = 0; r < NR; ++r) {
+        float wf[8];
+        unpack8(zero_unless(on, wv[u][r]), wf);
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][t] = fmaf(wf[e], a[t][e], acc[r][t]);
-        }
+          for (int e = 0; e < 8; ++e) acc[r][t] = fmaf(wf[e], a[t][e], acc[r][t]);
       }
     }
   }

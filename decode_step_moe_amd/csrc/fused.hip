@@ -157,6 +157,9 @@ struct Lds {
   int n_active;
   // gate/up sums of a round: [item][K half][W1 | W3][token]
   float uv[4][2][2][kFusedMaxB];
+  // list building: per-wave partial counts of keys below / of the same expert
+  int part_lt[kFWaves][kWave];
+  int part_same[kFWaves][kWave];
   float sqw[kFWaves][kFusedMaxB];  // per-wave partial sums of r1^2
   int arrive;
   int bad;
@@ -186,7 +189,7 @@ __device__ float oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
     gn[r] = mine ? bf16_lo(a.gain[i]) : 0.f;
   }
   float o[NR][NT];
-  wave_rows_dot<NR, NT, 2>(rows, 0, nch, act, o);
+  wave_rows_dot<NR, NT, (NT >= 8 ? 1 : 2)>(rows, 0, nch, act, o);
   float sq = 0.f;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -290,7 +293,7 @@ __device__ void gateup_pair(const GuRow &r, const uint16_t *row1, const uint16_t
 template <int LPG>
 struct Down {
   static constexpr int NG = kFT / LPG;  // lane groups
-  static constexpr int R = 8;
+  static constexpr int R = 16;  // units per lane group per load batch
   const FusedArgs &a;
   Lds &L;
   int i0, ni, item0, n_units;
@@ -301,15 +304,19 @@ struct Down {
                       : a.w2 + ((size_t)L.pair_exp[item - a.B] * a.H + i0 + il) * a.F;
   }
   // stream threads: word k of the staged range is unit k / LPG, lane k % LPG
+  // (addresses clamped to the last word, so every load of the batch issues
+  // unconditionally and the batch is one memory round trip)
   __device__ void stage() const {
     const int n = u0_end() * LPG;
+    if (n == 0) return;
     constexpr int J = kFusedW2Words / kStr;  // 16
     uint4 v[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int k = (threadIdx.x - kCtl) + kStr * j;
-      v[j] = k < n ? ld_stream16(row(k / LPG) + (k % LPG) * 8) : make_uint4(0, 0, 0, 0);
+      const int k = min((threadIdx.x - kCtl) + kStr * j, n - 1);
+      v[j] = ld_stream16(row(k / LPG) + (k % LPG) * 8);
     }
+    DL_SCHED_FENCE();
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int k = (threadIdx.x - kCtl) + kStr * j;
@@ -348,10 +355,8 @@ struct Down {
     for (int ub = ue; ub < n_units; ub += NG * R) {
       uint4 wv[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int u = ub + g + NG * r;
-        wv[r] = u < n_units ? ld_stream16(row(u) + lg * 8) : make_uint4(0, 0, 0, 0);
-      }
+      for (int r = 0; r < R; ++r) wv[r] = ld_stream16(row(min(ub + g + NG * r, n_units - 1)) + lg * 8);
+      DL_SCHED_FENCE();
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int u = ub + g + NG * r;
@@ -499,47 +504,58 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     }
   if (kind[0] || kind[1]) {  // uniform over the workgroup
     const int nc = H >> 3;    // 8-element chunks c = tid + kFT*j
-    for (int t = 0; t < B; ++t) {
-      const float *hrow = a.hg + (size_t)t * H;
-      float p[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [unit][router or S1 | S3]
-      float4 hx[kChunkJ][2];
+    constexpr int TG = 4;  // tokens whose hg chunks are requested together
+    for (int t0 = 0; t0 < B; t0 += TG) {
+      float4 hx[TG][kChunkJ][2];
 #pragma unroll
-      for (int j = 0; j < kChunkJ; ++j) {
-        const int c = min(tid + kFT * j, nc - 1);
-        hx[j][0] = ld16f(hrow + 8 * c);
-        hx[j][1] = ld16f(hrow + 8 * c + 4);
+      for (int tt = 0; tt < TG; ++tt) {
+        const float *hrow = a.hg + (size_t)min(t0 + tt, B - 1) * H;
+#pragma unroll
+        for (int j = 0; j < kChunkJ; ++j) {
+          const int c = min(tid + kFT * j, nc - 1);
+          hx[tt][j][0] = ld16f(hrow + 8 * c);
+          hx[tt][j][1] = ld16f(hrow + 8 * c + 4);
+        }
       }
+      DL_SCHED_FENCE();
 #pragma unroll
-      for (int j = 0; j < kChunkJ; ++j) {
-        const int c = tid + kFT * j;
-        if (c < nc) {
-          const float hv[8] = {hx[j][0].x, hx[j][0].y, hx[j][0].z, hx[j][0].w,
-                               hx[j][1].x, hx[j][1].y, hx[j][1].z, hx[j][1].w};
+      for (int tt = 0; tt < TG; ++tt) {
+        const int t = t0 + tt;
+        if (t >= B) break;
+        float p[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [unit][router or S1 | S3]
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            float wa[8];
-            if (kind[q] == 1) {
-              as8(L.u.unit[q][2 * c], L.u.unit[q][2 * c + 1], wa);
+        for (int j = 0; j < kChunkJ; ++j) {
+          const int c = tid + kFT * j;
+          if (c < nc) {
+            const float hv[8] = {hx[tt][j][0].x, hx[tt][j][0].y, hx[tt][j][0].z, hx[tt][j][0].w,
+                                 hx[tt][j][1].x, hx[tt][j][1].y, hx[tt][j][1].z, hx[tt][j][1].w};
 #pragma unroll
-              for (int k2 = 0; k2 < 8; ++k2) p[q][0] = fmaf(wa[k2], hv[k2], p[q][0]);
-            } else if (kind[q] == 2) {
-              unpack8(L.u.unit[q][c], wa);
+            for (int q = 0; q < 2; ++q) {
+              float wa[8];
+              if (kind[q] == 1) {
+                as8(L.u.unit[q][2 * c], L.u.unit[q][2 * c + 1], wa);
 #pragma unroll
-              for (int k2 = 0; k2 < 8; ++k2) p[q][0] = fmaf(wa[k2], hv[k2], p[q][0]);
-              unpack8(L.u.unit[q][nc + c], wa);
+                for (int k2 = 0; k2 < 8; ++k2) p[q][0] = fmaf(wa[k2], hv[k2], p[q][0]);
+              } else if (kind[q] == 2) {
+                unpack8(L.u.unit[q][c], wa);
 #pragma unroll
-              for (int k2 = 0; k2 < 8; ++k2) p[q][1] = fmaf(wa[k2], hv[k2], p[q][1]);
+                for (int k2 = 0; k2 < 8; ++k2) p[q][0] = fmaf(wa[k2], hv[k2], p[q][0]);
+                unpack8(L.u.unit[q][nc + c], wa);
+#pragma unroll
+                for (int k2 = 0; k2 < 8; ++k2) p[q][1] = fmaf(wa[k2], hv[k2], p[q][1]);
+              }
             }
           }
         }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            if (kind[q] == 0 || (m == 1 && kind[q] != 2)) continue;
+            const float v = wave_sum(p[q][m]);
+            if (lane == 0) L.red[((wv * kFusedMaxB + t) * 2 + q) * 2 + m] = v;
+          }
       }
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float v = wave_sum(p[q][m]);
-          if (lane == 0) L.red[((wv * kFusedMaxB + t) * 2 + q) * 2 + m] = v;
-        }
     }
     __syncthreads();
     if (tid < 2 * B) {
@@ -566,8 +582,8 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   if (ctl) gather_tagged(a.logit, L.u.logits, tid, kCtl, B * E, tag, a.spin_limit, &L.bad);
   __syncthreads();
   stamp(a, 7);
-  // top-k per token on the control waves: lane l holds experts l, l+64, ...
-  for (int t = wv; ctl && t < B; t += kCtl / kWave) {
+  // top-k per token, one wave per token: lane l holds experts l, l+64, ...
+  for (int t = wv; t < B; t += kFWaves) {
     constexpr int NC = kFusedMaxE / 64;
     float lv[NC];
 #pragma unroll
@@ -595,35 +611,58 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   }
   __syncthreads();
   stamp(a, 13);
-  // per-expert lists, one wave: lane p = pick (t, r) = t*K + r.  Pairs are
-  // ordered by (expert, token); active experts ascending.
+  // per-expert lists.  Pick p = t*K + r has key e_p * 64 + t; pairs are
+  // ordered by key (expert, then token), active experts ascending.  All
+  // threads count, for pick p, the keys below its own and the picks of the
+  // same expert in one eighth of the picks; wave 0 adds the eight parts,
+  // places the pairs and marks each expert's first pair.
+  {
+    const int P = B * K;
+    const int p = lane, part = wv, q0 = part * (kFusedMaxPairs / kFWaves);
+    int lt = 0, same = 0;
+    if (p < P) {
+      const int ep = L.sel[p], kp = ep * 64 + p / K;
+#pragma unroll
+      for (int i = 0; i < kFusedMaxPairs / kFWaves; ++i) {
+        const int q = q0 + i;
+        if (q < P) {
+          const int eq = L.sel[q];
+          lt += eq * 64 + q / K < kp;
+          same += eq == ep;
+        }
+      }
+    }
+    L.part_lt[part][p] = lt;
+    L.part_same[part][p] = same;
+  }
+  __syncthreads();
   if (wv == 0) {
     const int P = B * K;
-    const int e_p = lane < P ? L.sel[lane] : 0x7fff;
-    const int key = lane < P ? e_p * 64 + lane / K : 0x7fffffff;
-    int rank = 0, before = 0, same = 0;
-    for (int q = 0; q < P; ++q) {
-      const int kq = __builtin_amdgcn_readlane(key, q);
-      const int eq = kq >> 6;
-      rank += kq < key;
-      before += (eq == e_p) && kq < key;
-      same += eq == e_p;
+    int rank = 0, same = 0;
+#pragma unroll
+    for (int part = 0; part < kFWaves; ++part) {
+      rank += L.part_lt[part][lane];
+      same += L.part_same[part][lane];
     }
-    const bool first = lane < P && before == 0;
-    const unsigned long long fm = __ballot(first);
-    int slot = 0;
-    for (int q = 0; q < P; ++q)
-      if ((fm >> q) & 1ull) slot += __builtin_amdgcn_readlane(e_p, q) < e_p;
     if (lane < P) {
+      const int ep = L.sel[lane];
       L.pair_tok[rank] = lane / K;
-      L.pair_exp[rank] = e_p;
+      L.pair_exp[rank] = ep;
       L.pair_w[rank] = L.selw[lane];
       L.pos[lane] = rank;
-      if (first) {
-        L.act_exp[slot] = e_p;
-        L.act_cnt[slot] = same;
-        L.act_off[slot] = rank;
-      }
+      L.part_same[0][rank] = same;   // count of the pair's expert, by sorted position
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    const int r = lane;
+    const int er = r < P ? L.pair_exp[r] : -1;
+    const bool first = r < P && (r == 0 || L.pair_exp[r - 1] != er);
+    const unsigned long long fm = __ballot(first);
+    if (first) {
+      const int slot = __popcll(fm & ((1ull << r) - 1ull));
+      L.act_exp[slot] = er;
+      L.act_cnt[slot] = L.part_same[0][r];
+      L.act_off[slot] = r;
     }
     if (lane == 0) L.n_active = __popcll(fm);
   }
@@ -746,7 +785,7 @@ __global__ void __launch_bounds__(64) qkv_side_kernel(FusedArgs a) {
   const ActBf16Rows act{a.x, a.H, a.B - 1};
   const uint16_t *row[1] = {a.w_qkv + (size_t)j * a.H};
   float s[1][NT];
-  wave_rows_dot<1, NT, 4>(row, 0, a.H >> 3, act, s);
+  wave_rows_dot<1, NT, (NT >= 8 ? 2 : 4)>(row, 0, a.H >> 3, act, s);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     if (lane == t && t < a.B) a.qkv[(size_t)t * a.Dq + j] = s[0][t];
