@@ -370,8 +370,8 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
       a.act_exp[pa] = q;
       a.act_cnt[pa] = c;
       a.act_off[pa] = pc;
-      // gate/up work per slot: 16-token chunks on the matrix cores, else one VALU item
-      slot_nch[pa] = c >= kBatchMfmaMin ? (c + 15) >> 4 : 1;
+      // gate/up work per slot: 16-token chunks on the matrix cores, else one VALU entry
+      slot_nch[pa] = c >= kBatchMfmaMin ? (c + 15) >> 4 : 0;
       ++pa;
       pc += c;
     }
@@ -379,24 +379,36 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   const int n_act = sa[kBlock - 1];
   if (tid == kBlock - 1) *a.n_active = n_act;
   __syncthreads();
-  // gate/up work list: (slot, chunk) pairs, slots ascending
+  // gate/up work lists: matrix-core entries (slot, 16-token chunk), then VALU
+  // entries (slot, all of its fewer than 16 tokens); slots ascending in each
   {
     const int seg2 = (n_act + kBlock - 1) / kBlock;
     const int s0 = tid * seg2, s1 = min(n_act, s0 + seg2);
-    int lq = 0;
-    for (int q = s0; q < s1; ++q) lq += slot_nch[q];
-    sa[tid] = lq;
+    int lm = 0, lv = 0;
+    for (int q = s0; q < s1; ++q) {
+      lm += slot_nch[q];
+      lv += slot_nch[q] == 0;
+    }
+    sa[tid] = lm;
+    sc[tid] = lv;
     __syncthreads();
     for (int o = 1; o < kBlock; o <<= 1) {
-      const int v = tid >= o ? sa[tid - o] : 0;
+      const int vm = tid >= o ? sa[tid - o] : 0, vv = tid >= o ? sc[tid - o] : 0;
       __syncthreads();
-      sa[tid] += v;
+      sa[tid] += vm;
+      sc[tid] += vv;
       __syncthreads();
     }
-    int pq = sa[tid] - lq;
-    for (int q = s0; q < s1; ++q)
-      for (int c = 0; c < slot_nch[q]; ++c) a.gu_q[pq++] = q | (c << 16);
-    if (tid == kBlock - 1) *a.n_q = sa[kBlock - 1];
+    const int n_qm = sa[kBlock - 1], n_qv = sc[kBlock - 1];
+    int pm = sa[tid] - lm, pv = n_qm + sc[tid] - lv;
+    for (int q = s0; q < s1; ++q) {
+      for (int c = 0; c < slot_nch[q]; ++c) a.gu_q[pm++] = q | (c << 16);
+      if (slot_nch[q] == 0) a.gu_q[pv++] = q;
+    }
+    if (tid == kBlock - 1) {
+      a.n_q[0] = n_qm;
+      a.n_q[1] = n_qv;
+    }
   }
   __syncthreads();
   // a pair's place inside its expert = number of lower tokens with that expert
@@ -419,49 +431,6 @@ struct GuItem {
   int ld, cnt;              // cnt <= 16 rows on the matrix cores, < 16 on the VALU
   __device__ int tok(int m) const { return toks ? toks[m] : tok0 + m; }
 };
-
-// Up to 16 tokens on the matrix cores; the 4 waves split K.
-__device__ void gateup_mfma(const BatchArgs &a, const GuItem &it, float (*red)[2 * 256]) {
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int H = a.H, kw = wv * (H / 4) + 8 * g, nks = H / 128;
-  const uint16_t *p1 = it.w1 + (size_t)n * H + kw, *p3 = it.w3 + (size_t)n * H + kw;
-  const uint16_t *ph = a.hp + (size_t)it.tok(min(n, it.cnt - 1)) * H + kw;
-  const size_t plane = (size_t)a.B * H;
-  f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = acc1;
-  constexpr int U = 7;   // 28 loads per batch; H = 7168 gives 8 batches of 7 K-steps
-  for (int ks = 0; ks < nks; ks += U) {
-    uint4 w1v[U], w3v[U], hv[U], lv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = min(ks + u, nks - 1) * 32;
-      w1v[u] = ld_stream16(p1 + k);
-      w3v[u] = ld_stream16(p3 + k);
-      hv[u] = ld16(ph + k);
-      lv[u] = ld16(ph + plane + k);
-    }
-    DL_SCHED_FENCE();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint4 a1 = zero_unless(ks + u < nks, w1v[u]), a3 = zero_unless(ks + u < nks, w3v[u]);
-      acc1 = mfma_bf16(hv[u], a1, acc1);
-      acc3 = mfma_bf16(hv[u], a3, acc3);
-      acc1 = mfma_bf16(lv[u], a1, acc1);
-      acc3 = mfma_bf16(lv[u], a3, acc3);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    red[wv][(4 * g + i) * 16 + n] = acc1[i];
-    red[wv][256 + (4 * g + i) * 16 + n] = acc3[i];
-  }
-  __syncthreads();
-  for (int q = tid; q < it.cnt * 16; q += kBlock) {
-    const int m = q >> 4, nn = q & 15, i1 = m * 16 + nn;
-    const float u = ((red[0][i1] + red[1][i1]) + red[2][i1]) + red[3][i1];
-    const float v = ((red[0][i1 + 256] + red[1][i1 + 256]) + red[2][i1 + 256]) + red[3][i1 + 256];
-    it.out[(size_t)m * it.ld + nn] = silu_mul(u, v);
-  }
-}
 
 // Fewer than 16 tokens: wave w takes rows 4w .. 4w+3 of the item, one
 // (W1 row, W3 row) pair at a time over the full K, up to 8 tokens per pass.
@@ -495,54 +464,215 @@ __device__ void gateup_valu(const BatchArgs &a, const GuItem &it) {
   }
 }
 
-// Items: (work-list entry, 16-row tile) for the routed experts, where a
-// work-list entry is an active slot and, for an expert with 16 or more
-// tokens, one 16-token chunk of it; then (16-row tile, chunk) of the shared
-// expert.  Every matrix-core item is thus 16 rows x at most 16 tokens.
-// Block b runs on XCD b % 8; each XCD takes a contiguous range of items, so
-// the items that read the same token rows of h (or the same shared-expert
-// rows) mostly share one L2.
-__global__ void __launch_bounds__(kBlock, 3) gateup_b(BatchArgs a) {
-  __shared__ float red[kWavesPerBlock][2 * 256];
-  const int n_q = *a.n_q;
-  const int ntr = a.F / 16, nts = a.Fs / 16;
-  const bool s_mfma = a.B >= kBatchMfmaMin;
-  const int nch_s = s_mfma ? (a.B + 15) >> 4 : 1;
-  const int n_rt = n_q * ntr;
-  const int n_items = n_rt + nch_s * nts;
-  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, nloc = gridDim.x >> 3;
-  const int per = (n_items + 7) >> 3;
-  const int beg = xcd * per, end = min(beg + per, n_items);
-  for (int i = beg + loc; i < end; i += nloc) {
-    GuItem it;
-    bool mfma;
-    if (i < n_rt) {
-      const int q = a.gu_q[i / ntr], tile = i % ntr;
-      const int slot = q & 0xffff, c0 = 16 * (q >> 16);
-      const int e = a.act_exp[slot], off = a.act_off[slot] + c0, cnt = a.act_cnt[slot];
-      it.w1 = a.w1 + ((size_t)e * a.F + tile * 16) * a.H;
-      it.w3 = a.w3 + ((size_t)e * a.F + tile * 16) * a.H;
-      it.toks = a.pair_tok + off;
-      it.tok0 = 0;
-      it.out = a.act + (size_t)off * a.F + tile * 16;
-      it.ld = a.F;
-      mfma = cnt >= kBatchMfmaMin;
-      it.cnt = mfma ? min(16, cnt - c0) : cnt;
-    } else {
-      const int j = i - n_rt, tile = j / nch_s, c0 = 16 * (j % nch_s);
-      it.w1 = a.s1 + (size_t)tile * 16 * a.H;
-      it.w3 = a.s3 + (size_t)tile * 16 * a.H;
-      it.toks = nullptr;
-      it.tok0 = c0;
-      it.out = a.act_s + (size_t)c0 * a.Fs + tile * 16;
-      it.ld = a.Fs;
-      mfma = s_mfma;
-      it.cnt = mfma ? min(16, a.B - c0) : a.B;
+// A matrix-core item: one 16-token chunk x a group of 16 NTL rows of W1 and
+// of W3 (NTL <= 4), over one of kBatchGuSplit K ranges.  The chunk's
+// activations (bf16 hi and lo planes of h) for that K range are staged in
+// LDS once, with contiguous loads; wave w < NTL streams the 16 rows of tile w
+// of W1 and of W3 over the whole range, 7 K steps (448 bytes of each row)
+// per load batch, taking its activation fragments from LDS.  The partial
+// sums go to `part`; the split that arrives last adds the kBatchGuSplit
+// partials in split order and writes the SwiGLU output.
+struct GuGroup {
+  const uint16_t *w1, *w3;  // first row of the group, row stride H
+  const int *toks;          // the chunk's tokens (nullptr: tok0 + m)
+  int tok0, cnt;            // cnt <= 16 tokens
+  float *out;               // output row m at out + m * ld, columns [0, 16 NTL)
+  int ld;
+  __device__ int tok(int m) const { return toks ? toks[m] : tok0 + m; }
+};
+
+constexpr int kGuPart = 2 * kBatchGuRows * 16;  // floats per partial: [W1 | W3][tile][token][row]
+constexpr int kGuPad = 8;                       // bf16 elements of padding per LDS row
+
+// LDS rows of the staged chunk: 16 tokens x (klen + kGuPad) bf16, hi plane then lo plane.
+__device__ __forceinline__ void gateup_stage(const BatchArgs &a, const GuGroup &gg, int kbeg, int klen, uint16_t *lds) {
+  const int tid = threadIdx.x;
+  const int ld = klen + kGuPad, wpr = klen / 8;  // 16-byte words per row
+  const int nw = 2 * 16 * wpr;
+  const size_t plane = (size_t)a.B * a.H;
+  for (int w0 = 0; w0 < nw; w0 += 8 * kBlock) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = min(w0 + tid + kBlock * j, nw - 1);
+      const int pl = w / (16 * wpr), m = (w / wpr) % 16, c = w % wpr;
+      v[j] = ld16(a.hp + pl * plane + (size_t)gg.tok(min(m, gg.cnt - 1)) * a.H + kbeg + 8 * c);
     }
-    if (mfma) gateup_mfma(a, it, red);
-    else gateup_valu(a, it);
-    __syncthreads();  // red is reused by the next item
+    DL_SCHED_FENCE();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = w0 + tid + kBlock * j;
+      if (w < nw) {
+        const int pl = w / (16 * wpr), m = (w / wpr) % 16, c = w % wpr;
+        *reinterpret_cast<uint4 *>(lds + (size_t)(pl * 16 + m) * ld + 8 * c) = v[j];
+      }
+    }
   }
+}
+
+template <int NTL>
+__device__ void gateup_group(const BatchArgs &a, const GuGroup &gg, int split, float *part, unsigned *cnt,
+                             uint16_t *lds, int *flag) {
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int H = a.H, klen = H / kBatchGuSplit, kbeg = split * klen, ld = klen + kGuPad;
+  gateup_stage(a, gg, kbeg, klen, lds);
+  __syncthreads();
+  if (wv < NTL) {
+    const uint16_t *p1 = gg.w1 + (size_t)(16 * wv + n) * H + kbeg + 8 * g;
+    const uint16_t *p3 = gg.w3 + (size_t)(16 * wv + n) * H + kbeg + 8 * g;
+    const uint16_t *lh = lds + (size_t)n * ld + 8 * g, *ll = lh + (size_t)16 * ld;
+    const int nks = klen / 32;
+    f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = acc1;
+    constexpr int U = 7;
+    for (int ks = 0; ks < nks; ks += U) {
+      uint4 w1v[U], w3v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = min(ks + u, nks - 1) * 32;
+        w1v[u] = ld_stream16(p1 + k);
+        w3v[u] = ld_stream16(p3 + k);
+      }
+      DL_SCHED_FENCE();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = min(ks + u, nks - 1) * 32;
+        const uint4 hv = *reinterpret_cast<const uint4 *>(lh + k), lv = *reinterpret_cast<const uint4 *>(ll + k);
+        const bool on = ks + u < nks;
+        const uint4 b1 = zero_unless(on, w1v[u]), b3 = zero_unless(on, w3v[u]);
+        acc1 = mfma_bf16(hv, b1, acc1);
+        acc3 = mfma_bf16(hv, b3, acc3);
+        acc1 = mfma_bf16(lv, b1, acc1);
+        acc3 = mfma_bf16(lv, b3, acc3);
+      }
+    }
+    // [W1 | W3][tile][token 4g + i][row n], written through to the device
+    // coherence point (agent-scope stores), so no cache maintenance is needed
+    float *mine = part + (size_t)split * kGuPart;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __hip_atomic_store(mine + ((0 * NTL + wv) * 16 + 4 * g + i) * 16 + n, acc1[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + ((1 * NTL + wv) * 16 + 4 * g + i) * 16 + n, acc3[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // arrival: this workgroup's stores have completed before it is counted; the
+  // last of the kBatchGuSplit splits re-arms the counter and reads the
+  // partials with agent-scope loads
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = prev == kBatchGuSplit - 1;
+    if (*flag) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!*flag) return;
+  const int rows = 16 * NTL;
+  for (int q = tid; q < gg.cnt * rows; q += kBlock) {
+    const int m = q / rows, r = q % rows, t = r >> 4, nn = r & 15;
+    const int i1 = ((0 * NTL + t) * 16 + m) * 16 + nn, i3 = ((1 * NTL + t) * 16 + m) * 16 + nn;
+    float pu[kBatchGuSplit], pv[kBatchGuSplit];
+#pragma unroll
+    for (int sp = 0; sp < kBatchGuSplit; ++sp) {
+      pu[sp] = __hip_atomic_load(part + (size_t)sp * kGuPart + i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pv[sp] = __hip_atomic_load(part + (size_t)sp * kGuPart + i3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float u = 0.f, v = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kBatchGuSplit; ++sp) {
+      u += pu[sp];
+      v += pv[sp];
+    }
+    gg.out[(size_t)m * gg.ld + r] = silu_mul(u, v);
+  }
+}
+
+template <class Fn>
+__device__ __forceinline__ void by_tiles(int rows, Fn fn) {
+  if (rows >= 64) fn(std::integral_constant<int, 4>{});
+  else fn(std::integral_constant<int, 2>{});
+}
+
+// One workgroup per item, in this order:
+//  1 matrix-core items of the routed experts: (entry, row group, K split),
+//    entry = a 16-token chunk of an expert with 16 or more tokens;
+//  2 matrix-core items of the shared expert when it has 16 or more tokens;
+//  3 VALU items (entry, 16-row tile) of experts with fewer than 16 tokens;
+//  4 VALU items of the shared expert below 16 tokens.
+// Workgroups past the last item return at once.
+__global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
+  extern __shared__ __align__(16) uint16_t gu_lds[];  // staged activation chunk
+  __shared__ int flag;
+  const int n_qm = a.n_q[0], n_qv = a.n_q[1];
+  const int B = a.B, F = a.F, Fs = a.Fs;
+  const bool s_mfma = Fs > 0 && B >= kBatchMfmaMin;
+  const int nch_s = s_mfma ? (B + 15) >> 4 : 0;
+  const int rg_r = min(kBatchGuRows, F), ngr = F / rg_r;
+  const int rg_s = Fs > 0 ? min(kBatchGuRows, Fs) : 16, ngs = Fs / rg_s;
+  const int n_mr = n_qm * ngr * kBatchGuSplit, n_ms = nch_s * ngs * kBatchGuSplit;
+  const int n_vr = n_qv * (F / 16), n_vs = (Fs > 0 && !s_mfma) ? Fs / 16 : 0;
+  int i = blockIdx.x;
+  if (i < n_mr + n_ms) {
+    GuGroup gg;
+    int split, grp, rows;
+    if (i < n_mr) {
+      const int e = i / (ngr * kBatchGuSplit), rem = i % (ngr * kBatchGuSplit), gi = rem / kBatchGuSplit;
+      split = rem % kBatchGuSplit;
+      const int q = a.gu_q[e], slot = q & 0xffff, c0 = 16 * (q >> 16);
+      const int ex = a.act_exp[slot], off = a.act_off[slot] + c0;
+      rows = rg_r;
+      gg.w1 = a.w1 + ((size_t)ex * F + gi * rg_r) * a.H;
+      gg.w3 = a.w3 + ((size_t)ex * F + gi * rg_r) * a.H;
+      gg.toks = a.pair_tok + off;
+      gg.tok0 = 0;
+      gg.cnt = min(16, a.act_cnt[slot] - c0);
+      gg.out = a.act + (size_t)off * F + gi * rg_r;
+      gg.ld = F;
+      grp = e * 4 + gi;
+    } else {
+      i -= n_mr;
+      const int c = i / (ngs * kBatchGuSplit), rem = i % (ngs * kBatchGuSplit), gi = rem / kBatchGuSplit;
+      split = rem % kBatchGuSplit;
+      rows = rg_s;
+      gg.w1 = a.s1 + (size_t)gi * rg_s * a.H;
+      gg.w3 = a.s3 + (size_t)gi * rg_s * a.H;
+      gg.toks = nullptr;
+      gg.tok0 = 16 * c;
+      gg.cnt = min(16, B - 16 * c);
+      gg.out = a.act_s + (size_t)(16 * c) * Fs + gi * rg_s;
+      gg.ld = Fs;
+      grp = (n_qm + c) * 4 + gi;
+    }
+    float *part = a.gu_part + (size_t)grp * kBatchGuSplit * kGuPart;
+    by_tiles(rows, [&](auto ntl) { gateup_group<decltype(ntl)::value>(a, gg, split, part, a.gu_cnt + grp, gu_lds, &flag); });
+    return;
+  }
+  i -= n_mr + n_ms;
+  GuItem it;
+  if (i < n_vr) {
+    const int slot = a.gu_q[n_qm + i / (F / 16)], tile = i % (F / 16);
+    const int ex = a.act_exp[slot], off = a.act_off[slot];
+    it.w1 = a.w1 + ((size_t)ex * F + tile * 16) * a.H;
+    it.w3 = a.w3 + ((size_t)ex * F + tile * 16) * a.H;
+    it.toks = a.pair_tok + off;
+    it.tok0 = 0;
+    it.out = a.act + (size_t)off * F + tile * 16;
+    it.ld = F;
+    it.cnt = a.act_cnt[slot];
+  } else if (i - n_vr < n_vs) {
+    const int tile = i - n_vr;
+    it.w1 = a.s1 + (size_t)tile * 16 * a.H;
+    it.w3 = a.s3 + (size_t)tile * 16 * a.H;
+    it.toks = nullptr;
+    it.tok0 = 0;
+    it.out = a.act_s + tile * 16;
+    it.ld = Fs;
+    it.cnt = B;
+  } else {
+    return;
+  }
+  gateup_valu(a, it);
 }
 
 // ================================================================ launch 5
@@ -752,9 +882,14 @@ hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]
   const int n_wo = a.H / 16;
   const int n_q = (a.Dq + 15) / 16 * kBatchQkvSplit;
   const int n_rk = a.H / kBatchRtrK;
-  const int max_q = min(a.E, a.B * a.K) * ((a.B + 15) / 16);
-  const int max_items = max_q * (a.F / 16) + ((a.B + 15) / 16) * (a.Fs / 16);
-  const int g4 = min(kBatchGateupGrid, (max_items + 7) & ~7);
+  // upper bound of gate/up items (workgroups past the actual count return)
+  const int P = a.B * a.K;
+  const int max_qm = (P + 7) / 8, max_qv = min(a.E, P);
+  const int rg_r = min(kBatchGuRows, a.F), rg_s = a.Fs > 0 ? min(kBatchGuRows, a.Fs) : 16;
+  const int nch_s = (a.B + 15) / 16;
+  const long g4l = (long)max_qm * (a.F / rg_r) * kBatchGuSplit + (long)nch_s * (a.Fs / rg_s) * kBatchGuSplit +
+                   (long)max_qv * (a.F / 16) + a.Fs / 16;
+  const int g4 = (int)g4l;
   hipError_t e;
   auto rec = [&](int i, int j) { return ev ? hipEventRecord(ev[i][j], s) : hipSuccess; };
 #define DL_TRY(x) do { if ((e = (x)) != hipSuccess) return e; } while (0)
@@ -771,7 +906,11 @@ hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]
   DL_TRY(hipGetLastError());
   DL_TRY(rec(2, 1));
   DL_TRY(rec(3, 0));
-  hipLaunchKernelGGL(gateup_b, dim3(g4), dim3(kBlock), 0, s, a);
+  const size_t gu_lds = (size_t)2 * 16 * (a.H / kBatchGuSplit + kGuPad) * 2;
+  if (gu_lds > 65536)
+    DL_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(gateup_b), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)gu_lds));
+  hipLaunchKernelGGL(gateup_b, dim3(g4), dim3(kBlock), gu_lds, s, a);
   DL_TRY(hipGetLastError());
   DL_TRY(rec(3, 1));
   DL_TRY(rec(4, 0));

@@ -86,36 +86,48 @@ __device__ __forceinline__ void put_tagged(uint64_t *p, float v, unsigned tag) {
 __device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Completes a poll started with ld_tagged(p) -> x: re-reads until the tag
-// matches or the spin budget is spent (then *bad is set).
-__device__ __forceinline__ float finish_tagged(const uint64_t *p, uint64_t x, unsigned tag, int limit,
-                                               int *bad) {
-  int n = 0;
-  while ((unsigned)(x >> 32) != tag) {
-    if (++n > limit) {
+// Waits for N tagged values whose first reads x[i] (of p[i]) are already in
+// flight: every round re-reads all values whose tag is not yet this step's,
+// together, so a thread waiting on N late values pays one round trip per
+// round, not one per value.  On expiry of the spin budget *bad is set.
+template <int N>
+__device__ __forceinline__ void finish_tagged_n(const uint64_t *const (&p)[N], uint64_t (&x)[N], const bool (&use)[N],
+                                                unsigned tag, int limit, int *bad) {
+  for (int n = 0;; ++n) {
+    bool done = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) done &= !use[i] || (unsigned)(x[i] >> 32) == tag;
+    if (done) return;
+    if (n >= limit) {
       *bad = 1;
-      break;
+      return;
     }
     __builtin_amdgcn_s_sleep(1);
-    x = ld_tagged(p);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (use[i] && (unsigned)(x[i] >> 32) != tag) x[i] = ld_tagged(p[i]);
   }
-  return __uint_as_float((unsigned)x);
 }
 // Polls n tagged values src[i], i = first, first + stride, ... into dst[i],
 // eight requests in flight per thread.
 __device__ __forceinline__ void gather_tagged(const uint64_t *src, float *dst, int first, int stride, int n,
                                               unsigned tag, int limit, int *bad) {
   for (int i0 = first; i0 < n; i0 += 8 * stride) {
+    const uint64_t *p[8];
     uint64_t x[8];
+    bool use[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int i = i0 + r * stride;
-      if (i < n) x[r] = ld_tagged(src + i);
+      use[r] = i < n;
+      p[r] = src + (use[r] ? i : first);
+      x[r] = ld_tagged(p[r]);
     }
+    finish_tagged_n<8>(p, x, use, tag, limit, bad);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int i = i0 + r * stride;
-      if (i < n) dst[i] = finish_tagged(src + i, x[r], tag, limit, bad);
+      if (i < n) dst[i] = __uint_as_float((unsigned)x[r]);
     }
   }
 }
@@ -471,15 +483,20 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       }
   } else {
     // control threads: every workgroup's partial sums (thread q: workgroup q)
+    const uint64_t *pp[kFusedMaxB];
     uint64_t x[kFusedMaxB];
+    bool use[kFusedMaxB];
 #pragma unroll
-    for (int t = 0; t < kFusedMaxB; ++t)
-      if (tid < G && t < B) x[t] = ld_tagged(a.pss + (size_t)tid * B + t);
+    for (int t = 0; t < kFusedMaxB; ++t) {
+      use[t] = tid < G && t < B;
+      pp[t] = a.pss + (use[t] ? (size_t)tid * B + t : 0);
+      x[t] = use[t] ? ld_tagged(pp[t]) : 0ull;
+    }
+    finish_tagged_n<kFusedMaxB>(pp, x, use, tag, a.spin_limit, &L.bad);
 #pragma unroll
     for (int t = 0; t < kFusedMaxB; ++t) {
       if (t < B) {
-        float v = tid < G ? finish_tagged(a.pss + (size_t)tid * B + t, x[t], tag, a.spin_limit, &L.bad) : 0.f;
-        v = wave_sum(v);
+        const float v = wave_sum(use[t] ? __uint_as_float((unsigned)x[t]) : 0.f);
         if (lane == 0) L.red[wv * kFusedMaxB + t] = v;
       }
     }

@@ -70,7 +70,8 @@ constexpr int kBatchQkvSplit = 4;     // K splits of the attention input project
 constexpr int kBatchRtrExperts = 32;  // router experts per workgroup
 constexpr int kBatchRtrK = 256;       // router K per workgroup
 constexpr int kBatchMfmaMin = 16;     // an expert with at least this many tokens uses MFMA
-constexpr int kBatchGateupGrid = 1024;
+constexpr int kBatchGuRows = 64;      // gate/up rows of W1 (and of W3) per matrix-core item
+constexpr int kBatchGuSplit = 8;      // K splits of a matrix-core gate/up item (combined by the last)
 constexpr int kBatchLaunches = 5;
 
 struct BatchArgs {
@@ -98,8 +99,11 @@ struct BatchArgs {
   int *act_exp, *act_cnt, *act_off;  // [E] per active slot
   int *pair_tok;      // [B*k]
   float *pair_w;      // [B*k]
-  int *gu_q;          // [4 E] gate/up work list: slot | (16-token chunk << 16)
-  int *n_q;           // [1]   its length
+  int *gu_q;          // [4 E] gate/up work lists: matrix-core entries slot | (16-token chunk << 16),
+                      //       then VALU entries (slot)
+  int *n_q;           // [2]   their lengths
+  float *gu_part;     // [entries][groups][kBatchGuSplit][2 * kBatchGuRows][16] partial gate/up sums
+  unsigned *gu_cnt;   // [entries][groups] arrivals of a matrix-core item's K splits
   unsigned *counter;  // [1] arrivals of the top-k workgroups (re-armed by the last)
   int B, H, Dq, Do, E, K, F, Fs;
   float eps;

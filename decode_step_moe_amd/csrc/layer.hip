@@ -85,13 +85,20 @@ struct Scratch {
   float *rlog_part = nullptr;    // [H/kBatchRtrK][maxB][E]
   float *hn = nullptr;           // [maxB][H]
   uint16_t *hp = nullptr;        // [2][maxB][H]
-  int *gu_q = nullptr;           // [4 E] gate/up work list
-  int *n_q = nullptr;            // [1]
+  int *gu_q = nullptr;           // [4 E] gate/up work lists
+  int *n_q = nullptr;            // [2]
+  float *gu_part = nullptr;      // [entries][4][kBatchGuSplit][2 * kBatchGuRows * 16]
+  unsigned *gu_cnt = nullptr;    // [entries][4]
 };
+
+// Capacity of the batched gate/up matrix-core entries: 16-token chunks of
+// experts with >= 16 tokens (at most B*k/8 of them) plus the shared expert's
+// chunks (at most 4).
+size_t gu_entries(const decode_layer_config &c) { return ((size_t)c.max_batch * c.top_k + 7) / 8 + 4; }
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-constexpr int kNumBuf = 25;
+constexpr int kNumBuf = 27;
 struct Layout {
   size_t off[kNumBuf];
   size_t total;
@@ -112,7 +119,9 @@ Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
       4, 4,
       // batched arrays
       (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2,
-      Bb ? 4 * E * 4 : size_t(0), Bb ? size_t(4) : size_t(0)};
+      Bb ? 4 * E * 4 : size_t(0), Bb ? size_t(8) : size_t(0),
+      Bb ? gu_entries(c) * 4 * kBatchGuSplit * (2 * kBatchGuRows * 16) * 4 : size_t(0),
+      Bb ? gu_entries(c) * 4 * 4 : size_t(0)};
   Layout L;
   size_t o = 0;
   for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
@@ -329,6 +338,8 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
   h->s.hp = (uint16_t *)(b + L.off[22]);
   h->s.gu_q = (int *)(b + L.off[23]);
   h->s.n_q = (int *)(b + L.off[24]);
+  h->s.gu_part = (float *)(b + L.off[25]);
+  h->s.gu_cnt = (unsigned *)(b + L.off[26]);
   // The hand-off counters start at zero and are re-armed by the kernels
   // themselves, and the tagged hand-off values start with tag 0, which no
   // step uses (tags are the step counter + 1), so no step ever needs a memset.
@@ -458,6 +469,8 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
     ba.pair_w = h->s.pair_w;
     ba.gu_q = h->s.gu_q;
     ba.n_q = h->s.n_q;
+    ba.gu_part = h->s.gu_part;
+    ba.gu_cnt = h->s.gu_cnt;
     ba.counter = h->s.counters + 2;
     ba.B = B;
     ba.H = c.hidden;

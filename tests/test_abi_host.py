@@ -93,8 +93,10 @@ def test_batched_scratch_follows_the_path():
     as bf16 hi + lo planes) exist exactly when some step can take that path."""
     c = good()                       # TP16 shard shapes, max_batch 64
     B, H, Dq, E = 64, 7168, 512, 384
+    entries = (B * 8 + 7) // 8 + 4     # gate/up matrix-core entries: B*k/8 chunks + 4 shared
     batched = (_a256(4 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
-               + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(4))
+               + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(8)
+               + _a256(entries * 4 * 8 * 2048 * 4) + _a256(entries * 4 * 4))
     auto = dl.scratch_bytes(c, 256)
     c.path = dl.DL_PATH_MULTI
     multi = dl.scratch_bytes(c, 256)
