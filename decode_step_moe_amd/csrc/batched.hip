@@ -327,12 +327,12 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
     wave_topk<NCAND>(lv, E, K, my_idx, my_l);
     const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
     const float ssum = wave_sum(s);
-    if (lane < K) {
-      a.topk_idx[(size_t)t * K + lane] = my_idx;
-      a.topk_w[(size_t)t * K + lane] = s / ssum;
+    if (lane < K) {  // written through: the last workgroup reads them back
+      __hip_atomic_store(a.topk_idx + (size_t)t * K + lane, my_idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.topk_w + (size_t)t * K + lane, s / ssum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (!arrive_last(a.counter, B, &last_flag)) return;
+  if (!arrive_last_wt(a.counter, B, &last_flag)) return;
 
   // ---- the last workgroup: per-expert token lists ----
   for (int q = tid; q < E; q += kBlock) {
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __syncthreads();
   const int P = B * K;
   for (int i = tid; i < P; i += kBlock) {
-    const int e = a.topk_idx[i], tt = i / K;
+    const int e = __hip_atomic_load(a.topk_idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), tt = i / K;
     atomicAdd(&cnt[e], 1);
     atomicOr(&msk[e][tt >> 5], 1u << (tt & 31));
   }
@@ -413,12 +413,12 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __syncthreads();
   // a pair's place inside its expert = number of lower tokens with that expert
   for (int i = tid; i < P; i += kBlock) {
-    const int e = a.topk_idx[i], tt = i / K;
+    const int e = __hip_atomic_load(a.topk_idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), tt = i / K;
     const unsigned m0 = msk[e][0], m1 = msk[e][1];
     const int r = tt < 32 ? __popc(m0 & ((1u << tt) - 1u)) : __popc(m0) + __popc(m1 & ((1u << (tt - 32)) - 1u));
     const int pos = off[e] + r;
     a.pair_tok[pos] = tt;
-    a.pair_w[pos] = a.topk_w[i];
+    a.pair_w[pos] = __hip_atomic_load(a.topk_w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

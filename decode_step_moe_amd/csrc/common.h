@@ -359,4 +359,22 @@ __device__ __forceinline__ bool arrive_last(unsigned *counter, unsigned nblocks,
   return last;
 }
 
+// The same hand-off without cache-wide fences: the caller has written the
+// values it hands over with agent-scope atomic stores (written through to
+// the device's coherence point), and the last workgroup reads them back with
+// agent-scope atomic loads.  Each thread's stores have completed before the
+// workgroup is counted.  An agent-scope fence would instead write back and
+// invalidate the whole L2 of the XCD, once per workgroup.
+__device__ __forceinline__ bool arrive_last_wt(unsigned *counter, unsigned nblocks, int *lds_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = prev == nblocks - 1;
+    if (*lds_flag) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *lds_flag != 0;
+}
+
 }  // namespace dl
