@@ -27,8 +27,11 @@
 //              s / sum s with s = sigmoid(l).  The last workgroup to finish
 //              builds the per-expert token lists (active experts ascending,
 //              tokens ascending inside an expert).
-//  4 gateup_b  items (active expert or shared expert, 16 ffn rows):
-//              a[p, f] = silu(W1[e, f] . h[t_p]) * (W3[e, f] . h[t_p]).
+//  4 gateup_b  a[p, f] = silu(W1[e, f] . h[t_p]) * (W3[e, f] . h[t_p]):
+//              matrix-core units (64 rows of W1 and W3 x a 16-token chunk
+//              x a K chunk) cut into one contiguous run per workgroup, two
+//              workgroups per CU, K chunks combined by the last to arrive;
+//              then the VALU items of experts with fewer than 16 tokens.
 //  5 down_b    16 rows of y per workgroup over every active expert and the
 //              shared expert, summed in a fixed order in LDS:
 //              y[t, i] = S2[i] . a_s[t] + sum_p w_p W2[e_p, i] . a[p].
@@ -38,6 +41,11 @@
 // to bf16 (x - hi is exact) and lo = bf16(x - hi), and both halves are
 // multiplied into the same accumulator, which keeps about 16 significant
 // bits of x (relative error below 2^-16) against the weights' exact bf16.
+//
+// Weight loads.  A matrix-core operand fragment is 16 rows x 64 bytes per
+// load instruction (the next 64 bytes of each row follow in the next K
+// step), and these kernels read weights with ordinary cached loads: on this
+// pattern they stream measurably faster than non-temporal loads.
 //
 // Every output element is produced by one thread, in an order that depends
 // only on the shapes, so results are bit-identical from run to run.
@@ -98,7 +106,7 @@ __device__ __forceinline__ void mfma_rows(const uint16_t *wp, const uint16_t *co
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = min(ks + u, nks - 1) * 32;
-      wv[u] = ld_stream16(wp + k);
+      wv[u] = ld16(wp + k);
 #pragma unroll
       for (int c = 0; c < NC; ++c) av[u][c] = ld16(ap[c] + k);
     }
@@ -209,8 +217,8 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
     float4 b0[4], b1[4], av[4][NC];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      b0[it] = ld_stream16f(w0 + 16 * it);
-      b1[it] = ld_stream16f(w1 + 16 * it);
+      b0[it] = ld16f(w0 + 16 * it);
+      b1[it] = ld16f(w1 + 16 * it);
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -464,215 +472,292 @@ __device__ void gateup_valu(const BatchArgs &a, const GuItem &it) {
   }
 }
 
-// A matrix-core item: one 16-token chunk x a group of 16 NTL rows of W1 and
-// of W3 (NTL <= 4), over one of kBatchGuSplit K ranges.  The chunk's
-// activations (bf16 hi and lo planes of h) for that K range are staged in
-// LDS once, with contiguous loads; wave w < NTL streams the 16 rows of tile w
-// of W1 and of W3 over the whole range, 7 K steps (448 bytes of each row)
-// per load batch, taking its activation fragments from LDS.  The partial
-// sums go to `part`; the split that arrives last adds the kBatchGuSplit
-// partials in split order and writes the SwiGLU output.
-struct GuGroup {
-  const uint16_t *w1, *w3;  // first row of the group, row stride H
-  const int *toks;          // the chunk's tokens (nullptr: tok0 + m)
-  int tok0, cnt;            // cnt <= 16 tokens
+// Matrix-core units.  A group is 16 NTL rows (NTL <= 4) of W1 and the same
+// rows of W3 applied to one 16-token chunk: a chunk of a routed expert with
+// 16 or more tokens, or of the shared expert when B >= 16.  A unit is one
+// group over kGuKc K steps of 32 (448 K elements at H = 7168; a group has
+// ceil(H / (32 kGuKc)) units, its K chunks).  The workgroup stages the
+// chunk's activations for the unit's K range (bf16 hi and lo planes of h)
+// in LDS with contiguous loads; wave w < NTL then streams the 16 rows of
+// tile w of W1 and of W3, 7 K steps (448 bytes of each row) per load batch,
+// taking its activation fragments from LDS.  The sums go to the group's
+// slot for that K chunk, written through to the device coherence point; the
+// last unit of the group to arrive adds the slots in K-chunk order (so the
+// result does not depend on arrival order) and writes silu(u) * v.
+// VALU units.  (expert, 16-row tile) of experts with fewer than 16 tokens,
+// and of the shared expert below 16 tokens, after the matrix-core units.
+constexpr int kGuPad = 8;                  // bf16 elements of padding per LDS row
+constexpr int kGuLd = 32 * kGuKc + kGuPad; // LDS row of one staged token
+constexpr int kGuLds = 2 * 16 * kGuLd * 2; // bytes: [hi | lo][16 tokens][kGuLd]
+constexpr unsigned kGuSc1 = 16;            // cache policy: coherent at agent scope
+
+struct GuUnit {
+  const uint16_t *w1, *w3;  // row 0 of the group, row stride H
   float *out;               // output row m at out + m * ld, columns [0, 16 NTL)
-  int ld;
-  __device__ int tok(int m) const { return toks ? toks[m] : tok0 + m; }
+  float *slots;             // the group's slots, kGuSlotFloatsR floats each
+  unsigned *arrivals;       // the group's arrival counter
+  int ld, cnt, k0, k1, kc, nck, ntl, group;
 };
 
-constexpr int kGuPart = 2 * kBatchGuRows * 16;  // floats per partial: [W1 | W3][tile][token][row]
-constexpr int kGuPad = 8;                       // bf16 elements of padding per LDS row
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gu_rsrc(const float *p, int floats) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, floats * 4, 0x00020000);
+}
 
-// LDS rows of the staged chunk: 16 tokens x (klen + kGuPad) bf16, hi plane then lo plane.
-__device__ __forceinline__ void gateup_stage(const BatchArgs &a, const GuGroup &gg, int kbeg, int klen, uint16_t *lds) {
-  const int tid = threadIdx.x;
-  const int ld = klen + kGuPad, wpr = klen / 8;  // 16-byte words per row
-  const int nw = 2 * 16 * wpr;
-  const size_t plane = (size_t)a.B * a.H;
-  for (int w0 = 0; w0 < nw; w0 += 8 * kBlock) {
-    uint4 v[8];
+// One matrix-core unit: sums over its K chunk into its slot, as
+// [W1 | W3][tile][row][token] (a lane's 4 tokens are contiguous).
+template <int NTL>
+__device__ void gu_unit(const BatchArgs &a, const GuUnit &s, const uint16_t *lds) {
+  constexpr int U = 7;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  if (wv >= NTL) return;
+  const int H = a.H, kb = 32 * s.k0, nks = s.k1 - s.k0;
+  const uint16_t *p1 = s.w1 + (size_t)(16 * wv + n) * H + kb + 8 * g;
+  const uint16_t *p3 = s.w3 + (size_t)(16 * wv + n) * H + kb + 8 * g;
+  const uint16_t *lh = lds + n * kGuLd + 8 * g, *ll = lh + 16 * kGuLd;
+  f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = acc1;
+  for (int ks = 0; ks < nks; ks += U) {
+    uint4 w1v[U], w3v[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = min(w0 + tid + kBlock * j, nw - 1);
-      const int pl = w / (16 * wpr), m = (w / wpr) % 16, c = w % wpr;
-      v[j] = ld16(a.hp + pl * plane + (size_t)gg.tok(min(m, gg.cnt - 1)) * a.H + kbeg + 8 * c);
+    for (int u = 0; u < U; ++u) {
+      const int k = min(ks + u, nks - 1) * 32;
+      w1v[u] = ld16(p1 + k);
+      w3v[u] = ld16(p3 + k);
     }
     DL_SCHED_FENCE();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = w0 + tid + kBlock * j;
-      if (w < nw) {
-        const int pl = w / (16 * wpr), m = (w / wpr) % 16, c = w % wpr;
-        *reinterpret_cast<uint4 *>(lds + (size_t)(pl * 16 + m) * ld + 8 * c) = v[j];
-      }
+    for (int u = 0; u < U; ++u) {
+      const int k = min(ks + u, nks - 1) * 32;
+      const bool on = ks + u < nks;
+      const uint4 b1 = zero_unless(on, w1v[u]), b3 = zero_unless(on, w3v[u]);
+      const uint4 hv = *reinterpret_cast<const uint4 *>(lh + k), lv = *reinterpret_cast<const uint4 *>(ll + k);
+      acc1 = mfma_bf16(hv, b1, acc1);
+      acc3 = mfma_bf16(hv, b3, acc3);
+      acc1 = mfma_bf16(lv, b1, acc1);
+      acc3 = mfma_bf16(lv, b3, acc3);
     }
   }
+  const __amdgpu_buffer_rsrc_t r = gu_rsrc(s.slots, s.nck * kGuSlotFloatsR);
+  const int base = s.kc * kGuSlotFloatsR + (wv * 16 + n) * 16 + 4 * g;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc1), r, base * 4, 0, kGuSc1);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc3), r, (base + NTL * 256) * 4, 0, kGuSc1);
 }
 
+// The group's last unit: u and v summed over the K-chunk slots in order.
 template <int NTL>
-__device__ void gateup_group(const BatchArgs &a, const GuGroup &gg, int split, float *part, unsigned *cnt,
-                             uint16_t *lds, int *flag) {
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int H = a.H, klen = H / kBatchGuSplit, kbeg = split * klen, ld = klen + kGuPad;
-  gateup_stage(a, gg, kbeg, klen, lds);
-  __syncthreads();
-  if (wv < NTL) {
-    const uint16_t *p1 = gg.w1 + (size_t)(16 * wv + n) * H + kbeg + 8 * g;
-    const uint16_t *p3 = gg.w3 + (size_t)(16 * wv + n) * H + kbeg + 8 * g;
-    const uint16_t *lh = lds + (size_t)n * ld + 8 * g, *ll = lh + (size_t)16 * ld;
-    const int nks = klen / 32;
-    f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = acc1;
-    constexpr int U = 7;
-    for (int ks = 0; ks < nks; ks += U) {
-      uint4 w1v[U], w3v[U];
+__device__ void gu_combine(const GuUnit &s) {
+  constexpr int ROWS = 16 * NTL;
+  const int q = threadIdx.x;
+  if (q >= ROWS * 4) return;
+  const int r = q % ROWS, mq = q / ROWS, t = r >> 4, nn = r & 15;
+  const __amdgpu_buffer_rsrc_t rs = gu_rsrc(s.slots, s.nck * kGuSlotFloatsR);
+  const int i1 = ((0 * NTL + t) * 16 + nn) * 16 + 4 * mq, i3 = ((NTL + t) * 16 + nn) * 16 + 4 * mq;
+  f32x4 u = {0.f, 0.f, 0.f, 0.f}, v = u;
+  for (int s0 = 0; s0 < s.nck; s0 += 8) {
+    f32x4 pu[8], pv[8];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = min(ks + u, nks - 1) * 32;
-        w1v[u] = ld_stream16(p1 + k);
-        w3v[u] = ld_stream16(p3 + k);
+    for (int j = 0; j < 8; ++j) {
+      const int o = min(s0 + j, s.nck - 1) * kGuSlotFloatsR;
+      pu[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (o + i1) * 4, 0, kGuSc1));
+      pv[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (o + i3) * 4, 0, kGuSc1));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < s.nck) {
+        u += pu[j];
+        v += pv[j];
       }
-      DL_SCHED_FENCE();
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = min(ks + u, nks - 1) * 32;
-        const uint4 hv = *reinterpret_cast<const uint4 *>(lh + k), lv = *reinterpret_cast<const uint4 *>(ll + k);
-        const bool on = ks + u < nks;
-        const uint4 b1 = zero_unless(on, w1v[u]), b3 = zero_unless(on, w3v[u]);
-        acc1 = mfma_bf16(hv, b1, acc1);
-        acc3 = mfma_bf16(hv, b3, acc3);
-        acc1 = mfma_bf16(lv, b1, acc1);
-        acc3 = mfma_bf16(lv, b3, acc3);
-      }
-    }
-    // [W1 | W3][tile][token 4g + i][row n], written through to the device
-    // coherence point (agent-scope stores), so no cache maintenance is needed
-    float *mine = part + (size_t)split * kGuPart;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __hip_atomic_store(mine + ((0 * NTL + wv) * 16 + 4 * g + i) * 16 + n, acc1[i], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(mine + ((1 * NTL + wv) * 16 + 4 * g + i) * 16 + n, acc3[i], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
-  // arrival: this workgroup's stores have completed before it is counted; the
-  // last of the kBatchGuSplit splits re-arms the counter and reads the
-  // partials with agent-scope loads
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = prev == kBatchGuSplit - 1;
-    if (*flag) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!*flag) return;
-  const int rows = 16 * NTL;
-  for (int q = tid; q < gg.cnt * rows; q += kBlock) {
-    const int m = q / rows, r = q % rows, t = r >> 4, nn = r & 15;
-    const int i1 = ((0 * NTL + t) * 16 + m) * 16 + nn, i3 = ((1 * NTL + t) * 16 + m) * 16 + nn;
-    float pu[kBatchGuSplit], pv[kBatchGuSplit];
 #pragma unroll
-    for (int sp = 0; sp < kBatchGuSplit; ++sp) {
-      pu[sp] = __hip_atomic_load(part + (size_t)sp * kGuPart + i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      pv[sp] = __hip_atomic_load(part + (size_t)sp * kGuPart + i3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    float u = 0.f, v = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < kBatchGuSplit; ++sp) {
-      u += pu[sp];
-      v += pv[sp];
-    }
-    gg.out[(size_t)m * gg.ld + r] = silu_mul(u, v);
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * mq + i;
+    if (m < s.cnt) s.out[(size_t)m * s.ld + r] = silu_mul(u[i], v[i]);
   }
 }
 
-template <class Fn>
-__device__ __forceinline__ void by_tiles(int rows, Fn fn) {
-  if (rows >= 64) fn(std::integral_constant<int, 4>{});
-  else fn(std::integral_constant<int, 2>{});
+// The staged activations of one unit: 16-byte words of [hi | lo][token][K].
+constexpr int kGuStW = (2 * 16 * (32 * kGuKc / 8) + kBlock - 1) / kBlock;  // words per thread
+
+__device__ __forceinline__ int gu_token(const int *toks, int tok0, int m, int cnt) {
+  m = min(m, cnt - 1);
+  return toks ? toks[m] : tok0 + m;
 }
 
-// One workgroup per item, in this order:
-//  1 matrix-core items of the routed experts: (entry, row group, K split),
-//    entry = a 16-token chunk of an expert with 16 or more tokens;
-//  2 matrix-core items of the shared expert when it has 16 or more tokens;
-//  3 VALU items (entry, 16-row tile) of experts with fewer than 16 tokens;
-//  4 VALU items of the shared expert below 16 tokens.
-// Workgroups past the last item return at once.
-__global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
-  extern __shared__ __align__(16) uint16_t gu_lds[];  // staged activation chunk
-  __shared__ int flag;
-  const int n_qm = a.n_q[0], n_qv = a.n_q[1];
-  const int B = a.B, F = a.F, Fs = a.Fs;
-  const bool s_mfma = Fs > 0 && B >= kBatchMfmaMin;
-  const int nch_s = s_mfma ? (B + 15) >> 4 : 0;
-  const int rg_r = min(kBatchGuRows, F), ngr = F / rg_r;
-  const int rg_s = Fs > 0 ? min(kBatchGuRows, Fs) : 16, ngs = Fs / rg_s;
-  const int n_mr = n_qm * ngr * kBatchGuSplit, n_ms = nch_s * ngs * kBatchGuSplit;
-  const int n_vr = n_qv * (F / 16), n_vs = (Fs > 0 && !s_mfma) ? Fs / 16 : 0;
-  int i = blockIdx.x;
-  if (i < n_mr + n_ms) {
-    GuGroup gg;
-    int split, grp, rows;
-    if (i < n_mr) {
-      const int e = i / (ngr * kBatchGuSplit), rem = i % (ngr * kBatchGuSplit), gi = rem / kBatchGuSplit;
-      split = rem % kBatchGuSplit;
-      const int q = a.gu_q[e], slot = q & 0xffff, c0 = 16 * (q >> 16);
-      const int ex = a.act_exp[slot], off = a.act_off[slot] + c0;
-      rows = rg_r;
-      gg.w1 = a.w1 + ((size_t)ex * F + gi * rg_r) * a.H;
-      gg.w3 = a.w3 + ((size_t)ex * F + gi * rg_r) * a.H;
-      gg.toks = a.pair_tok + off;
-      gg.tok0 = 0;
-      gg.cnt = min(16, a.act_cnt[slot] - c0);
-      gg.out = a.act + (size_t)off * F + gi * rg_r;
-      gg.ld = F;
-      grp = e * 4 + gi;
-    } else {
-      i -= n_mr;
-      const int c = i / (ngs * kBatchGuSplit), rem = i % (ngs * kBatchGuSplit), gi = rem / kBatchGuSplit;
-      split = rem % kBatchGuSplit;
-      rows = rg_s;
-      gg.w1 = a.s1 + (size_t)gi * rg_s * a.H;
-      gg.w3 = a.s3 + (size_t)gi * rg_s * a.H;
-      gg.toks = nullptr;
-      gg.tok0 = 16 * c;
-      gg.cnt = min(16, B - 16 * c);
-      gg.out = a.act_s + (size_t)(16 * c) * Fs + gi * rg_s;
-      gg.ld = Fs;
-      grp = (n_qm + c) * 4 + gi;
-    }
-    float *part = a.gu_part + (size_t)grp * kBatchGuSplit * kGuPart;
-    by_tiles(rows, [&](auto ntl) { gateup_group<decltype(ntl)::value>(a, gg, split, part, a.gu_cnt + grp, gu_lds, &flag); });
-    return;
+__device__ __forceinline__ void gu_stage_load(const BatchArgs &a, const int *tok_l, const GuUnit &s,
+                                              uint4 (&st)[kGuStW]) {
+  const int kbeg = 32 * s.k0, wpr = 4 * (s.k1 - s.k0), nw = 32 * wpr;
+  const size_t plane = (size_t)a.B * a.H;
+#pragma unroll
+  for (int j = 0; j < kGuStW; ++j) {
+    const int w = min((int)threadIdx.x + kBlock * j, nw - 1);
+    const int pl = w / (16 * wpr), m = (w / wpr) & 15, c = w % wpr;
+    st[j] = ld16(a.hp + pl * plane + (size_t)tok_l[m] * a.H + kbeg + 8 * c);
   }
-  i -= n_mr + n_ms;
-  GuItem it;
-  if (i < n_vr) {
-    const int slot = a.gu_q[n_qm + i / (F / 16)], tile = i % (F / 16);
-    const int ex = a.act_exp[slot], off = a.act_off[slot];
-    it.w1 = a.w1 + ((size_t)ex * F + tile * 16) * a.H;
-    it.w3 = a.w3 + ((size_t)ex * F + tile * 16) * a.H;
-    it.toks = a.pair_tok + off;
-    it.tok0 = 0;
-    it.out = a.act + (size_t)off * F + tile * 16;
-    it.ld = F;
-    it.cnt = a.act_cnt[slot];
-  } else if (i - n_vr < n_vs) {
-    const int tile = i - n_vr;
-    it.w1 = a.s1 + (size_t)tile * 16 * a.H;
-    it.w3 = a.s3 + (size_t)tile * 16 * a.H;
-    it.toks = nullptr;
-    it.tok0 = 0;
-    it.out = a.act_s + tile * 16;
-    it.ld = Fs;
-    it.cnt = B;
+}
+
+__device__ __forceinline__ void gu_stage_store(const uint4 (&st)[kGuStW], const GuUnit &s, uint16_t *lds) {
+  const int wpr = 4 * (s.k1 - s.k0), nw = 32 * wpr;
+#pragma unroll
+  for (int j = 0; j < kGuStW; ++j) {
+    const int w = (int)threadIdx.x + kBlock * j;
+    if (w < nw) {
+      const int pl = w / (16 * wpr), m = (w / wpr) & 15, c = w % wpr;
+      *reinterpret_cast<uint4 *>(lds + (pl * 16 + m) * kGuLd + 8 * c) = st[j];
+    }
+  }
+}
+
+struct GuGeom {
+  int NK, NCK, F, Fs, B, rg_r, ngr, rg_s, ng_r, nch_s;
+};
+
+// Unit u: its group's weights, output, slots and tokens (toks[m], or tok0 + m).
+__device__ __forceinline__ void gu_meta(const BatchArgs &a, const GuGeom &q, int u, GuUnit &s, const int *&toks,
+                                        int &tok0) {
+  const int gi = u / q.NCK, H = a.H;
+  s.group = gi;
+  s.nck = q.NCK;
+  if (gi < q.ng_r) {
+    const int e = gi / q.ngr, r0 = (gi % q.ngr) * q.rg_r;
+    const int qe = a.gu_q[e], slot = qe & 0xffff, c0 = 16 * (qe >> 16);
+    const int ex = a.act_exp[slot], off = a.act_off[slot] + c0;
+    s.w1 = a.w1 + ((size_t)ex * q.F + r0) * H;
+    s.w3 = a.w3 + ((size_t)ex * q.F + r0) * H;
+    s.cnt = min(16, a.act_cnt[slot] - c0);
+    s.out = a.act + (size_t)off * q.F + r0;
+    s.ld = q.F;
+    s.ntl = q.rg_r >> 4;
+    s.slots = a.gu_part + (size_t)gi * q.NCK * kGuSlotFloatsR;
+    s.arrivals = a.gu_cnt + gi;
+    toks = a.pair_tok + off;
+    tok0 = 0;
   } else {
-    return;
+    const int gs = gi - q.ng_r, r0 = (gs / q.nch_s) * q.rg_s, c = gs % q.nch_s;
+    s.w1 = a.s1 + (size_t)r0 * H;
+    s.w3 = a.s3 + (size_t)r0 * H;
+    s.cnt = min(16, q.B - 16 * c);
+    s.out = a.act_s + (size_t)(16 * c) * q.Fs + r0;
+    s.ld = q.Fs;
+    s.ntl = q.rg_s >> 4;
+    s.slots = a.gu_part_s + (size_t)gs * q.NCK * kGuSlotFloatsR;
+    s.arrivals = a.gu_cnt_s + gs;
+    toks = nullptr;
+    tok0 = 16 * c;
   }
-  gateup_valu(a, it);
+}
+
+__device__ __forceinline__ void gu_chunk(GuUnit &s, int u, int NK) {
+  s.kc = u % s.nck;
+  s.k0 = s.kc * kGuKc;
+  s.k1 = min(NK, s.k0 + kGuKc);
+}
+
+// Matrix-core units laid end to end (group by group, K chunks in order) are
+// cut into one contiguous run per workgroup (two workgroups per CU), so
+// consecutive units of a workgroup mostly share a group and its tokens.
+// While a unit streams its weights, the next unit's activations are loaded
+// into registers and then written to the other LDS buffer, so staging does
+// not stall the weight stream.  VALU units are dealt round-robin after.
+__global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
+  __shared__ __align__(16) uint16_t lds[2][kGuLds / 2];
+  __shared__ int tok_l[2][16];
+  __shared__ int s_flag;
+  const int tid = threadIdx.x;
+  const int n_qm = a.n_q[0], n_qv = a.n_q[1];
+  GuGeom q;
+  q.B = a.B;
+  q.F = a.F;
+  q.Fs = a.Fs;
+  q.NK = a.H >> 5;
+  q.NCK = (q.NK + kGuKc - 1) / kGuKc;
+  const bool s_mfma = q.Fs > 0 && q.B >= kBatchMfmaMin;
+  q.nch_s = s_mfma ? (q.B + 15) >> 4 : 0;
+  q.rg_r = min(kBatchGuRows, q.F);
+  q.ngr = q.F / q.rg_r;
+  q.rg_s = q.Fs > 0 ? min(kBatchGuRows, q.Fs) : 16;
+  q.ng_r = n_qm * q.ngr;
+  const int ng = q.ng_r + q.nch_s * (q.Fs / q.rg_s);
+  const int n_mfma = ng * q.NCK;
+  const int G = gridDim.x, w = blockIdx.x;
+  // workgroups w and w + G/2 are dispatched to the same CU: give them
+  // neighbouring runs, so that every CU holds the same number of units
+  const int half = G >> 1, r = (G & 1) ? w : 2 * (w % half) + w / half;
+  const int ub = (int)((long)r * n_mfma / G), ue = (int)((long)(r + 1) * n_mfma / G);
+  if (ub < ue) {
+    GuUnit cur;
+    const int *toks;
+    int tok0;
+    gu_meta(a, q, ub, cur, toks, tok0);
+    gu_chunk(cur, ub, q.NK);
+    if (tid < 16) tok_l[0][tid] = gu_token(toks, tok0, tid, cur.cnt);
+    __syncthreads();
+    {
+      uint4 st[kGuStW];
+      gu_stage_load(a, tok_l[0], cur, st);
+      gu_stage_store(st, cur, lds[0]);
+    }
+    __syncthreads();
+    int b = 0;
+    for (int u = ub; u < ue; ++u) {
+      const bool more = u + 1 < ue;
+      GuUnit nx = cur;
+      if (more) {
+        if ((u + 1) % q.NCK == 0) {  // the next unit starts a new group
+          gu_meta(a, q, u + 1, nx, toks, tok0);
+          if (tid < 16) tok_l[b ^ 1][tid] = gu_token(toks, tok0, tid, nx.cnt);
+        } else if (tid < 16) {
+          tok_l[b ^ 1][tid] = tok_l[b][tid];
+        }
+        gu_chunk(nx, u + 1, q.NK);
+      }
+      __syncthreads();
+      uint4 st[kGuStW];
+      if (more) gu_stage_load(a, tok_l[b ^ 1], nx, st);
+      asm volatile("" ::: "memory");  // issue the staging loads ahead of the weight stream
+      if (cur.ntl == 4) gu_unit<4>(a, cur, lds[b]);
+      else gu_unit<2>(a, cur, lds[b]);
+      if (more) gu_stage_store(st, nx, lds[b ^ 1]);
+      // arrival: this workgroup's slot stores have completed before it is counted
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(cur.arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_flag = prev == (unsigned)q.NCK - 1;
+        if (s_flag) __hip_atomic_store(cur.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (s_flag) {
+        if (cur.ntl == 4) gu_combine<4>(cur);
+        else gu_combine<2>(cur);
+      }
+      cur = nx;
+      b ^= 1;
+    }
+  }
+  const int n_vr = n_qv * (q.F / 16), n_vs = (q.Fs > 0 && !s_mfma) ? q.Fs / 16 : 0;
+  for (int i = (w - (n_mfma > 0 ? n_mfma % G : 0) + G) % G; i < n_vr + n_vs; i += G) {
+    GuItem it;
+    if (i < n_vr) {
+      const int slot = a.gu_q[n_qm + i / (q.F / 16)], tile = i % (q.F / 16);
+      const int ex = a.act_exp[slot], off = a.act_off[slot];
+      it.w1 = a.w1 + ((size_t)ex * q.F + tile * 16) * a.H;
+      it.w3 = a.w3 + ((size_t)ex * q.F + tile * 16) * a.H;
+      it.toks = a.pair_tok + off;
+      it.tok0 = 0;
+      it.out = a.act + (size_t)off * q.F + tile * 16;
+      it.ld = q.F;
+      it.cnt = a.act_cnt[slot];
+    } else {
+      const int tile = i - n_vr;
+      it.w1 = a.s1 + (size_t)tile * 16 * a.H;
+      it.w3 = a.s3 + (size_t)tile * 16 * a.H;
+      it.toks = nullptr;
+      it.tok0 = 0;
+      it.out = a.act_s + tile * 16;
+      it.ld = q.Fs;
+      it.cnt = q.B;
+    }
+    gateup_valu(a, it);
+  }
 }
 
 // ================================================================ launch 5
@@ -684,7 +769,7 @@ __device__ __forceinline__ void down_load_w(const uint16_t *tile, uint4 (&wv)[NK
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const uint16_t *p = tile + (size_t)n * (32 * NKS) + 8 * g;
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) wv[s] = ld_stream16(p + 32 * s);
+  for (int s = 0; s < NKS; ++s) wv[s] = ld16(p + 32 * s);
 }
 
 struct DnItem {
@@ -882,14 +967,6 @@ hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]
   const int n_wo = a.H / 16;
   const int n_q = (a.Dq + 15) / 16 * kBatchQkvSplit;
   const int n_rk = a.H / kBatchRtrK;
-  // upper bound of gate/up items (workgroups past the actual count return)
-  const int P = a.B * a.K;
-  const int max_qm = (P + 7) / 8, max_qv = min(a.E, P);
-  const int rg_r = min(kBatchGuRows, a.F), rg_s = a.Fs > 0 ? min(kBatchGuRows, a.Fs) : 16;
-  const int nch_s = (a.B + 15) / 16;
-  const long g4l = (long)max_qm * (a.F / rg_r) * kBatchGuSplit + (long)nch_s * (a.Fs / rg_s) * kBatchGuSplit +
-                   (long)max_qv * (a.F / 16) + a.Fs / 16;
-  const int g4 = (int)g4l;
   hipError_t e;
   auto rec = [&](int i, int j) { return ev ? hipEventRecord(ev[i][j], s) : hipSuccess; };
 #define DL_TRY(x) do { if ((e = (x)) != hipSuccess) return e; } while (0)
@@ -906,11 +983,7 @@ hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]
   DL_TRY(hipGetLastError());
   DL_TRY(rec(2, 1));
   DL_TRY(rec(3, 0));
-  const size_t gu_lds = (size_t)2 * 16 * (a.H / kBatchGuSplit + kGuPad) * 2;
-  if (gu_lds > 65536)
-    DL_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(gateup_b), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)gu_lds));
-  hipLaunchKernelGGL(gateup_b, dim3(g4), dim3(kBlock), gu_lds, s, a);
+  hipLaunchKernelGGL(gateup_b, dim3(a.gu_grid), dim3(kBlock), 0, s, a);
   DL_TRY(hipGetLastError());
   DL_TRY(rec(3, 1));
   DL_TRY(rec(4, 0));

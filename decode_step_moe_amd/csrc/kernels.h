@@ -70,8 +70,11 @@ constexpr int kBatchQkvSplit = 4;     // K splits of the attention input project
 constexpr int kBatchRtrExperts = 32;  // router experts per workgroup
 constexpr int kBatchRtrK = 256;       // router K per workgroup
 constexpr int kBatchMfmaMin = 16;     // an expert with at least this many tokens uses MFMA
-constexpr int kBatchGuRows = 64;      // gate/up rows of W1 (and of W3) per matrix-core item
-constexpr int kBatchGuSplit = 8;      // K splits of a matrix-core gate/up item (combined by the last)
+constexpr int kBatchGuRows = 64;      // gate/up rows of W1 (and of W3) per matrix-core group
+constexpr int kGuKc = 14;             // K steps (of 32) of one matrix-core gate/up work unit
+// K chunks (units, and partial-sum slots) of one gate/up group.
+constexpr int batch_gu_chunks(int H) { return (H / 32 + kGuKc - 1) / kGuKc; }
+constexpr int kGuSlotFloatsR = 2 * 4 * 16 * 16;  // [W1 | W3][16-row tile][row][token], one 16-token chunk
 constexpr int kBatchLaunches = 5;
 
 struct BatchArgs {
@@ -102,8 +105,11 @@ struct BatchArgs {
   int *gu_q;          // [4 E] gate/up work lists: matrix-core entries slot | (16-token chunk << 16),
                       //       then VALU entries (slot)
   int *n_q;           // [2]   their lengths
-  float *gu_part;     // [entries][groups][kBatchGuSplit][2 * kBatchGuRows][16] partial gate/up sums
-  unsigned *gu_cnt;   // [entries][groups] arrivals of a matrix-core item's K splits
+  float *gu_part;     // [routed groups][K chunks][kGuSlotFloatsR] partial gate/up sums
+  float *gu_part_s;   // [shared groups][K chunks][kGuSlotFloatsR]
+  unsigned *gu_cnt;   // [routed groups] arrivals of a group's units (re-armed by the last)
+  unsigned *gu_cnt_s; // [shared groups]
+  int gu_grid;        // workgroups of the gate/up launch (two per CU)
   unsigned *counter;  // [1] arrivals of the top-k workgroups (re-armed by the last)
   int B, H, Dq, Do, E, K, F, Fs;
   float eps;

@@ -4,6 +4,7 @@
 // the kernels of proj.hip, router.hip and experts.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -87,14 +88,20 @@ struct Scratch {
   uint16_t *hp = nullptr;        // [2][maxB][H]
   int *gu_q = nullptr;           // [4 E] gate/up work lists
   int *n_q = nullptr;            // [2]
-  float *gu_part = nullptr;      // [entries][4][kBatchGuSplit][2 * kBatchGuRows * 16]
-  unsigned *gu_cnt = nullptr;    // [entries][4]
+  float *gu_part = nullptr;      // routed group slots, then shared group slots
+  unsigned *gu_cnt = nullptr;    // routed group counters, then shared group counters
 };
 
-// Capacity of the batched gate/up matrix-core entries: 16-token chunks of
-// experts with >= 16 tokens (at most B*k/8 of them) plus the shared expert's
-// chunks (at most 4).
-size_t gu_entries(const decode_layer_config &c) { return ((size_t)c.max_batch * c.top_k + 7) / 8 + 4; }
+// Batched gate/up matrix-core groups: 16-token chunks of the routed experts
+// with >= 16 tokens (at most B*k/8 chunks) times the row groups of one
+// expert, and the shared expert's 16-token chunks (at most 4) times its row
+// groups.
+size_t gu_groups_routed(const decode_layer_config &c) {
+  return ((size_t)c.max_batch * c.top_k + 7) / 8 * (c.expert_ffn / std::min(kBatchGuRows, c.expert_ffn));
+}
+size_t gu_groups_shared(const decode_layer_config &c) {
+  return c.shared_ffn > 0 ? (size_t)(c.max_batch + 15) / 16 * (c.shared_ffn / std::min(kBatchGuRows, c.shared_ffn)) : 0;
+}
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -120,8 +127,8 @@ Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
       // batched arrays
       (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2,
       Bb ? 4 * E * 4 : size_t(0), Bb ? size_t(8) : size_t(0),
-      Bb ? gu_entries(c) * 4 * kBatchGuSplit * (2 * kBatchGuRows * 16) * 4 : size_t(0),
-      Bb ? gu_entries(c) * 4 * 4 : size_t(0)};
+      Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * batch_gu_chunks(c.hidden) * kGuSlotFloatsR * 4 : size_t(0),
+      Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * 4 : size_t(0)};
   Layout L;
   size_t o = 0;
   for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
@@ -147,6 +154,7 @@ struct decode_layer {
   void *scratch_base = nullptr;
   Scratch s;
   SinglePlan single;
+  int gu_grid = 0;         // workgroups of the batched gate/up launch
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   void *trace = nullptr;   // caller's device buffer for the phase trace
@@ -340,6 +348,7 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
   h->s.n_q = (int *)(b + L.off[24]);
   h->s.gu_part = (float *)(b + L.off[25]);
   h->s.gu_cnt = (unsigned *)(b + L.off[26]);
+  h->gu_grid = 2 * std::max(1, cu_count(device));
   // The hand-off counters start at zero and are re-armed by the kernels
   // themselves, and the tagged hand-off values start with tag 0, which no
   // step uses (tags are the step counter + 1), so no step ever needs a memset.
@@ -470,7 +479,10 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
     ba.gu_q = h->s.gu_q;
     ba.n_q = h->s.n_q;
     ba.gu_part = h->s.gu_part;
+    ba.gu_part_s = h->s.gu_part + gu_groups_routed(c) * batch_gu_chunks(c.hidden) * kGuSlotFloatsR;
     ba.gu_cnt = h->s.gu_cnt;
+    ba.gu_cnt_s = h->s.gu_cnt + gu_groups_routed(c);
+    ba.gu_grid = h->gu_grid;
     ba.counter = h->s.counters + 2;
     ba.B = B;
     ba.H = c.hidden;

@@ -93,10 +93,13 @@ def test_batched_scratch_follows_the_path():
     as bf16 hi + lo planes) exist exactly when some step can take that path."""
     c = good()                       # TP16 shard shapes, max_batch 64
     B, H, Dq, E = 64, 7168, 512, 384
-    entries = (B * 8 + 7) // 8 + 4     # gate/up matrix-core entries: B*k/8 chunks + 4 shared
+    F = Fs = 128
+    groups_r = (B * 8 + 7) // 8 * (F // 64)   # gate/up groups: B*k/8 16-token chunks x 64-row groups
+    groups_s = (B + 15) // 16 * (Fs // 64)    # shared expert: 16-token chunks x 64-row groups
+    chunks = (H // 32 + 13) // 14             # K chunks of 14 steps of 32: one partial slot each
     batched = (_a256(4 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
                + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(8)
-               + _a256(entries * 4 * 8 * 2048 * 4) + _a256(entries * 4 * 4))
+               + _a256((groups_r + groups_s) * chunks * 2048 * 4) + _a256((groups_r + groups_s) * 4))
     auto = dl.scratch_bytes(c, 256)
     c.path = dl.DL_PATH_MULTI
     multi = dl.scratch_bytes(c, 256)
