@@ -32,9 +32,10 @@
 //              x a K chunk) cut into one contiguous run per workgroup, two
 //              workgroups per CU, K chunks combined by the last to arrive;
 //              then the VALU items of experts with fewer than 16 tokens.
-//  5 down_b    16 rows of y per workgroup over every active expert and the
-//              shared expert, summed in a fixed order in LDS:
-//              y[t, i] = S2[i] . a_s[t] + sum_p w_p W2[e_p, i] . a[p].
+//  5 down_b    y[t, i] = S2[i] . a_s[t] + sum_p w_p W2[e_p, i] . a[p]:
+//              units (64 rows of y, one expert) cut into one contiguous run
+//              per workgroup, each expert's activations staged once in LDS,
+//              per-workgroup y tiles added in a fixed order by the last.
 //
 // MFMA operands.  x, attn and the weights are bf16 already.  h and the SwiGLU
 // activations are fp32; each is split as x = hi + lo with hi = x truncated
@@ -761,203 +762,249 @@ __global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
 }
 
 // ================================================================ launch 5
-// Weights of one item for this lane: row n = lane % 16 of the 16-row tile,
-// K positions 32 s + 8 g (g = lane / 16) for s < NKS = Fd / 32.  MFMA items
-// use them as the B operand; VALU items reduce the four g lanes of a row.
-template <int NKS>
-__device__ __forceinline__ void down_load_w(const uint16_t *tile, uint4 (&wv)[NKS]) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const uint16_t *p = tile + (size_t)n * (32 * NKS) + 8 * g;
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) wv[s] = ld16(p + 32 * s);
+// Down projection, y[t, i] = S2[i] . a_s[t] + sum_p w_p W2[e_p, i] . a[p].
+// Units = (group of 64 rows of y, entry), an entry being one active expert
+// (all its tokens) or the shared expert (every token, weight 1).  The
+// units, laid end to end group by group, are cut into one contiguous run
+// per workgroup (two per CU; the two on one CU take neighbouring runs).
+// For a unit, wave w loads rows 16w .. 16w + 15 of the group from the
+// entry's weights (all of F: 8 loads of 16 bytes per lane at F = 256), and
+// the workgroup stages each 16-token chunk of the entry's activations in
+// LDS once — bf16 hi and lo planes for the matrix cores when the entry has
+// 16 or more tokens, fp32 rows for the VALU below that — instead of every
+// wave re-reading them.  The next unit's weights are requested right after
+// the current chunk's activation loads, so they stream during the compute.
+// Results are added into an LDS tile y[token][64 rows] (a wave owns its 16
+// rows; within an entry a token occurs once, so no two lanes add into one
+// element).  When its run leaves a group, the workgroup writes the tile to
+// the group's slot numbered by its place among the group's workgroups
+// (written through to the device coherence point) and counts itself; the
+// last to arrive adds the slots in slot order into moe_out.
+constexpr int kDnRows = 64;
+constexpr int kDnLd = 256 + 8;   // bf16 per LDS row of a staged chunk plane (F <= 256)
+constexpr int kDnLdF = 256 + 4;  // fp32 per LDS row of a staged VALU chunk
+
+__device__ __forceinline__ int dn_run(int w, int G) {
+  const int half = G >> 1;
+  return (G & 1) ? w : 2 * (w % half) + w / half;
 }
 
-struct DnItem {
-  const float *act;   // row m at act + m * Fd
-  const int *toks;    // token of row m (nullptr: m itself)
+// Rows 16 wv + n of the group, K positions 32 s + 8 g (s < Fd / 32).
+__device__ __forceinline__ void dn_load_w(const uint16_t *rows, int Fd, uint4 (&w)[8]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+  const int nks = Fd >> 5;
+  const uint16_t *p = rows + (size_t)(16 * wv + n) * Fd + 8 * g;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) w[s] = ld16(p + 32 * min(s, nks - 1));
+}
+
+struct DnSrc {
+  const float *act;   // chunk row m at act + m * Fd (m < cnt)
+  const int *toks;    // token of row m (nullptr: tok0 + m)
   const float *wts;   // weight of row m (nullptr: 1)
-  int cnt;
-  __device__ int tok(int m) const { return toks ? toks[m] : m; }
-  __device__ float wt(int m) const { return wts ? wts[m] : 1.f; }
+  int tok0, cnt, Fd;
 };
 
-// Rows [c0, c0 + 16) of an item on the matrix cores: load, then compute.
-template <int NKS>
-struct MfmaChunk {
-  float4 xv[NKS][2];
-  __device__ __forceinline__ void load(const DnItem &it, int c0) {
-    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const float *ap = it.act + (size_t)min(c0 + n, it.cnt - 1) * (32 * NKS) + 8 * g;
+// Activation loads of one chunk: 8 consecutive fp32 of row m per octet.
+__device__ __forceinline__ void dn_stage_load(const DnSrc &c, float4 (&v)[2][2]) {
+  const int opr = c.Fd >> 3, no = 16 * opr;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      xv[s][0] = ld16f(ap + 32 * s);
-      xv[s][1] = ld16f(ap + 32 * s + 4);
+  for (int j = 0; j < 2; ++j) {
+    const int o = min((int)threadIdx.x + kBlock * j, no - 1), m = min(o / opr, c.cnt - 1), k = 8 * (o % opr);
+    const float *p = c.act + (size_t)m * c.Fd + k;
+    v[j][0] = ld16f(p);
+    v[j][1] = ld16f(p + 4);
+  }
+}
+
+__device__ __forceinline__ void dn_stage_store(const DnSrc &c, const float4 (&v)[2][2], bool mfma, uint16_t *stg) {
+  const int opr = c.Fd >> 3, no = 16 * opr;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int o = (int)threadIdx.x + kBlock * j;
+    if (o < no) {
+      const int m = o / opr, k = 8 * (o % opr);
+      if (mfma) {
+        const float x[8] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w, v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
+        uint4 hi, lo;
+        split8(x, hi, lo);
+        *reinterpret_cast<uint4 *>(stg + m * kDnLd + k) = hi;
+        *reinterpret_cast<uint4 *>(stg + (16 + m) * kDnLd + k) = lo;
+      } else {
+        float *f = reinterpret_cast<float *>(stg) + m * kDnLdF + k;
+        *reinterpret_cast<float4 *>(f) = v[j][0];
+        *reinterpret_cast<float4 *>(f + 4) = v[j][1];
+      }
     }
   }
-  __device__ __forceinline__ void compute(const DnItem &it, int c0, const uint4 (&wv)[NKS], float (*y)[16]) const {
-    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+}
+
+// One staged chunk (rows m < cnt) against this wave's weights, into the tile.
+__device__ __forceinline__ void dn_compute(const DnSrc &c, bool mfma, const uint4 (&w)[8], const uint16_t *stg,
+                                           const int *s_tok, const float *s_wt, float *ytile) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+  const int nks = c.Fd >> 5, col = 16 * wv + n;
+  if (mfma) {
+    const uint16_t *lh = stg + n * kDnLd + 8 * g, *ll = lh + 16 * kDnLd;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const float x[8] = {xv[s][0].x, xv[s][0].y, xv[s][0].z, xv[s][0].w,
-                          xv[s][1].x, xv[s][1].y, xv[s][1].z, xv[s][1].w};
-      uint4 hi, lo;
-      split8(x, hi, lo);
-      acc = mfma_bf16(hi, wv[s], acc);
-      acc = mfma_bf16(lo, wv[s], acc);
-    }
+    for (int s = 0; s < 8; ++s)
+      if (s < nks) {
+        const uint4 hv = *reinterpret_cast<const uint4 *>(lh + 32 * s);
+        const uint4 lv = *reinterpret_cast<const uint4 *>(ll + 32 * s);
+        acc = mfma_bf16(hv, w[s], acc);
+        acc = mfma_bf16(lv, w[s], acc);
+      }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = c0 + 4 * g + i;
-      if (m < it.cnt) y[it.tok(m)][n] += it.wt(m) * acc[i];
-    }
-  }
-};
-
-// Rows m0 .. m0 + TB - 1 (below cnt) of an item on the VALU.
-template <int NKS>
-struct ValuRows {
-  static constexpr int TB = 8 / NKS;   // 64 VGPRs of activations per batch
-  float4 xv[TB][NKS][2];
-  __device__ __forceinline__ void load(const DnItem &it, int m0) {
-    const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const float *ap = it.act + (size_t)min(m0 + tb, it.cnt - 1) * (32 * NKS) + 8 * g;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        xv[tb][s][0] = ld16f(ap + 32 * s);
-        xv[tb][s][1] = ld16f(ap + 32 * s + 4);
-      }
-    }
-  }
-  __device__ __forceinline__ void compute(const DnItem &it, int m0, const uint4 (&wv)[NKS], float (*y)[16]) const {
-    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      float acc = 0.f;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        float wf[8];
-        unpack8(wv[s], wf);
-        const float x[8] = {xv[tb][s][0].x, xv[tb][s][0].y, xv[tb][s][0].z, xv[tb][s][0].w,
-                            xv[tb][s][1].x, xv[tb][s][1].y, xv[tb][s][1].z, xv[tb][s][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(wf[e], x[e], acc);
-      }
-      acc += __shfl_xor(acc, 16, kWave);   // lanes g, g ^ 1
-      acc += __shfl_xor(acc, 32, kWave);   // (v0 + v1) + (v2 + v3)
-      const int m = m0 + tb;
-      if (g == 0 && m < it.cnt) y[it.tok(m)][n] += it.wt(m) * acc;
-    }
-  }
-};
-
-// One item with weights wv; if `next` is set, the next item's weights are
-// requested right after this item's first activation batch, so the wait
-// for those activations does not include them (a wave's loads complete in
-// issue order).
-template <int NKS>
-__device__ __forceinline__ void down_item(const DnItem &it, const uint4 (&wv)[NKS], float (*y)[16],
-                                          const uint16_t *next, uint4 (&wn)[NKS]) {
-  if (it.cnt >= kBatchMfmaMin) {
-    for (int c0 = 0; c0 < it.cnt; c0 += 16) {
-      MfmaChunk<NKS> ch;
-      ch.load(it, c0);
-      if (c0 == 0 && next) down_load_w<NKS>(next, wn);
-      DL_SCHED_FENCE();
-      ch.compute(it, c0, wv, y);
+      const int m = 4 * g + i;
+      if (m < c.cnt) ytile[s_tok[m] * kDnRows + col] += s_wt[m] * acc[i];
     }
   } else {
-    for (int m0 = 0; m0 < it.cnt; m0 += ValuRows<NKS>::TB) {
-      ValuRows<NKS> rw;
-      rw.load(it, m0);
-      if (m0 == 0 && next) down_load_w<NKS>(next, wn);
-      DL_SCHED_FENCE();
-      rw.compute(it, m0, wv, y);
-    }
-  }
-}
-
-// Routed items of this wave: active slots wv, wv + 4, ... (metadata in LDS).
-template <int NKS>
-__device__ void down_routed(const BatchArgs &a, int i0, int n_act, const int *exp_, const int *cnt_,
-                            const int *off_, float (*y)[16]) {
-  constexpr int Fd = 32 * NKS;
-  const int wv = threadIdx.x >> 6;
-  if (wv >= n_act) return;
-  auto tile = [&](int slot) { return a.w2 + ((size_t)exp_[slot] * a.H + i0) * Fd; };
-  uint4 wc[NKS], wn[NKS];
-  down_load_w<NKS>(tile(wv), wc);
-  for (int i = wv; i < n_act; i += kWavesPerBlock) {
-    const int off = off_[i];
-    const DnItem it{a.act + (size_t)off * Fd, a.pair_tok + off, a.pair_w + off, cnt_[i]};
-    const int nx = i + kWavesPerBlock;
-    down_item<NKS>(it, wc, y, nx < n_act ? tile(nx) : nullptr, wn);
+    const float *xf = reinterpret_cast<const float *>(stg) + 8 * g;
+    for (int m = 0; m < c.cnt; ++m) {
+      float acc = 0.f;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) wc[s] = wn[s];
-  }
-}
-
-// The shared expert (weight 1, every token): with 16 or more tokens wave w
-// takes the 16-token chunk w on the matrix cores; below that one wave takes
-// all tokens on the VALU.
-template <int NKS>
-__device__ void down_shared(const BatchArgs &a, int i0, int n_act, float (*y)[16]) {
-  const int wv = threadIdx.x >> 6, B = a.B;
-  const DnItem it{a.act_s, nullptr, nullptr, B};
-  const uint16_t *tile = a.s2 + (size_t)i0 * (32 * NKS);
-  uint4 wv_[NKS];
-  if (B >= kBatchMfmaMin) {
-    if (16 * wv < B) {
-      down_load_w<NKS>(tile, wv_);
-      MfmaChunk<NKS> ch;
-      ch.load(it, 16 * wv);
-      DL_SCHED_FENCE();
-      ch.compute(it, 16 * wv, wv_, y);
-    }
-  } else if (wv == n_act % kWavesPerBlock) {
-    down_load_w<NKS>(tile, wv_);
-    for (int m0 = 0; m0 < B; m0 += ValuRows<NKS>::TB) {
-      ValuRows<NKS> rw;
-      rw.load(it, m0);
-      DL_SCHED_FENCE();
-      rw.compute(it, m0, wv_, y);
+      for (int s = 0; s < 8; ++s)
+        if (s < nks) {
+          float wf[8];
+          unpack8(w[s], wf);
+          const float4 x0 = *reinterpret_cast<const float4 *>(xf + m * kDnLdF + 32 * s);
+          const float4 x1 = *reinterpret_cast<const float4 *>(xf + m * kDnLdF + 32 * s + 4);
+          acc = fmaf(wf[0], x0.x, acc);
+          acc = fmaf(wf[1], x0.y, acc);
+          acc = fmaf(wf[2], x0.z, acc);
+          acc = fmaf(wf[3], x0.w, acc);
+          acc = fmaf(wf[4], x1.x, acc);
+          acc = fmaf(wf[5], x1.y, acc);
+          acc = fmaf(wf[6], x1.z, acc);
+          acc = fmaf(wf[7], x1.w, acc);
+        }
+      acc += __shfl_xor(acc, 16, kWave);   // lanes g, g ^ 1
+      acc += __shfl_xor(acc, 32, kWave);   // (v0 + v1) + (v2 + v3)
+      if (g == 0) ytile[s_tok[m] * kDnRows + col] += s_wt[m] * acc;
     }
   }
 }
 
-template <class Fn>
-__device__ __forceinline__ void by_nks(int Fd, Fn fn) {
-  switch (Fd) {
-    case 32: fn(std::integral_constant<int, 1>{}); break;
-    case 64: fn(std::integral_constant<int, 2>{}); break;
-    case 128: fn(std::integral_constant<int, 4>{}); break;
-    default: fn(std::integral_constant<int, 8>{}); break;
-  }
-}
-
-// Workgroup: rows [16 b, 16 b + 16) of y for every token.  Each wave adds its
-// items into its own LDS accumulator; the four are added in wave order.
-__global__ void __launch_bounds__(kBlock) down_b(BatchArgs a) {
-  __shared__ float yw[kWavesPerBlock][kMaxBatch][16];
+__global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
+  __shared__ float ytile[kMaxBatch * kDnRows];
+  __shared__ __align__(16) uint16_t stg[2 * 16 * kDnLd];
   __shared__ int s_exp[kMaxExperts], s_cnt[kMaxExperts], s_off[kMaxExperts];
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const int B = a.B, H = a.H, i0 = blockIdx.x * 16;
+  __shared__ int s_tok[16];
+  __shared__ float s_wt[16];
+  __shared__ int s_flag;
+  const int tid = threadIdx.x;
+  const int B = a.B, H = a.H, F = a.F, Fs = a.Fs;
   const int n_act = *a.n_active;
-  for (int q = tid; q < kWavesPerBlock * kMaxBatch * 16; q += kBlock) (&yw[0][0][0])[q] = 0.f;
+  const int ne = n_act + (Fs > 0 ? 1 : 0), ng = H / kDnRows;
+  const long U = (long)ng * ne;
+  const int G = gridDim.x, ri = dn_run(blockIdx.x, G);
+  const int Ga = (int)min((long)G, U);
+  if (U == 0 || ri >= Ga) return;
   for (int q = tid; q < n_act; q += kBlock) {
     s_exp[q] = a.act_exp[q];
     s_cnt[q] = a.act_cnt[q];
     s_off[q] = a.act_off[q];
   }
+  for (int q = tid; q < kMaxBatch * kDnRows; q += kBlock) ytile[q] = 0.f;
   __syncthreads();
-  by_nks(a.F, [&](auto k) { down_routed<decltype(k)::value>(a, i0, n_act, s_exp, s_cnt, s_off, yw[wv]); });
-  if (a.Fs > 0) by_nks(a.Fs, [&](auto k) { down_shared<decltype(k)::value>(a, i0, n_act, yw[wv]); });
-  __syncthreads();
-  for (int q = tid; q < B * 16; q += kBlock) {
-    const int t = q >> 4, nn = q & 15;
-    a.moe_out[(size_t)t * H + i0 + nn] = ((yw[0][t][nn] + yw[1][t][nn]) + yw[2][t][nn]) + yw[3][t][nn];
+  auto rows_of = [&](long u, int &Fd) -> const uint16_t * {
+    const int r = (int)(u / ne), i = (int)(u % ne);
+    if (i < n_act) {
+      Fd = F;
+      return a.w2 + ((size_t)s_exp[i] * H + (size_t)r * kDnRows) * F;
+    }
+    Fd = Fs;
+    return a.s2 + (size_t)r * kDnRows * Fs;
+  };
+  long u = (long)ri * U / Ga;
+  const long ue = (long)(ri + 1) * U / Ga;
+  uint4 wc[8], wn[8];
+  {
+    int Fd;
+    const uint16_t *rows = rows_of(u, Fd);
+    dn_load_w(rows, Fd, wc);
+  }
+  for (; u < ue; ++u) {
+    const int r = (int)(u / ne), i = (int)(u % ne);
+    const bool routed = i < n_act;
+    DnSrc c;
+    c.Fd = routed ? F : Fs;
+    const int cnt_all = routed ? s_cnt[i] : B;
+    const int off = routed ? s_off[i] : 0;
+    const bool mfma = cnt_all >= kBatchMfmaMin;
+    for (int c0 = 0; c0 < cnt_all; c0 += 16) {
+      c.cnt = min(16, cnt_all - c0);
+      c.act = routed ? a.act + (size_t)(off + c0) * F : a.act_s + (size_t)c0 * Fs;
+      float4 v[2][2];
+      dn_stage_load(c, v);
+      int tk = 0;
+      float wt = 1.f;
+      if (tid < 16) {
+        const int m = min(tid, c.cnt - 1);
+        tk = routed ? a.pair_tok[off + c0 + m] : c0 + m;
+        wt = routed ? a.pair_w[off + c0 + m] : 1.f;
+      }
+      asm volatile("" ::: "memory");
+      if (c0 == 0 && u + 1 < ue) {  // the next unit's weights stream during this one
+        int Fd;
+        const uint16_t *rows = rows_of(u + 1, Fd);
+        dn_load_w(rows, Fd, wn);
+      }
+      asm volatile("" ::: "memory");
+      dn_stage_store(c, v, mfma, stg);
+      if (tid < 16) {
+        s_tok[tid] = tk;
+        s_wt[tid] = wt;
+      }
+      __syncthreads();
+      dn_compute(c, mfma, wc, stg, s_tok, s_wt, ytile);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) wc[s] = wn[s];
+    if (u + 1 == ue || (u + 1) / ne != r) {
+      // this workgroup is done with group r: its tile goes to its slot
+      const int first = (int)((((long)r * ne + 1) * Ga - 1) / U);
+      const int last = (int)((((long)r + 1) * ne * Ga - 1) / U);
+      const int slot = ri - first, nslots = last - first + 1;
+      const int tile_f = kMaxBatch * kDnRows;
+      float *slots = a.dn_part + (size_t)r * a.dn_slots * tile_f;
+      const __amdgpu_buffer_rsrc_t rs = gu_rsrc(slots, a.dn_slots * tile_f);
+      for (int q = tid; q < B * (kDnRows / 4); q += kBlock)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(v4u, *reinterpret_cast<const f32x4 *>(ytile + 4 * q)), rs,
+            (slot * tile_f + 4 * q) * 4, 0, kGuSc1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(a.dn_cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_flag = prev == (unsigned)nslots - 1;
+        if (s_flag) __hip_atomic_store(a.dn_cnt + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (s_flag) {
+        for (int q = tid; q < B * (kDnRows / 4); q += kBlock) {
+          f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          for (int s0 = 0; s0 < nslots; s0 += 8) {
+            f32x4 p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              p[j] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (min(s0 + j, nslots - 1) * tile_f + 4 * q) * 4, 0,
+                                                               kGuSc1));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (s0 + j < nslots) y += p[j];
+          }
+          const int t = q / (kDnRows / 4), c4 = q % (kDnRows / 4);
+          *reinterpret_cast<f32x4 *>(a.moe_out + (size_t)t * H + (size_t)r * kDnRows + 4 * c4) = y;
+        }
+      }
+      for (int q = tid; q < kMaxBatch * kDnRows; q += kBlock) ytile[q] = 0.f;
+      __syncthreads();
+    }
   }
 }
 
@@ -987,7 +1034,7 @@ hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]
   DL_TRY(hipGetLastError());
   DL_TRY(rec(3, 1));
   DL_TRY(rec(4, 0));
-  hipLaunchKernelGGL(down_b, dim3(n_wo), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(down_b, dim3(min(a.gu_grid, kDnMaxGrid)), dim3(kBlock), 0, s, a);
   DL_TRY(hipGetLastError());
   DL_TRY(rec(4, 1));
 #undef DL_TRY

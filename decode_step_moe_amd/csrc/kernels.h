@@ -74,6 +74,10 @@ constexpr int kBatchGuRows = 64;      // gate/up rows of W1 (and of W3) per matr
 constexpr int kGuKc = 14;             // K steps (of 32) of one matrix-core gate/up work unit
 // K chunks (units, and partial-sum slots) of one gate/up group.
 constexpr int batch_gu_chunks(int H) { return (H / 32 + kGuKc - 1) / kGuKc; }
+// Partial y tiles per 64-row group of the down projection: the most
+// workgroups one group's units can be spread over with a grid of G.
+constexpr int kDnMaxGrid = 512;  // workgroups of the down launch at most
+constexpr int batch_dn_slots(int H) { return (kDnMaxGrid + H / 64 - 1) / (H / 64) + 2; }
 constexpr int kGuSlotFloatsR = 2 * 4 * 16 * 16;  // [W1 | W3][16-row tile][row][token], one 16-token chunk
 constexpr int kBatchLaunches = 5;
 
@@ -109,7 +113,10 @@ struct BatchArgs {
   float *gu_part_s;   // [shared groups][K chunks][kGuSlotFloatsR]
   unsigned *gu_cnt;   // [routed groups] arrivals of a group's units (re-armed by the last)
   unsigned *gu_cnt_s; // [shared groups]
-  int gu_grid;        // workgroups of the gate/up launch (two per CU)
+  int gu_grid;        // workgroups of the gate/up and down launches (two per CU)
+  float *dn_part;     // [H/64][dn_slots][64][64] partial y tiles of the down projection
+  unsigned *dn_cnt;   // [H/64] arrivals of a row group's workgroups (re-armed by the last)
+  int dn_slots;       // batch_dn_slots(H)
   unsigned *counter;  // [1] arrivals of the top-k workgroups (re-armed by the last)
   int B, H, Dq, Do, E, K, F, Fs;
   float eps;

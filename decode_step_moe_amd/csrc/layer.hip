@@ -90,6 +90,8 @@ struct Scratch {
   int *n_q = nullptr;            // [2]
   float *gu_part = nullptr;      // routed group slots, then shared group slots
   unsigned *gu_cnt = nullptr;    // routed group counters, then shared group counters
+  float *dn_part = nullptr;      // [H/64][dn slots][64][64] partial y tiles
+  unsigned *dn_cnt = nullptr;    // [H/64]
 };
 
 // Batched gate/up matrix-core groups: 16-token chunks of the routed experts
@@ -105,7 +107,7 @@ size_t gu_groups_shared(const decode_layer_config &c) {
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-constexpr int kNumBuf = 27;
+constexpr int kNumBuf = 29;
 struct Layout {
   size_t off[kNumBuf];
   size_t total;
@@ -128,7 +130,8 @@ Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
       (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2,
       Bb ? 4 * E * 4 : size_t(0), Bb ? size_t(8) : size_t(0),
       Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * batch_gu_chunks(c.hidden) * kGuSlotFloatsR * 4 : size_t(0),
-      Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * 4 : size_t(0)};
+      Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * 4 : size_t(0),
+      Bb ? (H / 64) * batch_dn_slots(c.hidden) * kMaxBatch * 64 * 4 : size_t(0), Bb ? (H / 64) * 4 : size_t(0)};
   Layout L;
   size_t o = 0;
   for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
@@ -348,6 +351,8 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
   h->s.n_q = (int *)(b + L.off[24]);
   h->s.gu_part = (float *)(b + L.off[25]);
   h->s.gu_cnt = (unsigned *)(b + L.off[26]);
+  h->s.dn_part = (float *)(b + L.off[27]);
+  h->s.dn_cnt = (unsigned *)(b + L.off[28]);
   h->gu_grid = 2 * std::max(1, cu_count(device));
   // The hand-off counters start at zero and are re-armed by the kernels
   // themselves, and the tagged hand-off values start with tag 0, which no
@@ -483,6 +488,9 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
     ba.gu_cnt = h->s.gu_cnt;
     ba.gu_cnt_s = h->s.gu_cnt + gu_groups_routed(c);
     ba.gu_grid = h->gu_grid;
+    ba.dn_part = h->s.dn_part;
+    ba.dn_cnt = h->s.dn_cnt;
+    ba.dn_slots = batch_dn_slots(c.hidden);
     ba.counter = h->s.counters + 2;
     ba.B = B;
     ba.H = c.hidden;

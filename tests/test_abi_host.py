@@ -99,7 +99,8 @@ def test_batched_scratch_follows_the_path():
     chunks = (H // 32 + 13) // 14             # K chunks of 14 steps of 32: one partial slot each
     batched = (_a256(4 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
                + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(8)
-               + _a256((groups_r + groups_s) * chunks * 2048 * 4) + _a256((groups_r + groups_s) * 4))
+               + _a256((groups_r + groups_s) * chunks * 2048 * 4) + _a256((groups_r + groups_s) * 4)
+               + _a256((H // 64) * (-(-512 // (H // 64)) + 2) * 64 * 64 * 4) + _a256((H // 64) * 4))
     auto = dl.scratch_bytes(c, 256)
     c.path = dl.DL_PATH_MULTI
     multi = dl.scratch_bytes(c, 256)
