@@ -68,10 +68,8 @@ def algorithmic_bytes(layer) -> dict:
     weights = 2 * (Dq * H + H * Do + H) + 4 * E * H + n_act * 3 * 2 * F * H + 3 * 2 * Fs * H
     io = 2 * B * (H + Do) + 4 * B * H * 2 + 4 * B * Dq + 4 * B * E + 8 * pairs + 4 * B * H
     b["step"] = weights + io
-    # the single-launch kernel does all but the attention input projection,
-    # which runs beside it on the second stream
-    b["qkv_side"] = 2 * Dq * H + 2 * B * H + 4 * B * Dq
-    b["single_launch_step"] = b["step"] - b["qkv_side"]
+    # the single-launch kernel does the whole step
+    b["single_launch_step"] = b["step"]
     b["batched_proj"] = 2 * (Dq * H + H * Do + H) + 2 * B * (H + Do) + 4 * B * H * 3
     b["batched_router"] = 4 * E * H + 4 * B * H + 4 * B * Dq
     b["batched_topk_permute"] = 4 * B * H * 2 + 4 * B * E + 8 * pairs

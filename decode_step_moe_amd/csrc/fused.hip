@@ -28,7 +28,11 @@
 //     with h = hg / rms read back from global memory:
 //     l[t, e] = h[t] . Wr[e] -> published;
 //     a_s[t, f] = silu(S1[f] . h[t]) * (S3[f] . h[t]) -> published.
-//  C  every workgroup reads all logits and takes the same top-k decision
+//  C  (while the control waves gather the logits, the stream waves compute
+//     this workgroup's rows of the attention input projection qkv = x Wqkv^T,
+//     which depends on nothing else and so fills that hand-off's idle HBM
+//     time — the role the pages give a side stream, bullets 1 and 3)
+//     every workgroup reads all logits and takes the same top-k decision
 //     (descending logit, ties to the lower expert id; s = sigmoid(l),
 //     w = s / sum s over the k picks), builds the same per-expert token lists
 //     in LDS, then computes its share of the routed gate/up rows:
@@ -173,6 +177,7 @@ struct Lds {
   int part_lt[kFWaves][kWave];
   int part_same[kFWaves][kWave];
   float sqw[kFWaves][kFusedMaxB];  // per-wave partial sums of r1^2
+  float qkvp[kStr / kWave][kFusedQkvRows][kFusedMaxB];  // input-projection partial sums per stream wave
   int arrive;
   int bad;
 };
@@ -398,6 +403,30 @@ __device__ __forceinline__ void by_lpg(int F, Fn fn) {
 
 }  // namespace
 
+// ---- phase C, stream waves: the attention input projection ------------------
+// It depends on nothing else in the step, so it fills the logits hand-off:
+// this workgroup's rows are j = w + G q (q < kFusedQkvRows), taken two at a
+// time; stream wave sw covers the quarter sw of K.  The four partial sums of
+// a row are added in wave order after the phase's barrier.
+template <int NT>
+__device__ void qkv_rows(const FusedArgs &a, Lds &L, int w, int G) {
+  constexpr int CPB = NT >= 4 ? 2 : 4;
+  const int sw = (threadIdx.x - kCtl) >> 6, lane = threadIdx.x & 63;
+  const int nc = a.H >> 3, cb = sw * nc / 4, ce = (sw + 1) * nc / 4;
+  const ActBf16Rows act{a.x, a.H, a.B - 1};
+  for (int q = 0; q < kFusedQkvRows && w + G * q < a.Dq; q += 2) {
+    const int j0 = w + G * q, j1 = min(j0 + G, a.Dq - 1);
+    const uint16_t *row[2] = {a.w_qkv + (size_t)j0 * a.H, a.w_qkv + (size_t)j1 * a.H};
+    float s[2][NT];
+    wave_rows_dot<2, NT, CPB>(row, cb, ce, act, s);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (lane == t && q + r < kFusedQkvRows) L.qkvp[sw][q + r][t] = s[r][t];
+  }
+}
+
 __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   __shared__ Lds L;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -597,8 +626,14 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
 
   // ================= phase C =================
   if (ctl) gather_tagged(a.logit, L.u.logits, tid, kCtl, B * E, tag, a.spin_limit, &L.bad);
+  else by_tokens(B, [&](auto nt) { qkv_rows<decltype(nt)::value>(a, L, w, G); });
   __syncthreads();
   stamp(a, 7);
+  for (int q = tid; q < kFusedQkvRows * B; q += kFT) {
+    const int r = q / B, t = q % B, j = w + G * r;
+    if (j < a.Dq)
+      a.qkv[(size_t)t * a.Dq + j] = ((L.qkvp[0][r][t] + L.qkvp[1][r][t]) + L.qkvp[2][r][t]) + L.qkvp[3][r][t];
+  }
   // top-k per token, one wave per token: lane l holds experts l, l+64, ...
   for (int t = wv; t < B; t += kFWaves) {
     constexpr int NC = kFusedMaxE / 64;
@@ -786,35 +821,6 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     if (L.bad) atomicOr(a.status, 1u);
     if (w == 0) *a.epoch = tag;   // every workgroup has read this step's epoch (all pss seen)
   }
-}
-
-// The attention input projection of the single-launch path, as its own small
-// kernel on the handle's second stream: it depends on nothing else in the
-// step, uses the registers and LDS the persistent kernel leaves free on each
-// CU, and fills HBM time the persistent kernel spends waiting on hand-offs
-// (wireai.ir, "Four key changes behind the jump": the small-batch
-// projection of bullet 1, run on a side stream as bullet 3 runs the shared
-// expert).
-// One wave per row of Wqkv.
-template <int NT>
-__global__ void __launch_bounds__(64) qkv_side_kernel(FusedArgs a) {
-  const int j = blockIdx.x, lane = threadIdx.x;
-  const ActBf16Rows act{a.x, a.H, a.B - 1};
-  const uint16_t *row[1] = {a.w_qkv + (size_t)j * a.H};
-  float s[1][NT];
-  wave_rows_dot<1, NT, (NT >= 8 ? 2 : 4)>(row, 0, a.H >> 3, act, s);
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-    if (lane == t && t < a.B) a.qkv[(size_t)t * a.Dq + j] = s[0][t];
-}
-
-hipError_t launch_qkv_side(const FusedArgs &a, hipStream_t s) {
-  const dim3 grid(a.Dq), block(64);
-  if (a.B <= 1) hipLaunchKernelGGL(qkv_side_kernel<1>, grid, block, 0, s, a);
-  else if (a.B <= 2) hipLaunchKernelGGL(qkv_side_kernel<2>, grid, block, 0, s, a);
-  else if (a.B <= 4) hipLaunchKernelGGL(qkv_side_kernel<4>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(qkv_side_kernel<8>, grid, block, 0, s, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s) {

@@ -33,6 +33,7 @@ constexpr int kFusedActS = 4096;      // B * Fs shared activations
 constexpr int kFusedMaxH = 8192;      // router / shared rows held in registers
 constexpr int kFusedMaxE = 512;       // experts (top-k candidates per lane)
 constexpr int kFusedMaxGrid = 256;    // workgroups (one poll per control thread)
+constexpr int kFusedQkvRows = 8;      // input-projection rows per workgroup
 constexpr int kFusedW2Words = 4096;   // 16-byte words of down-projection rows staged in LDS (64 KB)
 
 struct FusedArgs {
@@ -167,7 +168,6 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t s);
 hipError_t launch_gateup(const GateUpArgs &a, int grid, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s);
-hipError_t launch_qkv_side(const FusedArgs &a, hipStream_t s);
 // ev: kBatchLaunches event pairs recorded around the launches, or nullptr.
 hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]);
 // Resident workgroups of the single-launch kernel per CU (0 if it cannot run).

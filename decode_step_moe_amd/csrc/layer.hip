@@ -30,6 +30,8 @@ struct SinglePlan {
 
 int single_max_batch_for(const decode_layer_config &c, int grid, int slice) {
   if (grid < 1 || grid > kFusedMaxGrid || slice > kFusedMaxSlice) return 0;
+  // each workgroup computes at most kFusedQkvRows rows of the input projection
+  if (c.qkv_out > kFusedQkvRows * grid) return 0;
   // each workgroup holds at most 2 router rows in LDS
   if (c.hidden > kFusedMaxH || c.n_experts > kFusedMaxE || c.n_experts > 2 * grid) return 0;
   if (c.shared_ffn != 0 && c.shared_ffn != c.expert_ffn) return 0;
@@ -431,17 +433,10 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
     fa.eps = c.rms_eps;
     fa.spin_limit = 1 << 20;   // about a second of polling per wait
     fa.trace = (uint64_t *)h->trace;
-    // the attention input projection runs beside the persistent kernel on
-    // the second stream (forked from and joined back into the caller's)
-    HIP_TRY(h, hipEventRecord(h->ev_fork, st));
-    HIP_TRY(h, hipStreamWaitEvent(h->side, h->ev_fork, 0));
     ProfScope p5{h, 5, st};
     HIP_TRY(h, p5.begin());
     HIP_TRY(h, launch_fused(fa, h->single.grid, st));
     HIP_TRY(h, p5.end());
-    HIP_TRY(h, launch_qkv_side(fa, h->side));
-    HIP_TRY(h, hipEventRecord(h->ev_join, h->side));
-    HIP_TRY(h, hipStreamWaitEvent(st, h->ev_join, 0));
     if (h->profiling) h->profiled_step = true;
     return DL_OK;
   }

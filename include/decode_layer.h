@@ -76,12 +76,13 @@ enum {
  *   DL_PATH_SINGLE  the whole step in ONE launch: one workgroup per CU, all
  *                   resident, phases handing data to each other through
  *                   device memory (the shared expert's and the router's
- *                   weights stream while the norm is being exchanged).
- *                   The attention input projection runs beside it as a
- *                   small kernel on the handle's second stream.
+ *                   weights stream while the norm is being exchanged, and
+ *                   the attention input projection is computed while the
+ *                   router logits are exchanged).
  *                   Available on devices with at most 256 CUs when
  *                   hidden <= 8192 and <= 32 * CUs, n_experts <= 512 and
- *                   <= 2 * CUs, and shared_ffn == 0 or == expert_ffn; for
+ *                   <= 2 * CUs, qkv_out <= 8 * CUs, and shared_ffn == 0 or
+ *                   == expert_ffn; for
  *                   batches up to
  *                   decode_layer_single_max_batch(), which is at most 8 and
  *                   also bounded by B*k <= 64, B*E <= 8192, B*k*F <= 8192 and
@@ -166,8 +167,8 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
 
 /* Enqueue one layer-step on `hip_stream` (a hipStream_t; NULL = the null
  * stream) and return without synchronising.  Device work: on the single-launch
- * path one persistent kernel on `hip_stream` and the attention input
- * projection on the handle's second stream; on the multi-launch path up to five kernel
+ * path one persistent kernel on `hip_stream`; on the batched path five kernel
+ * launches on `hip_stream`; on the multi-launch path up to five kernel
  * launches, four on `hip_stream` and one (the shared expert's gate/up
  * projection) on the handle's second stream, which is forked from and joined
  * back into `hip_stream` with events.  Either can be captured in a HIP graph.
