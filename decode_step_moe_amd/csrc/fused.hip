@@ -548,9 +548,10 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       const int t = q / ni, il = q % ni;
       a.h_out[(size_t)t * H + i0 + il] = L.hg[t][il] * L.inv_rms[t];
     }
-  if (kind[0] || kind[1]) {  // uniform over the workgroup
+  if (kind[0] || kind[1]) by_tokens(B, [&](auto tgc) {  // uniform over the workgroup
     const int nc = H >> 3;    // 8-element chunks c = tid + kFT*j
-    constexpr int TG = 4;  // tokens whose hg chunks are requested together
+    // tokens whose hg chunks are requested together: the whole batch (up to 8)
+    constexpr int TG = decltype(tgc)::value;
     for (int t0 = 0; t0 < B; t0 += TG) {
       float4 hx[TG][kChunkJ][2];
 #pragma unroll
@@ -620,7 +621,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         put_tagged(a.act_s + (size_t)t * a.Fs + f, silu_mul(sp[0] * L.inv_rms[t], sp[1] * L.inv_rms[t]), tag);
       }
     }
-  }
+  });
   __syncthreads();   // the unit rows in LDS are dead from here on
   stamp(a, 5);
 
