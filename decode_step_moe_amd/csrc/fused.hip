@@ -300,6 +300,53 @@ __device__ void gateup_pair(const GuRow &r, const uint16_t *row1, const uint16_t
   }
 }
 
+// The same with the item's hg rows staged in LDS (hl: [cnt][H] fp32, row t
+// of token t of the item): only the weights travel from memory, 7 chunks of
+// each row per load batch.
+template <int NT>
+__device__ void gateup_pair_lds(const uint16_t *row1, const uint16_t *row3, const float *hl, int cnt, int H,
+                                int cbeg, int cend, float (&su)[NT], float (&sv)[NT]) {
+  constexpr int CPB = 7;
+  const int lane = threadIdx.x & 63;
+  float au[NT], av[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) au[t] = av[t] = 0.f;
+  for (int c0 = cbeg; c0 < cend; c0 += CPB * kWave) {
+    uint4 w1[CPB], w3[CPB];
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int cc = min(c0 + lane + kWave * u, cend - 1);
+      w1[u] = ld_stream16(row1 + (size_t)cc * 8);
+      w3[u] = ld_stream16(row3 + (size_t)cc * 8);
+    }
+    DL_SCHED_FENCE();
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int cc = min(c0 + lane + kWave * u, cend - 1);
+      const bool on = c0 + lane + kWave * u < cend;
+      float f1[8], f3[8];
+      unpack8(zero_unless(on, w1[u]), f1);
+      unpack8(zero_unless(on, w3[u]), f3);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float *hp = hl + (size_t)min(t, cnt - 1) * H + (size_t)cc * 8;
+        const float4 x0 = *reinterpret_cast<const float4 *>(hp), x1 = *reinterpret_cast<const float4 *>(hp + 4);
+        const float hv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          au[t] = fmaf(f1[e], hv[e], au[t]);
+          av[t] = fmaf(f3[e], hv[e], av[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    su[t] = wave_sum(au[t]);
+    sv[t] = wave_sum(av[t]);
+  }
+}
+
 // ---- phase D: one (item, row) unit per group of LPG lanes --------------------
 // Items 0..B-1 are the shared expert's tokens (weights S2, activations
 // act_s), items B..B+P-1 the routed pairs (weights W2 of the pair's expert,
@@ -723,39 +770,73 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   __syncthreads();
   stamp(a, 8);
   // gate/up items: routed (active slot, ffn row) pairs, then the shared
-  // expert's rows f >= fs_b that phase B did not take; workgroup w takes
-  // items w, w + G, ...  Rounds of 4 items: waves 2i and 2i + 1 take both
-  // rows (W1 and W3) of item i of the round over the two halves of K, so the
-  // item's activation loads serve both rows.
+  // expert's rows f >= fs_b that phase B did not take, in that order;
+  // workgroup w takes the contiguous run [w total / G, (w + 1) total / G),
+  // so its items are mostly rows of one expert.  Rounds of up to 4 items of
+  // one expert: waves 2i and 2i + 1 take both rows (W1 and W3) of item i of
+  // the round over the two halves of K, so the item's activation loads serve
+  // both rows.  With 8 or more items per workgroup, the hg rows of the
+  // expert's tokens are staged in LDS once per expert (when they fit) and the
+  // waves stream only weights.
   {
     const int n_rt = L.n_active * a.F;
     const int total = n_rt + (a.Fs - fs_b);
-    const int nit = w < total ? (total - w + G - 1) / G : 0;
+    const int ib = (int)((long)w * total / G), ie = (int)((long)(w + 1) * total / G);
     const int nc = H >> 3, cmid = nc >> 1;
-    for (int k0 = 0; k0 < nit; k0 += 4) {
+    const int cap = (int)(sizeof(L.u) / (4 * (size_t)H));  // tokens whose hg rows fit in LDS
+    const bool stage = ie - ib >= 8;
+    float *hl = reinterpret_cast<float *>(&L.u);
+    int staged = -2;  // token set in LDS: active slot, or -1 for the shared expert
+    for (int k0 = ib; k0 < ie;) {
+      const int sk = k0 < n_rt ? k0 / a.F : -1;
+      int kend = min(ie, k0 + 4);
+      for (int k = k0 + 1; k < kend; ++k)
+        if ((k < n_rt ? k / a.F : -1) != sk) {
+          kend = k;
+          break;
+        }
+      GuRow r;
+      r.toks = sk >= 0 ? L.pair_tok + L.act_off[sk] : nullptr;
+      r.cnt = sk >= 0 ? L.act_cnt[sk] : B;
+      const bool lds = stage && r.cnt <= cap;
+      if (lds && staged != sk) {
+        const int wpr = H >> 2, nw = r.cnt * wpr;  // 16-byte words
+        for (int q0 = tid; q0 < nw; q0 += 8 * kFT) {
+          float4 v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int q = min(q0 + kFT * j, nw - 1), t = q / wpr, c = q % wpr;
+            v[j] = ld16f(a.hg + (size_t)r.tok(t) * H + 4 * c);
+          }
+          DL_SCHED_FENCE();
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int q = q0 + kFT * j;
+            if (q < nw) *reinterpret_cast<float4 *>(hl + 4 * q) = v[j];
+          }
+        }
+        __syncthreads();
+        staged = sk;
+      }
       const int ki = k0 + (wv >> 1), hf = wv & 1;
-      if (ki < nit) {
-        const int it = w + G * ki;
-        GuRow r;
+      if (ki < kend) {
         const uint16_t *row1, *row3;
-        if (it < n_rt) {
-          const int slot = it / a.F, f = it % a.F;
-          const size_t ro = ((size_t)L.act_exp[slot] * a.F + f) * H;
+        if (ki < n_rt) {
+          const size_t ro = ((size_t)L.act_exp[sk] * a.F + ki % a.F) * H;
           row1 = a.w1 + ro;
           row3 = a.w3 + ro;
-          r.toks = L.pair_tok + L.act_off[slot];
-          r.cnt = L.act_cnt[slot];
         } else {
-          const size_t ro = (size_t)(fs_b + it - n_rt) * H;
+          const size_t ro = (size_t)(fs_b + ki - n_rt) * H;
           row1 = a.s1 + ro;
           row3 = a.s3 + ro;
-          r.toks = nullptr;
-          r.cnt = B;
         }
         by_tokens(r.cnt, [&](auto ntc) {
           constexpr int NT = decltype(ntc)::value;
           float su[NT], sv[NT];
-          gateup_pair<NT>(r, row1, row3, a.hg, H, hf ? cmid : 0, hf ? nc : cmid, su, sv);
+          if (lds)
+            gateup_pair_lds<NT>(row1, row3, hl, r.cnt, H, hf ? cmid : 0, hf ? nc : cmid, su, sv);
+          else
+            gateup_pair<NT>(r, row1, row3, a.hg, H, hf ? cmid : 0, hf ? nc : cmid, su, sv);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             if (lane == t) {
@@ -768,13 +849,13 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       __syncthreads();
       // combine: thread (item-in-round is, token j)
       const int is = tid >> 3, j = tid & 7;
-      if (is < 4 && k0 + is < nit) {
-        const int it = w + G * (k0 + is);
+      if (is < kend - k0) {
+        const int it = k0 + is;
         const float su = L.uv[is][0][0][j] + L.uv[is][1][0][j];
         const float sv = L.uv[is][0][1][j] + L.uv[is][1][1][j];
         if (it < n_rt) {
-          const int s2 = it / a.F, f2 = it % a.F;
-          const int c2 = L.act_cnt[s2], o2 = L.act_off[s2];
+          const int f2 = it % a.F;
+          const int c2 = L.act_cnt[sk], o2 = L.act_off[sk];
           if (j < c2) {
             const int t = L.pair_tok[o2 + j];
             put_tagged(a.act + (size_t)(o2 + j) * a.F + f2, silu_mul(su * L.inv_rms[t], sv * L.inv_rms[t]), tag);
@@ -785,6 +866,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         }
       }
       __syncthreads();
+      k0 = kend;
     }
   }
   stamp(a, 9);
