@@ -13,11 +13,11 @@
 // and norm, router before the shared and routed experts).
 //
 // Launches (all on the caller's stream; data passes through L2/HBM):
-//  1 proj_b    Wo tiles of 16 rows, K = Do split over the 4 waves:
+//  1 proj_b    64 rows of Wo per workgroup, K = Do split over the 4 waves:
 //                r1 = r + attn Wo^T -> resid_out, hg = g r1, per-workgroup
 //                sums of r1^2.
-//              Wqkv tiles of 16 rows, K = H split over 4 workgroups x 4 waves:
-//                partial qkv sums.
+//              64 rows of Wqkv per workgroup, K = H split over 8 workgroups
+//                (4 when H % 1024 != 0) x 4 waves: partial qkv sums.
 //  2 router_b  fp32 router dot products d[t, e] = hg[t] . Wr[e] on MFMA
 //              (v_mfma_f32_16x16x4_f32), 32 experts x 256 K per workgroup;
 //              also sums the qkv partials (fixed order) -> qkv.
@@ -132,67 +132,122 @@ __device__ __forceinline__ void by_chunks(int nc, Fn fn) {
 }
 
 // ================================================================ launch 1
-// red[w][token][n]: wave w's share of output (token, row r0 + n).
+// NR row tiles x NC 16-token chunks per wave, K split over the waves: per K
+// step a wave loads NR weight fragments and NC activation fragments and
+// runs NR * NC matrix-core steps, so a workgroup reads as many activation
+// bytes as weight bytes (with 16-row tiles per workgroup it read NC times
+// more).  U K steps of loads per batch; the K steps of the last batch beyond
+// nks re-read step nks-1 and multiply zero weights.
+template <int NR, int NC, int U>
+__device__ __forceinline__ void mfma_tiles(const uint16_t *const (&wp)[NR], const uint16_t *const (&ap)[NC], int nks,
+                                           f32x4 (&acc)[NR][NC]) {
+  for (int ks = 0; ks < nks; ks += U) {
+    uint4 wv[U][NR], av[U][NC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = min(ks + u, nks - 1) * 32;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) wv[u][r] = ld16(wp[r] + k);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) av[u][c] = ld16(ap[c] + k);
+    }
+    DL_SCHED_FENCE();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint4 w = zero_unless(ks + u < nks, wv[u][r]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[r][c] = mfma_bf16(av[u][c], w, acc[r][c]);
+      }
+  }
+}
+
+// Workgroup: kProjRows rows of Wo (blocks < n_wo; K = Do split over the 4
+// waves) or of Wqkv (K = H split over qkv_split workgroups x 4 waves).
+// red[w][token][row]: wave w's partial sum.
+constexpr int kProjRows = 64;
 __global__ void __launch_bounds__(kBlock) proj_b(BatchArgs a, int n_wo) {
-  __shared__ float red[kWavesPerBlock][kMaxBatch][16];
-  __shared__ float sq[kMaxBatch][16];
+  __shared__ float red[kWavesPerBlock][kMaxBatch][kProjRows];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int B = a.B;
   const bool wo = (int)blockIdx.x < n_wo;
-  int r0, split = 0, nks, ld;
-  const uint16_t *wp, *abase;
+  int r0, split = 0, nks, ld, nrow;
+  const uint16_t *wbase, *abase;
+  size_t wld;
   if (wo) {
-    r0 = blockIdx.x * 16;
+    r0 = blockIdx.x * kProjRows;
     const int kw = wv * (a.Do / 4) + 8 * g;
-    wp = a.w_o + (size_t)(r0 + n) * a.Do + kw;
+    wbase = a.w_o + kw;
+    wld = a.Do;
     abase = a.attn + kw;
     ld = a.Do;
     nks = a.Do / 128;
+    nrow = a.H;
   } else {
-    const int b = blockIdx.x - n_wo;
-    r0 = (b / kBatchQkvSplit) * 16;
-    split = b % kBatchQkvSplit;
-    const int kq = a.H / (kBatchQkvSplit * kWavesPerBlock);
-    const int kw = split * (a.H / kBatchQkvSplit) + wv * kq + 8 * g;
-    wp = a.w_qkv + (size_t)min(r0 + n, a.Dq - 1) * a.H + kw;
+    const int b = blockIdx.x - n_wo, S = a.qkv_split;
+    r0 = (b / S) * kProjRows;
+    split = b % S;
+    const int kq = a.H / (S * kWavesPerBlock);
+    const int kw = split * (a.H / S) + wv * kq + 8 * g;
+    wbase = a.w_qkv + kw;
+    wld = a.H;
     abase = a.x + kw;
     ld = a.H;
     nks = kq / 32;
+    nrow = a.Dq;
   }
+  // the residual rows of this workgroup's tokens, requested before the
+  // weights so the epilogue does not wait on a load per token
+  constexpr int TPW = kMaxBatch / kWavesPerBlock;  // tokens per wave in the epilogue
+  float rin[TPW];
+  if (wo) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) rin[j] = a.resid_in[(size_t)min(wv + kWavesPerBlock * j, B - 1) * a.H + r0 + lane];
+  }
+  constexpr int NR = kProjRows / 16;
+  const uint16_t *wp[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) wp[r] = wbase + (size_t)min(r0 + 16 * r + n, nrow - 1) * wld;
   by_chunks((B + 15) >> 4, [&](auto ncc) {
     constexpr int NC = decltype(ncc)::value;
     const uint16_t *ap[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) ap[c] = abase + (size_t)min(16 * c + n, B - 1) * ld;
-    f32x4 acc[NC];
+    f32x4 acc[NR][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_rows<NC, (NC <= 2 ? 8 : 4)>(wp, ap, nks, acc);
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+      for (int c = 0; c < NC; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_tiles<NR, NC, 4>(wp, ap, nks, acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wv][16 * c + 4 * g + i][n] = acc[c][i];
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wv][16 * c + 4 * g + i][16 * r + n] = acc[r][c][i];
   });
   __syncthreads();
   if (wo) {
-    for (int q = tid; q < B * 16; q += kBlock) {
-      const int t = q >> 4, nn = q & 15, i = r0 + nn;
-      const float s = ((red[0][t][nn] + red[1][t][nn]) + red[2][t][nn]) + red[3][t][nn];
-      const size_t o = (size_t)t * a.H + i;
-      const float r1 = a.resid_in[o] + s;
-      a.resid_out[o] = r1;
-      a.hg[o] = bf16_lo(a.gain[i]) * r1;
-      sq[t][nn] = r1 * r1;
-    }
-    __syncthreads();
-    if (tid < B) {
-      float s = 0.f;
-      for (int nn = 0; nn < 16; ++nn) s += sq[tid][nn];
-      a.ss_part[(size_t)blockIdx.x * B + tid] = s;
+    // wave wv takes token 4j + wv with its 64 rows in the lanes
+    const int i = r0 + lane;
+    const float gi = bf16_lo(a.gain[i]);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wv + kWavesPerBlock * j;
+      if (t < B) {
+        const float s = ((red[0][t][lane] + red[1][t][lane]) + red[2][t][lane]) + red[3][t][lane];
+        const size_t o = (size_t)t * a.H + i;
+        const float r1 = rin[j] + s;
+        a.resid_out[o] = r1;
+        a.hg[o] = gi * r1;
+        const float sq = wave_sum(r1 * r1);
+        if (lane == 0) a.ss_part[(size_t)blockIdx.x * B + t] = sq;
+      }
     }
   } else {
-    for (int q = tid; q < B * 16; q += kBlock) {
-      const int t = q >> 4, nn = q & 15, j = r0 + nn;
+    for (int q = tid; q < B * kProjRows; q += kBlock) {
+      const int t = q / kProjRows, nn = q % kProjRows, j = r0 + nn;
       if (j < a.Dq)
         a.qkv_part[((size_t)split * B + t) * a.Dq + j] =
             ((red[0][t][nn] + red[1][t][nn]) + red[2][t][nn]) + red[3][t][nn];
@@ -265,7 +320,9 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
   const size_t nq = (size_t)B * a.Dq, plane = nq;
   for (size_t q = (size_t)bl * kBlock + tid; q < nq; q += (size_t)nblk * kBlock) {
     const float *p = a.qkv_part + q;
-    a.qkv[q] = ((p[0] + p[plane]) + p[2 * plane]) + p[3 * plane];
+    float v = p[0];
+    for (int sp = 1; sp < a.qkv_split; ++sp) v += p[sp * plane];
+    a.qkv[q] = v;
   }
 }
 
@@ -1011,8 +1068,8 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
 }  // namespace
 
 hipError_t launch_batched(const BatchArgs &a, hipStream_t s, hipEvent_t (*ev)[2]) {
-  const int n_wo = a.H / 16;
-  const int n_q = (a.Dq + 15) / 16 * kBatchQkvSplit;
+  const int n_wo = a.H / kProjRows;
+  const int n_q = (a.Dq + kProjRows - 1) / kProjRows * a.qkv_split;
   const int n_rk = a.H / kBatchRtrK;
   hipError_t e;
   auto rec = [&](int i, int j) { return ev ? hipEventRecord(ev[i][j], s) : hipSuccess; };

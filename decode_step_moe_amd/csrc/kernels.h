@@ -67,7 +67,7 @@ constexpr int kTracePoints = 16;
 // Batched path (batched.hip): five launches for batches the single-launch
 // path does not take (up to 64 tokens); MFMA wherever 16 or more tokens share
 // a weight matrix.  Needs H % 512 == 0 and Do % 128 == 0.
-constexpr int kBatchQkvSplit = 4;     // K splits of the attention input projection
+constexpr int kBatchQkvSplit = 8;     // K splits of the attention input projection (at most)
 constexpr int kBatchRtrExperts = 32;  // router experts per workgroup
 constexpr int kBatchRtrK = 256;       // router K per workgroup
 constexpr int kBatchMfmaMin = 16;     // an expert with at least this many tokens uses MFMA
@@ -96,8 +96,8 @@ struct BatchArgs {
   float *moe_out, *h_out;
   // scratch
   float *hg;          // [B][H]        g * r1
-  float *ss_part;     // [H/16][B]     partial sums of r1^2 per out-projection workgroup
-  float *qkv_part;    // [kBatchQkvSplit][B][Dq]
+  float *ss_part;     // [H/64][B]     partial sums of r1^2 per out-projection workgroup
+  float *qkv_part;    // [qkv_split][B][Dq]
   float *rlog_part;   // [H/kBatchRtrK][B][E]  router dot products per K chunk
   float *hn;          // [B][H]        normalised h (fp32)
   uint16_t *hp;       // [2][B][H]     h as bf16 hi + lo planes (MFMA operands)
@@ -120,6 +120,7 @@ struct BatchArgs {
   int dn_slots;       // batch_dn_slots(H)
   unsigned *counter;  // [1] arrivals of the top-k workgroups (re-armed by the last)
   int B, H, Dq, Do, E, K, F, Fs;
+  int qkv_split;      // K splits of the input projection: 8 when H % 1024 == 0, else 4
   float eps;
 };
 

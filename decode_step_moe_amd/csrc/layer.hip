@@ -483,6 +483,7 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
     ba.gu_cnt = h->s.gu_cnt;
     ba.gu_cnt_s = h->s.gu_cnt + gu_groups_routed(c);
     ba.gu_grid = h->gu_grid;
+    ba.qkv_split = c.hidden % 1024 == 0 ? kBatchQkvSplit : kBatchQkvSplit / 2;
     ba.dn_part = h->s.dn_part;
     ba.dn_cnt = h->s.dn_cnt;
     ba.dn_slots = batch_dn_slots(c.hidden);

@@ -97,7 +97,7 @@ def test_batched_scratch_follows_the_path():
     groups_r = (B * 8 + 7) // 8 * (F // 64)   # gate/up groups: B*k/8 16-token chunks x 64-row groups
     groups_s = (B + 15) // 16 * (Fs // 64)    # shared expert: 16-token chunks x 64-row groups
     chunks = (H // 32 + 13) // 14             # K chunks of 14 steps of 32: one partial slot each
-    batched = (_a256(4 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
+    batched = (_a256(8 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
                + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(8)
                + _a256((groups_r + groups_s) * chunks * 2048 * 4) + _a256((groups_r + groups_s) * 4)
                + _a256((H // 64) * (-(-512 // (H // 64)) + 2) * 64 * 64 * 4) + _a256((H // 64) * 4))
