@@ -337,6 +337,18 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __shared__ int last_flag;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int B = a.B, H = a.H, E = a.E, K = a.K, t = blockIdx.x;
+  // every load of the token's hg row is requested together with the norm's
+  // partial sums (one round trip instead of one per loop pass)
+  constexpr int HJ = 16384 / (kBlock * 8);  // 8-element chunks per thread (H <= 16384)
+  float4 hx[HJ][2];
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    const int i = tid * 8 + kBlock * 8 * j;
+    if (i < H) {
+      hx[j][0] = ld16f(a.hg + (size_t)t * H + i);
+      hx[j][1] = ld16f(a.hg + (size_t)t * H + i + 4);
+    }
+  }
   // 1/rms from the out-projection workgroups' partial sums
   float ss = 0.f;
   for (int q = tid; q < n_ow; q += kBlock) ss += a.ss_part[(size_t)q * B + t];
@@ -345,12 +357,14 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __syncthreads();
   const float inv = 1.0f / sqrtf(((wred[0] + wred[1]) + (wred[2] + wred[3])) / (float)H + a.eps);
   // h = hg / rms: fp32 copy, optional output, bf16 hi/lo planes
-  for (int i = tid * 8; i < H; i += kBlock * 8) {
-    const size_t o = (size_t)t * H + i;
-    float x[8];
-    load8f(a.hg + o, x);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] *= inv;
+  for (int j = 0; j < HJ; ++j) {
+    const int i = tid * 8 + kBlock * 8 * j;
+    if (i >= H) break;
+    const size_t o = (size_t)t * H + i;
+    float x[8] = {hx[j][0].x, hx[j][0].y, hx[j][0].z, hx[j][0].w, hx[j][1].x, hx[j][1].y, hx[j][1].z, hx[j][1].w};
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) x[jj] *= inv;
     const float4 u = make_float4(x[0], x[1], x[2], x[3]), v = make_float4(x[4], x[5], x[6], x[7]);
     *reinterpret_cast<float4 *>(a.hn + o) = u;
     *reinterpret_cast<float4 *>(a.hn + o + 4) = v;
@@ -368,12 +382,12 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
     float d = 0.f;
     const float *p = a.rlog_part + (size_t)t * E + e;
     const size_t stride = (size_t)B * E;
-    for (int ky0 = 0; ky0 < n_rk; ky0 += 8) {  // 8 independent loads per batch
-      float v[8];
+    for (int ky0 = 0; ky0 < n_rk; ky0 += 32) {  // 32 independent loads per batch
+      float v[32];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = p[min(ky0 + j, n_rk - 1) * stride];
+      for (int j = 0; j < 32; ++j) v[j] = p[min(ky0 + j, n_rk - 1) * stride];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) d += ky0 + j < n_rk ? v[j] : 0.f;
+      for (int j = 0; j < 32; ++j) d += ky0 + j < n_rk ? v[j] : 0.f;
     }
     const float l = d * inv;
     lg[e] = l;

@@ -770,43 +770,68 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   __syncthreads();
   stamp(a, 8);
   // gate/up items: routed (active slot, ffn row) pairs, then the shared
-  // expert's rows f >= fs_b that phase B did not take, in that order;
-  // workgroup w takes the contiguous run [w total / G, (w + 1) total / G),
-  // so its items are mostly rows of one expert.  Rounds of up to 4 items of
-  // one expert: waves 2i and 2i + 1 take both rows (W1 and W3) of item i of
-  // the round over the two halves of K, so the item's activation loads serve
-  // both rows.  With 8 or more items per workgroup, the hg rows of the
-  // expert's tokens are staged in LDS once per expert (when they fit) and the
-  // waves stream only weights.
+  // expert's rows f >= fs_b that phase B did not take, in that order.  An
+  // item costs 1, plus its token count when the hg rows of its tokens do not
+  // fit in LDS (its activations then travel with its weights); workgroup w
+  // takes the items whose cost prefix lies in [w C / G, (w + 1) C / G), a
+  // contiguous run of about equal cost, mostly rows of one expert.  With 8 or
+  // more items in its run a workgroup stages the hg rows of each expert's
+  // tokens in LDS once (when they fit) and its waves stream only weights.
+  // Rounds of up to 4 items: waves 2i and 2i + 1 take both rows (W1 and W3)
+  // of item i of the round over the two halves of K, so the item's
+  // activation loads serve both rows.
   {
     const int n_rt = L.n_active * a.F;
     const int total = n_rt + (a.Fs - fs_b);
-    const int ib = (int)((long)w * total / G), ie = (int)((long)(w + 1) * total / G);
     const int nc = H >> 3, cmid = nc >> 1;
     const int cap = (int)(sizeof(L.u) / (4 * (size_t)H));  // tokens whose hg rows fit in LDS
-    const bool stage = ie - ib >= 8;
+    // per-slot item cost and its exclusive prefix over the slots (n_active <= 64 lanes)
+    const int ns = L.n_active;
+    const int cl = lane < ns ? 1 + (L.act_cnt[lane] > cap ? L.act_cnt[lane] : 0) : 0;
+    int incl = cl * a.F;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += v;
+    }
+    const int excl = incl - cl * a.F;
+    const int c_rt = __shfl(incl, kWave - 1, kWave);
+    const int c_sh = 1 + (B > cap ? B : 0);
+    const long C = c_rt + (long)(a.Fs - fs_b) * c_sh;
+    // the first item whose cost prefix is >= x
+    auto first_item = [&](long x) -> int {
+      if (x >= C) return total;
+      if (x >= c_rt) return n_rt + (int)((x - c_rt + c_sh - 1) / c_sh);
+      const int sl = __popcll(__ballot(lane < ns && excl <= x)) - 1;
+      const int es = __shfl(excl, sl, kWave), cs = __shfl(cl, sl, kWave);
+      return sl * a.F + (int)((x - es + cs - 1) / cs);
+    };
+    const int kb = first_item((long)w * C / G), ke = first_item((long)(w + 1) * C / G);
+    const bool stage = ke - kb >= 8;
     float *hl = reinterpret_cast<float *>(&L.u);
     int staged = -2;  // token set in LDS: active slot, or -1 for the shared expert
-    for (int k0 = ib; k0 < ie;) {
-      const int sk = k0 < n_rt ? k0 / a.F : -1;
-      int kend = min(ie, k0 + 4);
-      for (int k = k0 + 1; k < kend; ++k)
-        if ((k < n_rt ? k / a.F : -1) != sk) {
-          kend = k;
-          break;
-        }
-      GuRow r;
-      r.toks = sk >= 0 ? L.pair_tok + L.act_off[sk] : nullptr;
-      r.cnt = sk >= 0 ? L.act_cnt[sk] : B;
-      const bool lds = stage && r.cnt <= cap;
-      if (lds && staged != sk) {
-        const int wpr = H >> 2, nw = r.cnt * wpr;  // 16-byte words
+    auto set_of = [&](int it) { return it < n_rt ? it / a.F : -1; };
+    for (int k0 = kb; k0 < ke;) {
+      const int sk0 = set_of(k0);
+      int kend = min(ke, k0 + 4);
+      if (stage)  // a staged round holds one expert's items
+        for (int k = k0 + 1; k < kend; ++k)
+          if (set_of(k) != sk0) {
+            kend = k;
+            break;
+          }
+      const int cnt0 = sk0 >= 0 ? L.act_cnt[sk0] : B;
+      const bool lds = stage && cnt0 <= cap;  // this round's activations come from LDS
+      if (lds && staged != sk0) {
+        GuRow r0;
+        r0.toks = sk0 >= 0 ? L.pair_tok + L.act_off[sk0] : nullptr;
+        r0.cnt = cnt0;
+        const int wpr = H >> 2, nw = r0.cnt * wpr;  // 16-byte words
         for (int q0 = tid; q0 < nw; q0 += 8 * kFT) {
           float4 v[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int q = min(q0 + kFT * j, nw - 1), t = q / wpr, c = q % wpr;
-            v[j] = ld16f(a.hg + (size_t)r.tok(t) * H + 4 * c);
+            v[j] = ld16f(a.hg + (size_t)r0.tok(t) * H + 4 * c);
           }
           DL_SCHED_FENCE();
 #pragma unroll
@@ -816,19 +841,25 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
           }
         }
         __syncthreads();
-        staged = sk;
+        staged = sk0;
       }
       const int ki = k0 + (wv >> 1), hf = wv & 1;
       if (ki < kend) {
+        const int it = ki, sk = set_of(it);
+        GuRow r;
         const uint16_t *row1, *row3;
-        if (ki < n_rt) {
-          const size_t ro = ((size_t)L.act_exp[sk] * a.F + ki % a.F) * H;
+        if (sk >= 0) {
+          const size_t ro = ((size_t)L.act_exp[sk] * a.F + it % a.F) * H;
           row1 = a.w1 + ro;
           row3 = a.w3 + ro;
+          r.toks = L.pair_tok + L.act_off[sk];
+          r.cnt = L.act_cnt[sk];
         } else {
-          const size_t ro = (size_t)(fs_b + ki - n_rt) * H;
+          const size_t ro = (size_t)(fs_b + it - n_rt) * H;
           row1 = a.s1 + ro;
           row3 = a.s3 + ro;
+          r.toks = nullptr;
+          r.cnt = B;
         }
         by_tokens(r.cnt, [&](auto ntc) {
           constexpr int NT = decltype(ntc)::value;
@@ -850,10 +881,10 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       // combine: thread (item-in-round is, token j)
       const int is = tid >> 3, j = tid & 7;
       if (is < kend - k0) {
-        const int it = k0 + is;
+        const int it = k0 + is, sk = set_of(it);
         const float su = L.uv[is][0][0][j] + L.uv[is][1][0][j];
         const float sv = L.uv[is][0][1][j] + L.uv[is][1][1][j];
-        if (it < n_rt) {
+        if (sk >= 0) {
           const int f2 = it % a.F;
           const int c2 = L.act_cnt[sk], o2 = L.act_off[sk];
           if (j < c2) {
