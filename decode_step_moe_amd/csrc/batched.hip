@@ -261,21 +261,22 @@ __global__ void __launch_bounds__(kBlock) proj_b(BatchArgs a, int n_wo) {
 // reads 4 consecutive fp32 values: at sub-step s, MFMA K index g stands for
 // k = kb + 4g + s.
 __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
-  __shared__ float red[kWavesPerBlock][4 * 2 * 256];  // [wave][chunk][tile][m * 16 + n]
+  constexpr int NT = kBatchRtrExperts / 16;  // expert tiles per workgroup
+  __shared__ float red[kWavesPerBlock][4 * NT * 256];  // [wave][chunk][tile][m * 16 + n]
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int B = a.B, H = a.H, E = a.E;
   const int e0 = blockIdx.x * kBatchRtrExperts, ky = blockIdx.y;
   const int kb = ky * kBatchRtrK + wv * (kBatchRtrK / kWavesPerBlock) + 4 * g;
-  const float *w0 = a.w_router + (size_t)min(e0 + n, E - 1) * H + kb;
-  const float *w1 = a.w_router + (size_t)min(e0 + 16 + n, E - 1) * H + kb;
+  const float *wrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) wrow[nt] = a.w_router + (size_t)min(e0 + 16 * nt + n, E - 1) * H + kb;
   by_chunks((B + 15) >> 4, [&](auto ncc) {
     constexpr int NC = decltype(ncc)::value;
-    float4 b0[4], b1[4], av[4][NC];
+    float4 bw[4][NT], av[4][NC];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      b0[it] = ld16f(w0 + 16 * it);
-      b1[it] = ld16f(w1 + 16 * it);
-    }
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bw[it][nt] = ld16f(wrow[nt] + 16 * it);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const float *ap = a.hg + (size_t)min(16 * c + n, B - 1) * H + kb;
@@ -283,34 +284,34 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
       for (int it = 0; it < 4; ++it) av[it][c] = ld16f(ap + 16 * it);
     }
     DL_SCHED_FENCE();
-    f32x4 acc[NC][2];
+    f32x4 acc[NC][NT];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const float wa[4] = {b0[it].x, b0[it].y, b0[it].z, b0[it].w};
-      const float wb[4] = {b1[it].x, b1[it].y, b1[it].z, b1[it].w};
+      for (int nt = 0; nt < NT; ++nt) acc[c][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const float x[4] = {av[it][c].x, av[it][c].y, av[it][c].z, av[it][c].w};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          acc[c][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], wa[s], acc[c][0], 0, 0, 0);
-          acc[c][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], wb[s], acc[c][1], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          const float w4[4] = {bw[it][nt].x, bw[it][nt].y, bw[it][nt].z, bw[it][nt].w};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc[c][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], w4[s], acc[c][nt], 0, 0, 0);
         }
       }
-    }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wv][(c * 2 + nt) * 256 + (4 * g + i) * 16 + n] = acc[c][nt][i];
+        for (int i = 0; i < 4; ++i) red[wv][(c * NT + nt) * 256 + (4 * g + i) * 16 + n] = acc[c][nt][i];
   });
   __syncthreads();
   for (int q = tid; q < B * kBatchRtrExperts; q += kBlock) {
-    const int t = q >> 5, el = q & 31;
-    const int idx = ((t >> 4) * 2 + (el >> 4)) * 256 + (t & 15) * 16 + (el & 15);
+    const int t = q / kBatchRtrExperts, el = q % kBatchRtrExperts;
+    const int idx = ((t >> 4) * NT + (el >> 4)) * 256 + (t & 15) * 16 + (el & 15);
     if (e0 + el < E)
       a.rlog_part[((size_t)ky * B + t) * E + e0 + el] =
           ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx];
@@ -320,8 +321,13 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
   const size_t nq = (size_t)B * a.Dq, plane = nq;
   for (size_t q = (size_t)bl * kBlock + tid; q < nq; q += (size_t)nblk * kBlock) {
     const float *p = a.qkv_part + q;
-    float v = p[0];
-    for (int sp = 1; sp < a.qkv_split; ++sp) v += p[sp * plane];
+    float pv[kBatchQkvSplit];  // every split's load issued before the sum
+#pragma unroll
+    for (int sp = 0; sp < kBatchQkvSplit; ++sp) pv[sp] = p[min(sp, a.qkv_split - 1) * plane];
+    float v = pv[0];
+#pragma unroll
+    for (int sp = 1; sp < kBatchQkvSplit; ++sp)
+      if (sp < a.qkv_split) v += pv[sp];
     a.qkv[q] = v;
   }
 }

@@ -68,7 +68,7 @@ constexpr int kTracePoints = 16;
 // path does not take (up to 64 tokens); MFMA wherever 16 or more tokens share
 // a weight matrix.  Needs H % 512 == 0 and Do % 128 == 0.
 constexpr int kBatchQkvSplit = 8;     // K splits of the attention input projection (at most)
-constexpr int kBatchRtrExperts = 32;  // router experts per workgroup
+constexpr int kBatchRtrExperts = 48;  // router experts per workgroup (3 tiles of 16)
 constexpr int kBatchRtrK = 256;       // router K per workgroup
 constexpr int kBatchMfmaMin = 16;     // an expert with at least this many tokens uses MFMA
 constexpr int kBatchGuRows = 64;      // gate/up rows of W1 (and of W3) per matrix-core group
