@@ -340,6 +340,8 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __shared__ unsigned msk[kMaxExperts][2];
   __shared__ int sa[kBlock], sc[kBlock];
   __shared__ int slot_nch[kMaxExperts];
+  __shared__ int s_pe[kMaxBatch * kMaxTopK];   // the last workgroup: every pick's expert
+  __shared__ float s_pw[kMaxBatch * kMaxTopK]; // and weight
   __shared__ int last_flag;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int B = a.B, H = a.H, E = a.E, K = a.K, t = blockIdx.x;
@@ -400,17 +402,24 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
     if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
   }
   __syncthreads();
-  if (wv == 0) {  // lane holds experts lane, lane + 64, ...
-    constexpr int NCAND = kMaxExperts / kWave;
-    float lv[NCAND];
-#pragma unroll
-    for (int c = 0; c < NCAND; ++c) {
-      const int e = lane + 64 * c;
-      lv[c] = e < E ? lg[e] : 0.f;
-    }
+  if (wv == 0) {  // lane holds experts lane, lane + 64, ... (as many as E needs)
     int my_idx;
     float my_l;
-    wave_topk<NCAND>(lv, E, K, my_idx, my_l);
+    auto pick = [&](auto ncc) {
+      constexpr int NCAND = decltype(ncc)::value;
+      float lv[NCAND];
+#pragma unroll
+      for (int c = 0; c < NCAND; ++c) {
+        const int e = lane + 64 * c;
+        lv[c] = e < E ? lg[e] : 0.f;
+      }
+      wave_topk<NCAND>(lv, E, K, my_idx, my_l);
+    };
+    if (E <= 128) pick(std::integral_constant<int, 2>{});
+    else if (E <= 256) pick(std::integral_constant<int, 4>{});
+    else if (E <= 384) pick(std::integral_constant<int, 6>{});
+    else if (E <= 512) pick(std::integral_constant<int, 8>{});
+    else pick(std::integral_constant<int, kMaxExperts / kWave>{});
     const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
     const float ssum = wave_sum(s);
     if (lane < K) {  // written through: the last workgroup reads them back
@@ -427,8 +436,11 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   }
   __syncthreads();
   const int P = B * K;
-  for (int i = tid; i < P; i += kBlock) {
+  for (int i = tid; i < P; i += kBlock) {  // each pick read once, kept in LDS
     const int e = __hip_atomic_load(a.topk_idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), tt = i / K;
+    const float wgt = __hip_atomic_load(a.topk_w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_pe[i] = e;
+    s_pw[i] = wgt;
     atomicAdd(&cnt[e], 1);
     atomicOr(&msk[e][tt >> 5], 1u << (tt & 31));
   }
@@ -499,12 +511,12 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __syncthreads();
   // a pair's place inside its expert = number of lower tokens with that expert
   for (int i = tid; i < P; i += kBlock) {
-    const int e = __hip_atomic_load(a.topk_idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), tt = i / K;
+    const int e = s_pe[i], tt = i / K;
     const unsigned m0 = msk[e][0], m1 = msk[e][1];
     const int r = tt < 32 ? __popc(m0 & ((1u << tt) - 1u)) : __popc(m0) + __popc(m1 & ((1u << (tt - 32)) - 1u));
     const int pos = off[e] + r;
     a.pair_tok[pos] = tt;
-    a.pair_w[pos] = __hip_atomic_load(a.topk_w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.pair_w[pos] = s_pw[i];
   }
 }
 
