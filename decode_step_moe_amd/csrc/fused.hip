@@ -684,17 +684,23 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   }
   // top-k per token, one wave per token: lane l holds experts l, l+64, ...
   for (int t = wv; t < B; t += kFWaves) {
-    constexpr int NC = kFusedMaxE / 64;
-    float lv[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int e = lane + 64 * c;
-      lv[c] = e < E ? L.u.logits[t * E + e] : 0.f;
-    }
     int my_idx;
     float my_l;
     stamp(a, 14);
-    wave_topk<NC>(lv, E, K, my_idx, my_l);
+    auto pick = [&](auto ncc) {  // as many candidates per lane as E needs
+      constexpr int NC = decltype(ncc)::value;
+      float lv[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int e = lane + 64 * c;
+        lv[c] = e < E ? L.u.logits[t * E + e] : 0.f;
+      }
+      wave_topk<NC>(lv, E, K, my_idx, my_l);
+    };
+    if (E <= 128) pick(std::integral_constant<int, 2>{});
+    else if (E <= 256) pick(std::integral_constant<int, 4>{});
+    else if (E <= 384) pick(std::integral_constant<int, 6>{});
+    else pick(std::integral_constant<int, kFusedMaxE / 64>{});
     stamp(a, 15);
     // scores of the k picks, renormalised (lane j holds pick j)
     const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
