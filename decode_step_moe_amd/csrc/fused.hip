@@ -354,6 +354,28 @@ __device__ void gateup_pair_lds(const uint16_t *row1, const uint16_t *row3, cons
 // Without a shared expert the items start at B.  Unit u = (item0 + u / ni,
 // row u % ni).  The weights of units [0, U0) are staged in LDS by the stream
 // threads while the activations are awaited; the rest are streamed.
+// A lane group walks its units with a fixed stride, so the (item, row) of
+// each is advanced by an add and one compare instead of a division by the
+// slice height.
+struct UnitWalk {
+  int item, il, dq, dr, ni;
+  // position of unit u and the increment of a stride of s units
+  __device__ UnitWalk(int u, int s, int item0, int ni_) : ni(ni_) {
+    item = item0 + u / ni;
+    il = u % ni;
+    dq = s / ni;
+    dr = s % ni;
+  }
+  __device__ void next() {
+    item += dq;
+    il += dr;
+    if (il >= ni) {
+      il -= ni;
+      ++item;
+    }
+  }
+};
+
 template <int LPG>
 struct Down {
   static constexpr int NG = kFT / LPG;  // lane groups
@@ -362,34 +384,39 @@ struct Down {
   Lds &L;
   int i0, ni, item0, n_units;
   __device__ int u0_end() const { return min(n_units, kFusedW2Words / LPG); }
-  __device__ const uint16_t *row(int u) const {
-    const int item = item0 + u / ni, il = u % ni;
+  __device__ const uint16_t *row(int item, int il) const {
     return item < a.B ? a.s2 + (size_t)(i0 + il) * a.F
                       : a.w2 + ((size_t)L.pair_exp[item - a.B] * a.H + i0 + il) * a.F;
   }
+  __device__ const uint16_t *row_of(int u) const { return row(item0 + u / ni, u % ni); }
   // stream threads: word k of the staged range is unit k / LPG, lane k % LPG
-  // (addresses clamped to the last word, so every load of the batch issues
-  // unconditionally and the batch is one memory round trip)
+  // (words past the range load the last word, so every load of the batch
+  // issues unconditionally and the batch is one memory round trip)
   __device__ void stage() const {
-    const int n = u0_end() * LPG;
+    const int ue = u0_end(), n = ue * LPG;
     if (n == 0) return;
     constexpr int J = kFusedW2Words / kStr;  // 16
+    constexpr int S = kStr / LPG;            // units between a thread's words
+    static_assert(kStr % LPG == 0, "staging stride");
+    const int st = threadIdx.x - kCtl, lg = st % LPG;
+    const uint16_t *last = row_of(ue - 1) + (LPG - 1) * 8;
+    UnitWalk wk(st / LPG, S, item0, ni);
     uint4 v[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int k = min((threadIdx.x - kCtl) + kStr * j, n - 1);
-      v[j] = ld_stream16(row(k / LPG) + (k % LPG) * 8);
+      const int u = st / LPG + S * j;
+      v[j] = ld_stream16(u < ue ? row(wk.item, wk.il) + lg * 8 : last);
+      wk.next();
     }
     DL_SCHED_FENCE();
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int k = (threadIdx.x - kCtl) + kStr * j;
+      const int k = st + kStr * j;
       if (k < n) L.w2[k] = v[j];
     }
   }
-  __device__ void use(int u, const uint4 &wv) const {
+  __device__ void use(int item, int il, const uint4 &wv) const {
     const int lg = threadIdx.x % LPG;
-    const int item = item0 + u / ni, il = u % ni;
     const float *ap = item < a.B ? L.u.d.act_s + item * a.F + lg * 8 : L.u.d.act + (item - a.B) * a.F + lg * 8;
     float wf[8];
     unpack8(wv, wf);
@@ -401,30 +428,44 @@ struct Down {
   }
   // all threads: staged units from LDS, then the rest streamed
   __device__ void compute() const {
+    if (n_units == 0) return;
     const int g = threadIdx.x / LPG, lg = threadIdx.x % LPG;
     const int ue = u0_end();
-    for (int ub = 0; ub < ue; ub += NG * R) {
-      uint4 wv[R];
+    {
+      UnitWalk wk(g, NG, item0, ni);
+      for (int ub = 0; ub < ue; ub += NG * R) {
+        uint4 wv[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int u = ub + g + NG * r;
-        wv[r] = u < ue ? L.w2[u * LPG + lg] : make_uint4(0, 0, 0, 0);
-      }
+        for (int r = 0; r < R; ++r) {
+          const int u = ub + g + NG * r;
+          wv[r] = u < ue ? L.w2[u * LPG + lg] : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int u = ub + g + NG * r;
-        if (u < ue) use(u, wv[r]);
+        for (int r = 0; r < R; ++r) {
+          const int u = ub + g + NG * r;
+          if (u < ue) use(wk.item, wk.il, wv[r]);
+          wk.next();
+        }
       }
     }
+    if (ue >= n_units) return;
+    const uint16_t *last = row_of(n_units - 1) + lg * 8;
+    UnitWalk wk(ue + g, NG, item0, ni);
     for (int ub = ue; ub < n_units; ub += NG * R) {
       uint4 wv[R];
+      UnitWalk lw = wk;
 #pragma unroll
-      for (int r = 0; r < R; ++r) wv[r] = ld_stream16(row(min(ub + g + NG * r, n_units - 1)) + lg * 8);
+      for (int r = 0; r < R; ++r) {
+        const int u = ub + g + NG * r;
+        wv[r] = ld_stream16(u < n_units ? row(lw.item, lw.il) + lg * 8 : last);
+        lw.next();
+      }
       DL_SCHED_FENCE();
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int u = ub + g + NG * r;
-        if (u < n_units) use(u, wv[r]);
+        if (u < n_units) use(wk.item, wk.il, wv[r]);
+        wk.next();
       }
     }
   }
@@ -558,30 +599,57 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         if (kind[q] && i < nw) L.u.unit[q][i] = v[q][j];
       }
   } else {
-    // control threads: every workgroup's partial sums (thread q: workgroup q)
+    // control threads: the G*B partial sums pss[w][t], thread tid polling
+    // words tid + kCtl*j, so each wave instruction reads 64 consecutive words
+    const int N = G * B;
     const uint64_t *pp[kFusedMaxB];
     uint64_t x[kFusedMaxB];
     bool use[kFusedMaxB];
 #pragma unroll
-    for (int t = 0; t < kFusedMaxB; ++t) {
-      use[t] = tid < G && t < B;
-      pp[t] = a.pss + (use[t] ? (size_t)tid * B + t : 0);
-      x[t] = use[t] ? ld_tagged(pp[t]) : 0ull;
+    for (int j = 0; j < kFusedMaxB; ++j) {
+      const int i = tid + kCtl * j;
+      use[j] = i < N;
+      pp[j] = a.pss + (use[j] ? i : 0);
+      x[j] = use[j] ? ld_tagged(pp[j]) : 0ull;
     }
     finish_tagged_n<kFusedMaxB>(pp, x, use, tag, a.spin_limit, &L.bad);
+    stamp(a, 2);
+    if ((kWave % B) == 0) {
+      // B divides the wave: every word of this thread is token tid % B; sum
+      // them, then over the lanes of the same token (xor strides >= B), and
+      // leave one partial per wave and token
+      float v = 0.f;
 #pragma unroll
-    for (int t = 0; t < kFusedMaxB; ++t) {
-      if (t < B) {
-        const float v = wave_sum(use[t] ? __uint_as_float((unsigned)x[t]) : 0.f);
-        if (lane == 0) L.red[wv * kFusedMaxB + t] = v;
-      }
+      for (int j = 0; j < kFusedMaxB; ++j) v += use[j] ? __uint_as_float((unsigned)x[j]) : 0.f;
+      if (B == 1)
+        v = wave_sum(v);
+      else
+        for (int m = B; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+      if (lane < B) L.red[wv * kFusedMaxB + lane] = v;
+    } else {
+      // otherwise the words land in LDS (the down-projection staging area,
+      // free until phase D) and one wave per token adds them
+      float *pssv = reinterpret_cast<float *>(L.w2);
+#pragma unroll
+      for (int j = 0; j < kFusedMaxB; ++j)
+        if (use[j]) pssv[tid + kCtl * j] = __uint_as_float((unsigned)x[j]);
     }
   }
   __syncthreads();
-  if (tid < B) {
+  // token t's sum over the workgroups in a fixed order (the same in every
+  // workgroup, so every workgroup derives the same 1/rms)
+  if ((kWave % B) == 0) {
+    if (tid < B) {
+      float s = 0.f;
+      for (int q = 0; q < kCtl / kWave; ++q) s += L.red[q * kFusedMaxB + tid];
+      L.inv_rms[tid] = 1.0f / sqrtf(s / (float)H + a.eps);
+    }
+  } else if (wv < B) {
+    const float *pssv = reinterpret_cast<const float *>(L.w2);
     float s = 0.f;
-    for (int q = 0; q < kCtl / kWave; ++q) s += L.red[q * kFusedMaxB + tid];
-    L.inv_rms[tid] = 1.0f / sqrtf(s / (float)H + a.eps);
+    for (int q = lane; q < G; q += kWave) s += pssv[q * B + wv];
+    s = wave_sum(s);
+    if (lane == 0) L.inv_rms[wv] = 1.0f / sqrtf(s / (float)H + a.eps);
   }
   // every workgroup's hg is now announced: acquire before reading it (drops
   // any line of an earlier step's hg from this XCD's caches)

@@ -104,6 +104,35 @@ def test_topk_and_shared_edges(top_k, shared, path):
     assert m
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_exact_logit_ties(path):
+    """Exact logit ties, made by duplicating router rows of the batch-1 TP16
+    shard: one inside the top-k and one across its boundary.  Equal logits
+    rank by expert id, lower first, and the boundary tie keeps the lower id."""
+    import dataclasses
+    say(f"[exact logit ties, TP16 shard batch 1, path={PATH_NAMES[path]}] start")
+    base = workload.build(1, h_source="stored")
+    k = base.shape.top_k
+    order = np.argsort(-workload.expected(base)["logits"][0], kind="stable")
+    picked = set(order[:k].tolist())
+    free = [e for e in range(base.shape.n_experts) if e not in picked]
+    r_in, r_edge = int(order[2]), int(order[k - 2])
+    d_in = free[0]
+    lower = [e for e in free[1:] if e < r_edge]
+    d_edge = lower[0] if lower else free[1]
+    wr = base.w_router.copy()
+    wr[d_in] = wr[r_in]
+    wr[d_edge] = wr[r_edge]
+    layer = dataclasses.replace(base, w_router=wr)
+    ref = workload.expected(layer)
+    idx = ref["topk_idx"][0].tolist()
+    assert d_in in idx and r_in in idx and idx.index(min(d_in, r_in)) + 1 == idx.index(max(d_in, r_in))
+    assert (min(d_edge, r_edge) in idx) and (max(d_edge, r_edge) not in idx)
+    layer = dataclasses.replace(layer, targets=np.asarray(ref["topk_idx"], np.int32))
+    got, obj = run_gpu(layer, path=path)
+    check(layer, got, f"ties_{used_name(obj, 1, path)}")
+
+
 def test_batch_zero_is_noop():
     say("[batch 0] start")
     from decode_step_moe_amd import IO
