@@ -773,8 +773,8 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     // scores of the k picks, renormalised (lane j holds pick j)
     const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
     const float ssum = wave_sum(s);
+    const float wgt = s / ssum;
     if (lane < K) {
-      const float wgt = s / ssum;
       L.sel[t * K + lane] = my_idx;
       L.selw[t * K + lane] = wgt;
       if (w == 0) {
@@ -782,64 +782,82 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         a.topk_w[(size_t)t * K + lane] = wgt;
       }
     }
+    if (B == 1) {
+      // one token: its k picks are k distinct experts, so this wave builds
+      // the lists at once - pair order is expert order, each expert one pair
+      int rank = 0;
+      for (int i = 0; i < K; ++i) rank += __builtin_amdgcn_readlane(my_idx, i) < my_idx;
+      if (lane < K) {
+        L.pair_tok[rank] = 0;
+        L.pair_exp[rank] = my_idx;
+        L.pair_w[rank] = wgt;
+        L.pos[lane] = rank;
+        L.act_exp[rank] = my_idx;
+        L.act_cnt[rank] = 1;
+        L.act_off[rank] = rank;
+      }
+      if (lane == 0) L.n_active = K;
+    }
   }
-  __syncthreads();
-  stamp(a, 13);
-  // per-expert lists.  Pick p = t*K + r has key e_p * 64 + t; pairs are
-  // ordered by key (expert, then token), active experts ascending.  All
-  // threads count, for pick p, the keys below its own and the picks of the
-  // same expert in one eighth of the picks; wave 0 adds the eight parts,
-  // places the pairs and marks each expert's first pair.
-  {
-    const int P = B * K;
-    const int p = lane, part = wv, q0 = part * (kFusedMaxPairs / kFWaves);
-    int lt = 0, same = 0;
-    if (p < P) {
-      const int ep = L.sel[p], kp = ep * 64 + p / K;
-#pragma unroll
-      for (int i = 0; i < kFusedMaxPairs / kFWaves; ++i) {
-        const int q = q0 + i;
-        if (q < P) {
-          const int eq = L.sel[q];
-          lt += eq * 64 + q / K < kp;
-          same += eq == ep;
+  if (B > 1) {  // several tokens: counted in parallel by all waves
+    __syncthreads();
+    stamp(a, 13);
+    // per-expert lists.  Pick p = t*K + r has key e_p * 64 + t; pairs are
+    // ordered by key (expert, then token), active experts ascending.  All
+    // threads count, for pick p, the keys below its own and the picks of the
+    // same expert in one eighth of the picks; wave 0 adds the eight parts,
+    // places the pairs and marks each expert's first pair.
+    {
+      const int P = B * K;
+      const int p = lane, part = wv, q0 = part * (kFusedMaxPairs / kFWaves);
+      int lt = 0, same = 0;
+      if (p < P) {
+        const int ep = L.sel[p], kp = ep * 64 + p / K;
+  #pragma unroll
+        for (int i = 0; i < kFusedMaxPairs / kFWaves; ++i) {
+          const int q = q0 + i;
+          if (q < P) {
+            const int eq = L.sel[q];
+            lt += eq * 64 + q / K < kp;
+            same += eq == ep;
+          }
         }
       }
+      L.part_lt[part][p] = lt;
+      L.part_same[part][p] = same;
     }
-    L.part_lt[part][p] = lt;
-    L.part_same[part][p] = same;
-  }
-  __syncthreads();
-  if (wv == 0) {
-    const int P = B * K;
-    int rank = 0, same = 0;
-#pragma unroll
-    for (int part = 0; part < kFWaves; ++part) {
-      rank += L.part_lt[part][lane];
-      same += L.part_same[part][lane];
+    __syncthreads();
+    if (wv == 0) {
+      const int P = B * K;
+      int rank = 0, same = 0;
+  #pragma unroll
+      for (int part = 0; part < kFWaves; ++part) {
+        rank += L.part_lt[part][lane];
+        same += L.part_same[part][lane];
+      }
+      if (lane < P) {
+        const int ep = L.sel[lane];
+        L.pair_tok[rank] = lane / K;
+        L.pair_exp[rank] = ep;
+        L.pair_w[rank] = L.selw[lane];
+        L.pos[lane] = rank;
+        L.part_same[0][rank] = same;   // count of the pair's expert, by sorted position
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+      __builtin_amdgcn_wave_barrier();
+      const int r = lane;
+      const int er = r < P ? L.pair_exp[r] : -1;
+      const bool first = r < P && (r == 0 || L.pair_exp[r - 1] != er);
+      const unsigned long long fm = __ballot(first);
+      if (first) {
+        const int slot = __popcll(fm & ((1ull << r) - 1ull));
+        L.act_exp[slot] = er;
+        L.act_cnt[slot] = L.part_same[0][r];
+        L.act_off[slot] = r;
+      }
+      if (lane == 0) L.n_active = __popcll(fm);
     }
-    if (lane < P) {
-      const int ep = L.sel[lane];
-      L.pair_tok[rank] = lane / K;
-      L.pair_exp[rank] = ep;
-      L.pair_w[rank] = L.selw[lane];
-      L.pos[lane] = rank;
-      L.part_same[0][rank] = same;   // count of the pair's expert, by sorted position
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
-    const int r = lane;
-    const int er = r < P ? L.pair_exp[r] : -1;
-    const bool first = r < P && (r == 0 || L.pair_exp[r - 1] != er);
-    const unsigned long long fm = __ballot(first);
-    if (first) {
-      const int slot = __popcll(fm & ((1ull << r) - 1ull));
-      L.act_exp[slot] = er;
-      L.act_cnt[slot] = L.part_same[0][r];
-      L.act_off[slot] = r;
-    }
-    if (lane == 0) L.n_active = __popcll(fm);
-  }
+  }  // B > 1
   stamp(a, 12);
   __syncthreads();
   stamp(a, 8);
