@@ -412,9 +412,13 @@ struct Down {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int k = st + kStr * j;
-      if (k < n) L.w2[k] = v[j];
+      if (k < n) L.w2[swz(k / LPG, k % LPG)] = v[j];
     }
   }
+  // LDS word of word j of staged unit u: the words of a unit are rotated by
+  // an xor with u, so that threads reading word j of consecutive units hit
+  // different banks, and a lane group reading one unit still covers all
+  __device__ static int swz(int u, int j) { return u * LPG + (j ^ (u & (LPG - 1))); }
   __device__ void use(int item, int il, const uint4 &wv) const {
     const int lg = threadIdx.x % LPG;
     const float *ap = item < a.B ? L.u.d.act_s + item * a.F + lg * 8 : L.u.d.act + (item - a.B) * a.F + lg * 8;
@@ -426,11 +430,40 @@ struct Down {
     s = group_sum(s, LPG);
     if (lg == 0) L.u.d.contrib[item * kFusedMaxSlice + il] = item < a.B ? s : s * L.pair_w[item - a.B];
   }
+  // every unit staged: one unit per thread, its whole row summed in order,
+  // with no cross-lane sums
+  __device__ void compute_staged() const {
+    for (int u = threadIdx.x; u < n_units; u += kFT) {
+      const int item = item0 + u / ni, il = u % ni;
+      const float *ap = item < a.B ? L.u.d.act_s + item * a.F : L.u.d.act + (item - a.B) * a.F;
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < LPG; ++j) {
+        float wf[8];
+        unpack8(L.w2[swz(u, j)], wf);
+        const float4 x0 = *reinterpret_cast<const float4 *>(ap + 8 * j);
+        const float4 x1 = *reinterpret_cast<const float4 *>(ap + 8 * j + 4);
+        s = fmaf(wf[0], x0.x, s);
+        s = fmaf(wf[1], x0.y, s);
+        s = fmaf(wf[2], x0.z, s);
+        s = fmaf(wf[3], x0.w, s);
+        s = fmaf(wf[4], x1.x, s);
+        s = fmaf(wf[5], x1.y, s);
+        s = fmaf(wf[6], x1.z, s);
+        s = fmaf(wf[7], x1.w, s);
+      }
+      L.u.d.contrib[item * kFusedMaxSlice + il] = item < a.B ? s : s * L.pair_w[item - a.B];
+    }
+  }
   // all threads: staged units from LDS, then the rest streamed
   __device__ void compute() const {
     if (n_units == 0) return;
     const int g = threadIdx.x / LPG, lg = threadIdx.x % LPG;
     const int ue = u0_end();
+    if (ue == n_units) {
+      compute_staged();
+      return;
+    }
     {
       UnitWalk wk(g, NG, item0, ni);
       for (int ub = 0; ub < ue; ub += NG * R) {
@@ -438,7 +471,7 @@ struct Down {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int u = ub + g + NG * r;
-          wv[r] = u < ue ? L.w2[u * LPG + lg] : make_uint4(0, 0, 0, 0);
+          wv[r] = u < ue ? L.w2[swz(u, lg)] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
