@@ -265,7 +265,14 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
   __shared__ float red[kWavesPerBlock][4 * NT * 256];  // [wave][chunk][tile][m * 16 + n]
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int B = a.B, H = a.H, E = a.E;
-  const int e0 = blockIdx.x * kBatchRtrExperts, ky = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id, so ids L,
+  // L + 8, ... share one XCD's L2.  Tiles (K chunk ky, expert group ex) are
+  // numbered with ex fastest and each XCD takes a contiguous range of them:
+  // its workgroups then share a few hg K chunks instead of every XCD reading
+  // every chunk.
+  const int nb = gridDim.x * gridDim.y, lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int tile = nb % 8 == 0 ? (lin % 8) * (nb / 8) + lin / 8 : lin;
+  const int e0 = (tile % gridDim.x) * kBatchRtrExperts, ky = tile / gridDim.x;
   const int kb = ky * kBatchRtrK + wv * (kBatchRtrK / kWavesPerBlock) + 4 * g;
   const float *wrow[NT];
 #pragma unroll
