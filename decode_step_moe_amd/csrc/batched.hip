@@ -339,6 +339,43 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
   }
 }
 
+// Exclusive prefix sums of two per-thread counts over the workgroup (kBlock
+// threads), with the totals: a scan inside each wave, then the wave totals
+// from LDS (two barriers instead of one pair per doubling step).
+__device__ __forceinline__ void block_excl_scan2(int x, int y, int &px, int &py, int &tx, int &ty, int *sx, int *sy) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int ix = x, iy = y;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int vx = __shfl_up(ix, d, kWave), vy = __shfl_up(iy, d, kWave);
+    if (lane >= d) {
+      ix += vx;
+      iy += vy;
+    }
+  }
+  __syncthreads();  // earlier readers of sx / sy are done
+  if (lane == kWave - 1) {
+    sx[wv] = ix;
+    sy[wv] = iy;
+  }
+  __syncthreads();
+  int ox = 0, oy = 0;
+  tx = 0;
+  ty = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const int wx = sx[w], wy = sy[w];
+    if (w < wv) {
+      ox += wx;
+      oy += wy;
+    }
+    tx += wx;
+    ty += wy;
+  }
+  px = ox + ix - x;
+  py = oy + iy - y;
+}
+
 // ================================================================ launch 3
 __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk) {
   __shared__ float lg[kMaxExperts];
@@ -457,17 +494,8 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   const int q0 = tid * seg, q1 = min(E, q0 + seg);
   int la = 0, lc = 0;
   for (int q = q0; q < q1; ++q) { la += cnt[q] > 0; lc += cnt[q]; }
-  sa[tid] = la;
-  sc[tid] = lc;
-  __syncthreads();
-  for (int o = 1; o < kBlock; o <<= 1) {
-    const int va = tid >= o ? sa[tid - o] : 0, vc = tid >= o ? sc[tid - o] : 0;
-    __syncthreads();
-    sa[tid] += va;
-    sc[tid] += vc;
-    __syncthreads();
-  }
-  int pa = sa[tid] - la, pc = sc[tid] - lc;
+  int pa, pc, n_act, n_pairs;
+  block_excl_scan2(la, lc, pa, pc, n_act, n_pairs, sa, sc);
   for (int q = q0; q < q1; ++q) {
     const int c = cnt[q];
     off[q] = pc;
@@ -481,7 +509,6 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
       pc += c;
     }
   }
-  const int n_act = sa[kBlock - 1];
   if (tid == kBlock - 1) *a.n_active = n_act;
   __syncthreads();
   // gate/up work lists: matrix-core entries (slot, 16-token chunk), then VALU
@@ -494,18 +521,9 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
       lm += slot_nch[q];
       lv += slot_nch[q] == 0;
     }
-    sa[tid] = lm;
-    sc[tid] = lv;
-    __syncthreads();
-    for (int o = 1; o < kBlock; o <<= 1) {
-      const int vm = tid >= o ? sa[tid - o] : 0, vv = tid >= o ? sc[tid - o] : 0;
-      __syncthreads();
-      sa[tid] += vm;
-      sc[tid] += vv;
-      __syncthreads();
-    }
-    const int n_qm = sa[kBlock - 1], n_qv = sc[kBlock - 1];
-    int pm = sa[tid] - lm, pv = n_qm + sc[tid] - lv;
+    int pm, pv, n_qm, n_qv;
+    block_excl_scan2(lm, lv, pm, pv, n_qm, n_qv, sa, sc);
+    pv += n_qm;
     for (int q = s0; q < s1; ++q) {
       for (int c = 0; c < slot_nch[q]; ++c) a.gu_q[pm++] = q | (c << 16);
       if (slot_nch[q] == 0) a.gu_q[pv++] = q;
