@@ -234,11 +234,12 @@ int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
  * values (caller-owned, 16-byte aligned), every later single-launch step has
  * thread 0 of each workgroup w write the device wall clock (100 MHz) into
  * buffer[w * points + p] at these points: 0 start, 1 out-projection done and
- * norm partials published, 4 norm known, 5 logits (and shared-expert
- * activations) published, 7 all logits read, 14 top-k start, 15 top-k
- * selection done, 13 top-k done, 12 expert lists built (wave 0), 8 lists
- * visible to the workgroup, 9 routed SwiGLU activations published,
- * 10 activations read, 11 y written, 3 end; others unused.
+ * norm partials published, 2 every norm partial polled, 4 norm known,
+ * 5 logits (and shared-expert activations) published, 7 all logits read,
+ * 14 top-k start, 15 top-k selection done, 13 top-k done (batches above one
+ * token), 12 expert lists built (wave 0), 8 lists visible to the workgroup,
+ * 9 routed SwiGLU activations published, 10 activations read, 11 y written,
+ * 3 end; others unused.
  * NULL turns it off.  Returns DL_OK or DL_ERR_INVALID_ARG. */
 int decode_layer_set_trace(decode_layer *h, void *device_buffer);
 int decode_layer_trace_points(void);
