@@ -163,12 +163,64 @@ __device__ __forceinline__ void mfma_tiles(const uint16_t *const (&wp)[NR], cons
   }
 }
 
+// The same product with both operands staged through LDS.  A wave stages one
+// 128-element K chunk (four matrix-core K steps) of its NR*16 weight rows and
+// NC*16 token rows at a time, 256 bytes per row, loaded straight from memory
+// into LDS: one load instruction covers 4 rows x 256 contiguous bytes (8 whole
+// cache lines), where the matrix-core operand pattern touches 16 half lines.
+// Row R keeps its 16-byte word c at slot c ^ (R & 15), so the operand reads
+// (16 rows x one word) hit 16 different bank groups.  (The compiler waits for
+// every load into LDS before any LDS read, so the chunk is single-buffered:
+// one memory round trip per chunk.)
+constexpr int kStgRows = 128;                 // rows of the buffer (weights then tokens)
+constexpr int kStgWords = kStgRows * 16;      // 16-byte words of the buffer (32 KB)
+__device__ __forceinline__ int stg_slot(int row, int c) { return row * 16 + (c ^ (row & 15)); }
+
+template <int NR, int NC>
+__device__ __forceinline__ void mfma_tiles_lds(const uint16_t *w0, size_t wld, int nw, const uint16_t *a0, size_t ald,
+                                               int na, int nks, uint4 *buf, f32x4 (&acc)[NR][NC]) {
+  static_assert((NR + NC) * 16 <= kStgRows, "buffer rows");
+  constexpr int NI = (NR + NC) * 16 / 4;  // load instructions per chunk (4 rows each)
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  for (int j = 0; 4 * j < nks; ++j) {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int R = 4 * q + (lane >> 4), p = lane & 15;
+      int c = p ^ (R & 15);
+      if (4 * j + (c >> 2) >= nks) c &= 3;  // a K step past the wave's range: re-read step 4j (its product is skipped)
+      const uint16_t *src = R < NR * 16 ? w0 + (size_t)min(R, nw - 1) * wld + 128 * j + 8 * c
+                                        : a0 + (size_t)min(R - NR * 16, na - 1) * ald + 128 * j + 8 * c;
+      __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(buf + 64 * q), 16, 0,
+                                       0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the chunk is in LDS
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      if (4 * j + s4 < nks) {
+        uint4 wv[NR], av[NC];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) wv[r] = buf[stg_slot(16 * r + n, 4 * s4 + g)];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) av[c] = buf[stg_slot(NR * 16 + 16 * c + n, 4 * s4 + g)];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[r][c] = mfma_bf16(av[c], wv[r], acc[r][c]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this chunk's LDS reads are done before the next overwrites it
+  }
+}
+
 // Workgroup: kProjRows rows of Wo (blocks < n_wo; K = Do split over the 4
 // waves) or of Wqkv (K = H split over qkv_split workgroups x 4 waves).
 // red[w][token][row]: wave w's partial sum.
 constexpr int kProjRows = 64;
 __global__ void __launch_bounds__(kBlock) proj_b(BatchArgs a, int n_wo) {
-  __shared__ float red[kWavesPerBlock][kMaxBatch][kProjRows];
+  // staging buffers of the main loop, then the per-wave partial sums
+  __shared__ __align__(16) uint4 lds_raw[kWavesPerBlock * kStgWords];
+  float (*red)[kMaxBatch][kProjRows] = reinterpret_cast<float (*)[kMaxBatch][kProjRows]>(lds_raw);
+  static_assert(sizeof(float) * kWavesPerBlock * kMaxBatch * kProjRows <= sizeof(uint4) * kWavesPerBlock * kStgWords, "red fits");
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int B = a.B;
   const bool wo = (int)blockIdx.x < n_wo;
@@ -206,20 +258,17 @@ __global__ void __launch_bounds__(kBlock) proj_b(BatchArgs a, int n_wo) {
     for (int j = 0; j < TPW; ++j) rin[j] = a.resid_in[(size_t)min(wv + kWavesPerBlock * j, B - 1) * a.H + r0 + lane];
   }
   constexpr int NR = kProjRows / 16;
-  const uint16_t *wp[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) wp[r] = wbase + (size_t)min(r0 + 16 * r + n, nrow - 1) * wld;
   by_chunks((B + 15) >> 4, [&](auto ncc) {
     constexpr int NC = decltype(ncc)::value;
-    const uint16_t *ap[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) ap[c] = abase + (size_t)min(16 * c + n, B - 1) * ld;
     f32x4 acc[NR][NC];
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_tiles<NR, NC, 4>(wp, ap, nks, acc);
+    // rows r0.. of the weights and tokens 0.. from this wave's K start
+    mfma_tiles_lds<NR, NC>(wbase - 8 * g + (size_t)r0 * wld, wld, nrow - r0, abase - 8 * g, (size_t)ld, B, nks,
+                           lds_raw + wv * kStgWords, acc);
+    __syncthreads();  // the partial sums below overwrite other waves' staging buffers
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
