@@ -389,12 +389,22 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """The source without comments, trailing blanks and empty lines (the kernel
+    sources hold no comment markers inside string literals), so that edits to
+    comments alone do not retire a counter summary."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "decode_step_moe_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "decode_step_moe_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -18,15 +18,17 @@
 //                sums of r1^2.
 //              64 rows of Wqkv per workgroup, K = H split over 8 workgroups
 //                (4 when H % 1024 != 0) x 4 waves: partial qkv sums.
+//              Operands staged through LDS in 128-element K chunks.
 //  2 router_b  fp32 router dot products d[t, e] = hg[t] . Wr[e] on MFMA
-//              (v_mfma_f32_16x16x4_f32), 32 experts x 256 K per workgroup;
+//              (v_mfma_f32_16x16x4_f32), 48 experts x 256 K per workgroup,
+//              tiles ordered so each XCD's workgroups share hg K chunks;
 //              also sums the qkv partials (fixed order) -> qkv.
 //  3 topk_b    one workgroup per token: 1/rms, h = hg / rms (fp32 and bf16
 //              hi + lo planes), logits l = d / rms, top-k by repeated wave
 //              arg-max (descending, ties to the lower expert id), weights
 //              s / sum s with s = sigmoid(l).  The last workgroup to finish
 //              builds the per-expert token lists (active experts ascending,
-//              tokens ascending inside an expert).
+//              tokens ascending inside an expert) with wave prefix sums.
 //  4 gateup_b  a[p, f] = silu(W1[e, f] . h[t_p]) * (W3[e, f] . h[t_p]):
 //              matrix-core units (64 rows of W1 and W3 x a 16-token chunk
 //              x a K chunk) cut into one contiguous run per workgroup, two
@@ -46,7 +48,9 @@
 // Weight loads.  A matrix-core operand fragment is 16 rows x 64 bytes per
 // load instruction (the next 64 bytes of each row follow in the next K
 // step), and these kernels read weights with ordinary cached loads: on this
-// pattern they stream measurably faster than non-temporal loads.
+// pattern they stream measurably faster than non-temporal loads.  The
+// projections instead stage whole 256-byte row segments in LDS (4 rows per
+// load instruction) and read the fragments from there.
 //
 // Every output element is produced by one thread, in an order that depends
 // only on the shapes, so results are bit-identical from run to run.

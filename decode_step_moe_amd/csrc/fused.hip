@@ -35,15 +35,17 @@
 //     every workgroup reads all logits and takes the same top-k decision
 //     (descending logit, ties to the lower expert id; s = sigmoid(l),
 //     w = s / sum s over the k picks), builds the same per-expert token lists
-//     in LDS, then computes its share of the routed gate/up rows:
+//     in LDS (with one token, the top-k wave ranks its k distinct experts
+//     directly), then computes its share of the routed gate/up rows:
 //     a[p, f] = silu(W1[e, f] . h[t_p]) * (W3[e, f] . h[t_p])
 //     for every (expert e, token t_p) pair p -> published.
 //  D  y[t, i] for i in S_w:  sum_f S2[i, f] a_s[t, f]
 //                           + sum over the k picks of t, in pick order, of
 //                             w_p sum_f W2[e_p, i, f] a[p, f].
-//     Each y element is produced by one thread in a fixed order.
-//     qkv[t, j] = x[t] . Wqkv[j] for this workgroup's rows j is computed while
-//     the activations of phase C are in flight.
+//     The first down-projection rows of the slice are staged in LDS while the
+//     activations are in flight.  Each (item, row) dot product is formed in
+//     a fixed order (by one thread when every unit is staged, else by a lane
+//     group), and each y element is the sum of its items in pick order.
 //
 // Wave roles.  A wave's loads complete in issue order, so a poll issued after
 // a bulk weight request waits for that request.  Waves 0-3 (control) poll and
