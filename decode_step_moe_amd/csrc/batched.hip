@@ -454,6 +454,20 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
       hx[j][1] = ld16f(a.hg + (size_t)t * H + i + 4);
     }
   }
+  // the router partial sums of this thread's experts (e = tid, tid + kBlock)
+  // are requested in the same round trip: the logits need 1/rms only at the end
+  constexpr int PRE = 32;  // K chunks preloaded per expert
+  const bool pre = n_rk <= PRE && E <= 2 * kBlock;
+  const size_t lstride = (size_t)B * E;
+  float pv[2][PRE];
+  if (pre) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const float *p = a.rlog_part + (size_t)t * E + min(tid + kBlock * x, E - 1);
+#pragma unroll
+      for (int j = 0; j < PRE; ++j) pv[x][j] = p[min(j, n_rk - 1) * lstride];
+    }
+  }
   // 1/rms from the out-projection workgroups' partial sums
   float ss = 0.f;
   for (int q = tid; q < n_ow; q += kBlock) ss += a.ss_part[(size_t)q * B + t];
@@ -483,7 +497,21 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
     *reinterpret_cast<uint4 *>(a.hp + (size_t)B * H + o) = lo;
   }
   // logits: K chunks summed in ascending order, then scaled
-  for (int e = tid; e < E; e += kBlock) {
+  if (pre) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int e = tid + kBlock * x;
+      if (e < E) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) d += j < n_rk ? pv[x][j] : 0.f;
+        const float l = d * inv;
+        lg[e] = l;
+        if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
+      }
+    }
+  }
+  for (int e = pre ? E : tid; e < E; e += kBlock) {
     float d = 0.f;
     const float *p = a.rlog_part + (size_t)t * E + e;
     const size_t stride = (size_t)B * E;
