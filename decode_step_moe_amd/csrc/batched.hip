@@ -21,8 +21,9 @@
 //              Operands staged through LDS in 128-element K chunks.
 //  2 router_b  fp32 router dot products d[t, e] = hg[t] . Wr[e] on MFMA
 //              (v_mfma_f32_16x16x4_f32), 48 experts x 256 K per workgroup,
-//              tiles ordered so each XCD's workgroups share hg K chunks;
-//              also sums the qkv partials (fixed order) -> qkv.
+//              tiles ordered so each XCD's workgroups share hg K chunks,
+//              operands staged through LDS; also sums the qkv partials
+//              (fixed order) -> qkv.
 //  3 topk_b    one workgroup per token: 1/rms, h = hg / rms (fp32 and bf16
 //              hi + lo planes), logits l = d / rms, top-k by repeated wave
 //              arg-max (descending, ties to the lower expert id), weights
@@ -49,8 +50,8 @@
 // load instruction (the next 64 bytes of each row follow in the next K
 // step), and these kernels read weights with ordinary cached loads: on this
 // pattern they stream measurably faster than non-temporal loads.  The
-// projections instead stage whole 256-byte row segments in LDS (4 rows per
-// load instruction) and read the fragments from there.
+// projections and the router instead stage whole 256-byte row segments in
+// LDS (4 rows per load instruction) and read the fragments from there.
 //
 // Every output element is produced by one thread, in an order that depends
 // only on the shapes, so results are bit-identical from run to run.
@@ -315,7 +316,13 @@ __global__ void __launch_bounds__(kBlock) proj_b(BatchArgs a, int n_wo) {
 // k = kb + 4g + s.
 __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
   constexpr int NT = kBatchRtrExperts / 16;  // expert tiles per workgroup
-  __shared__ float red[kWavesPerBlock][4 * NT * 256];  // [wave][chunk][tile][m * 16 + n]
+  // staging: per wave, the 64-element K range of its NT*16 expert rows and
+  // up to 64 token rows, 256 bytes per row (16 words); then the partial sums
+  constexpr int RW = NT * 16 + kMaxBatch;     // staged rows per wave
+  __shared__ __align__(16) uint4 lds_raw[kWavesPerBlock * RW * 16];
+  float (*red)[4 * NT * 256] = reinterpret_cast<float (*)[4 * NT * 256]>(lds_raw);  // [wave][chunk][tile][m * 16 + n]
+  static_assert(sizeof(float) * kWavesPerBlock * 4 * NT * 256 <= sizeof(uint4) * kWavesPerBlock * RW * 16, "red fits");
+  static_assert(kBatchRtrK / kWavesPerBlock == 64, "one 256-byte fp32 segment per row and wave");
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int B = a.B, H = a.H, E = a.E;
   // Workgroups are dealt to the 8 XCDs round-robin by linear id, so ids L,
@@ -326,24 +333,37 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
   const int nb = gridDim.x * gridDim.y, lin = blockIdx.y * gridDim.x + blockIdx.x;
   const int tile = nb % 8 == 0 ? (lin % 8) * (nb / 8) + lin / 8 : lin;
   const int e0 = (tile % gridDim.x) * kBatchRtrExperts, ky = tile / gridDim.x;
-  const int kb = ky * kBatchRtrK + wv * (kBatchRtrK / kWavesPerBlock) + 4 * g;
-  const float *wrow[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wrow[nt] = a.w_router + (size_t)min(e0 + 16 * nt + n, E - 1) * H + kb;
+  const int kb0 = ky * kBatchRtrK + wv * (kBatchRtrK / kWavesPerBlock);  // this wave's K start
+  uint4 *buf = lds_raw + wv * RW * 16;
   by_chunks((B + 15) >> 4, [&](auto ncc) {
     constexpr int NC = decltype(ncc)::value;
+    // rows R < NT*16 are experts e0 + R, the rest tokens; each load
+    // instruction covers 4 rows x 256 contiguous bytes (word c of row R at
+    // slot c ^ (R & 15), so the operand reads below are conflict-free)
+    constexpr int NI = (NT * 16 + NC * 16) / 4;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int R = 4 * q + (lane >> 4), p = lane & 15, c = p ^ (R & 15);
+      const float *src = R < NT * 16 ? a.w_router + (size_t)min(e0 + R, E - 1) * H + kb0 + 4 * c
+                                     : a.hg + (size_t)min(R - NT * 16, B - 1) * H + kb0 + 4 * c;
+      __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(buf + 64 * q), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the rows are in LDS
+    // lane (n, g) at step it takes word 4 it + g: K = 16 it + 4 g .. + 3
     float4 bw[4][NT], av[4][NC];
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = 0; it < 4; ++it) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) bw[it][nt] = ld16f(wrow[nt] + 16 * it);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int R = 16 * nt + n;
+        bw[it][nt] = __builtin_bit_cast(float4, buf[R * 16 + ((4 * it + g) ^ (R & 15))]);
+      }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float *ap = a.hg + (size_t)min(16 * c + n, B - 1) * H + kb;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) av[it][c] = ld16f(ap + 16 * it);
+      for (int c = 0; c < NC; ++c) {
+        const int R = NT * 16 + 16 * c + n;
+        av[it][c] = __builtin_bit_cast(float4, buf[R * 16 + ((4 * it + g) ^ (R & 15))]);
+      }
     }
-    DL_SCHED_FENCE();
     f32x4 acc[NC][NT];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -361,6 +381,7 @@ __global__ void __launch_bounds__(kBlock) router_b(BatchArgs a) {
           for (int s = 0; s < 4; ++s) acc[c][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], w4[s], acc[c][nt], 0, 0, 0);
         }
       }
+    __syncthreads();  // the partial sums below overlay other waves' staging rows
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
