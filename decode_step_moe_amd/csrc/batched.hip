@@ -1005,13 +1005,39 @@ __device__ __forceinline__ int dn_run(int w, int G) {
   return (G & 1) ? w : 2 * (w % half) + w / half;
 }
 
-// Rows 16 wv + n of the group, K positions 32 s + 8 g (s < Fd / 32).
+// The wave's 16 rows 16 wv .. 16 wv + 15 of the group, loaded as 4 rows x 256
+// contiguous bytes per instruction (whole cache lines): word j = 2q + h of a
+// lane holds row 4q + lane / 16, 16-byte word (lane % 16) + 16h of the row.
 __device__ __forceinline__ void dn_load_w(const uint16_t *rows, int Fd, uint4 (&w)[8]) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
-  const int nks = Fd >> 5;
-  const uint16_t *p = rows + (size_t)(16 * wv + n) * Fd + 8 * g;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wpr = Fd >> 3;  // 16-byte words per row
 #pragma unroll
-  for (int s = 0; s < 8; ++s) w[s] = ld16(p + 32 * min(s, nks - 1));
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * wv + 4 * q + (lane >> 4), c = min((lane & 15) + 16 * h, wpr - 1);
+      w[2 * q + h] = ld16(rows + (size_t)r * Fd + 8 * c);
+    }
+}
+
+// From the load layout to the matrix-core layout (lane (n, g) at K step s:
+// row n, K 32 s + 8 g) through this wave's LDS rows: word c of row r sits at
+// slot c ^ (r & 15), so both the writes and the reads are free of bank
+// conflicts.  Only this wave touches its rows, and a wave's LDS operations
+// run in order.
+__device__ __forceinline__ void dn_relayout(const uint4 (&w)[8], uint4 *ws, uint4 (&wm)[8]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 4 * q + (lane >> 4), c = (lane & 15) + 16 * h;
+      ws[r * 32 + (c ^ (r & 15))] = w[2 * q + h];
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int st = 0; st < 8; ++st) wm[st] = ws[n * 32 + ((4 * st + g) ^ n)];
 }
 
 struct DnSrc {
@@ -1106,6 +1132,7 @@ __device__ __forceinline__ void dn_compute(const DnSrc &c, bool mfma, const uint
 __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
   __shared__ float ytile[kMaxBatch * kDnRows];
   __shared__ __align__(16) uint16_t stg[2 * 16 * kDnLd];
+  __shared__ __align__(16) uint4 wst[kWavesPerBlock][16 * 32];  // each wave's 16 weight rows (512 bytes each)
   __shared__ int s_exp[kMaxExperts], s_cnt[kMaxExperts], s_off[kMaxExperts];
   __shared__ int s_tok[16];
   __shared__ float s_wt[16];
@@ -1136,7 +1163,7 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
   };
   long u = (long)ri * U / Ga;
   const long ue = (long)(ri + 1) * U / Ga;
-  uint4 wc[8], wn[8];
+  uint4 wc[8], wn[8], wm[8];
   {
     int Fd;
     const uint16_t *rows = rows_of(u, Fd);
@@ -1169,13 +1196,14 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
         dn_load_w(rows, Fd, wn);
       }
       asm volatile("" ::: "memory");
+      if (c0 == 0) dn_relayout(wc, wst[threadIdx.x >> 6], wm);
       dn_stage_store(c, v, mfma, stg);
       if (tid < 16) {
         s_tok[tid] = tk;
         s_wt[tid] = wt;
       }
       __syncthreads();
-      dn_compute(c, mfma, wc, stg, s_tok, s_wt, ytile);
+      dn_compute(c, mfma, wm, stg, s_tok, s_wt, ytile);
       __syncthreads();
     }
 #pragma unroll
