@@ -722,35 +722,68 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gu_rsrc(const float *p, int fl
 
 // One matrix-core unit: sums over its K chunk into its slot, as
 // [W1 | W3][tile][row][token] (a lane's 4 tokens are contiguous).
+// Weights are loaded by pairs of K steps, 8 rows x 128 contiguous bytes per
+// instruction (whole cache lines), and moved into the matrix-core layout
+// through the wave's own 4 KB of LDS (ws): word c of row r of a pair sits at
+// slot c ^ ((r >> 1) & 7), so writes and reads are free of bank conflicts.
+constexpr int kGuPairs = 4;  // K-step pairs per load batch
 template <int NTL>
-__device__ void gu_unit(const BatchArgs &a, const GuUnit &s, const uint16_t *lds) {
-  constexpr int U = 7;
+__device__ void gu_unit(const BatchArgs &a, const GuUnit &s, const uint16_t *lds, uint4 *ws) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   if (wv >= NTL) return;
-  const int H = a.H, kb = 32 * s.k0, nks = s.k1 - s.k0;
-  const uint16_t *p1 = s.w1 + (size_t)(16 * wv + n) * H + kb + 8 * g;
-  const uint16_t *p3 = s.w3 + (size_t)(16 * wv + n) * H + kb + 8 * g;
+  const int H = a.H, kb = 32 * s.k0, nks = s.k1 - s.k0, npair = (nks + 1) >> 1;
+  // load lane: rows 8h + lane / 8 of the tile, word lane % 8 of a pair
+  const int lr = lane >> 3, lw = lane & 7;
+  const uint16_t *q1[2], *q3[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    q1[h] = s.w1 + (size_t)(16 * wv + 8 * h + lr) * H + kb;
+    q3[h] = s.w3 + (size_t)(16 * wv + 8 * h + lr) * H + kb;
+  }
   const uint16_t *lh = lds + n * kGuLd + 8 * g, *ll = lh + 16 * kGuLd;
   f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = acc1;
-  for (int ks = 0; ks < nks; ks += U) {
-    uint4 w1v[U], w3v[U];
+  for (int p0 = 0; p0 < npair; p0 += kGuPairs) {
+    uint4 w1v[kGuPairs][2], w3v[kGuPairs][2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = min(ks + u, nks - 1) * 32;
-      w1v[u] = ld16(p1 + k);
-      w3v[u] = ld16(p3 + k);
+    for (int pp = 0; pp < kGuPairs; ++pp) {
+      const int pr = min(p0 + pp, npair - 1);
+      // a second K step past the unit re-reads the first (its product is skipped)
+      const int wd = 2 * pr + (lw >> 2) < nks ? lw : (lw & 3);
+      const int k = 64 * pr + 8 * wd;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        w1v[pp][h] = ld16(q1[h] + k);
+        w3v[pp][h] = ld16(q3[h] + k);
+      }
     }
     DL_SCHED_FENCE();
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = min(ks + u, nks - 1) * 32;
-      const bool on = ks + u < nks;
-      const uint4 b1 = zero_unless(on, w1v[u]), b3 = zero_unless(on, w3v[u]);
-      const uint4 hv = *reinterpret_cast<const uint4 *>(lh + k), lv = *reinterpret_cast<const uint4 *>(ll + k);
-      acc1 = mfma_bf16(hv, b1, acc1);
-      acc3 = mfma_bf16(hv, b3, acc3);
-      acc1 = mfma_bf16(lv, b1, acc1);
-      acc3 = mfma_bf16(lv, b3, acc3);
+    for (int pp = 0; pp < kGuPairs; ++pp) {
+      const int pr = p0 + pp;
+      if (pr >= npair) break;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + lr, sl = r * 8 + (lw ^ ((r >> 1) & 7));
+        ws[sl] = w1v[pp][h];
+        ws[128 + sl] = w3v[pp][h];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows are written
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int ks = 2 * pr + s2;
+        if (ks < nks) {
+          const int sl = n * 8 + ((4 * s2 + g) ^ ((n >> 1) & 7));
+          const uint4 b1 = ws[sl], b3 = ws[128 + sl];
+          const uint4 hv = *reinterpret_cast<const uint4 *>(lh + 32 * ks);
+          const uint4 lv = *reinterpret_cast<const uint4 *>(ll + 32 * ks);
+          acc1 = mfma_bf16(hv, b1, acc1);
+          acc3 = mfma_bf16(hv, b3, acc3);
+          acc1 = mfma_bf16(lv, b1, acc1);
+          acc3 = mfma_bf16(lv, b3, acc3);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
   const __amdgpu_buffer_rsrc_t r = gu_rsrc(s.slots, s.nck * kGuSlotFloatsR);
@@ -876,6 +909,7 @@ __device__ __forceinline__ void gu_chunk(GuUnit &s, int u, int NK) {
 // not stall the weight stream.  VALU units are dealt round-robin after.
 __global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
   __shared__ __align__(16) uint16_t lds[2][kGuLds / 2];
+  __shared__ __align__(16) uint4 gws[kWavesPerBlock][256];  // each wave's weight pair rows (W1 | W3)
   __shared__ int tok_l[2][16];
   __shared__ int s_flag;
   const int tid = threadIdx.x;
@@ -930,8 +964,8 @@ __global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
       uint4 st[kGuStW];
       if (more) gu_stage_load(a, tok_l[b ^ 1], nx, st);
       asm volatile("" ::: "memory");  // issue the staging loads ahead of the weight stream
-      if (cur.ntl == 4) gu_unit<4>(a, cur, lds[b]);
-      else gu_unit<2>(a, cur, lds[b]);
+      if (cur.ntl == 4) gu_unit<4>(a, cur, lds[b], gws[tid >> 6]);
+      else gu_unit<2>(a, cur, lds[b], gws[tid >> 6]);
       if (more) gu_stage_store(st, nx, lds[b ^ 1]);
       // arrival: this workgroup's slot stores have completed before it is counted
       __builtin_amdgcn_s_waitcnt(0);
