@@ -18,7 +18,7 @@
 //                sums of r1^2.
 //              64 rows of Wqkv per workgroup, K = H split over 8 workgroups
 //                (4 when H % 1024 != 0) x 4 waves: partial qkv sums.
-//              Operands staged through LDS in 128-element K chunks.
+//              Operands loaded as whole cache lines, relaid through LDS.
 //  2 router_b  fp32 router dot products d[t, e] = hg[t] . Wr[e] on MFMA
 //              (v_mfma_f32_16x16x4_f32), 48 experts x 256 K per workgroup,
 //              tiles ordered so each XCD's workgroups share hg K chunks,
@@ -49,9 +49,12 @@
 // Weight loads.  A matrix-core operand fragment is 16 rows x 64 bytes per
 // load instruction (the next 64 bytes of each row follow in the next K
 // step), and these kernels read weights with ordinary cached loads: on this
-// pattern they stream measurably faster than non-temporal loads.  The
-// projections and the router instead stage whole 256-byte row segments in
-// LDS (4 rows per load instruction) and read the fragments from there.
+// pattern they stream measurably faster than non-temporal loads.  That
+// pattern touches 16 half-used cache lines per instruction, so the weights
+// are loaded as whole lines instead (4 or 8 rows x 256 or 128 contiguous
+// bytes per instruction) and moved into the fragment layout through LDS:
+// by each wave through its own rows in the projections, gate/up and down,
+// and by global-to-LDS loads in the router.
 //
 // Every output element is produced by one thread, in an order that depends
 // only on the shapes, so results are bit-identical from run to run.
@@ -168,52 +171,70 @@ __device__ __forceinline__ void mfma_tiles(const uint16_t *const (&wp)[NR], cons
   }
 }
 
-// The same product with both operands staged through LDS.  A wave stages one
-// 128-element K chunk (four matrix-core K steps) of its NR*16 weight rows and
-// NC*16 token rows at a time, 256 bytes per row, loaded straight from memory
-// into LDS: one load instruction covers 4 rows x 256 contiguous bytes (8 whole
-// cache lines), where the matrix-core operand pattern touches 16 half lines.
-// Row R keeps its 16-byte word c at slot c ^ (R & 15), so the operand reads
-// (16 rows x one word) hit 16 different bank groups.  (The compiler waits for
-// every load into LDS before any LDS read, so the chunk is single-buffered:
-// one memory round trip per chunk.)
-constexpr int kStgRows = 128;                 // rows of the buffer (weights then tokens)
-constexpr int kStgWords = kStgRows * 16;      // 16-byte words of the buffer (32 KB)
-__device__ __forceinline__ int stg_slot(int row, int c) { return row * 16 + (c ^ (row & 15)); }
+constexpr int kPjRowWords = 128 * 8;  // 16-byte words of one wave's relayout rows (128 rows x 128 bytes)
 
+// The same product with the operands loaded into registers as 8 rows x 128
+// contiguous bytes per instruction (whole cache lines; 64-element K chunks,
+// two matrix-core K steps) and moved into the matrix-core layout through the
+// wave's own LDS rows (word c of row R at slot c ^ ((R >> 1) & 7), free of
+// bank conflicts).  The next chunk's loads are issued before the current
+// chunk is used (two register buffers), so the loads overlap the work.
 template <int NR, int NC>
-__device__ __forceinline__ void mfma_tiles_lds(const uint16_t *w0, size_t wld, int nw, const uint16_t *a0, size_t ald,
-                                               int na, int nks, uint4 *buf, f32x4 (&acc)[NR][NC]) {
-  static_assert((NR + NC) * 16 <= kStgRows, "buffer rows");
-  constexpr int NI = (NR + NC) * 16 / 4;  // load instructions per chunk (4 rows each)
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  for (int j = 0; 4 * j < nks; ++j) {
+__device__ __forceinline__ void mfma_tiles_reg(const uint16_t *w0, size_t wld, int nw, const uint16_t *a0, size_t ald,
+                                               int na, int nks, uint4 *ws, f32x4 (&acc)[NR][NC]) {
+  constexpr int NI = (NR + NC) * 2;  // load instructions per chunk (8 rows each)
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, lr = lane >> 3, lw = lane & 7;
+  const int nch = (nks + 1) >> 1;
+  auto load = [&](int j, uint4 (&v)[NI]) {
+    j = min(j, nch - 1);  // past the last chunk: reload it (unused), so every load issues
+    const int wd = 2 * j + (lw >> 2) < nks ? lw : (lw & 3);  // a K step past the range re-reads step 2j
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      const int R = 4 * q + (lane >> 4), p = lane & 15;
-      int c = p ^ (R & 15);
-      if (4 * j + (c >> 2) >= nks) c &= 3;  // a K step past the wave's range: re-read step 4j (its product is skipped)
-      const uint16_t *src = R < NR * 16 ? w0 + (size_t)min(R, nw - 1) * wld + 128 * j + 8 * c
-                                        : a0 + (size_t)min(R - NR * 16, na - 1) * ald + 128 * j + 8 * c;
-      __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(buf + 64 * q), 16, 0,
-                                       0);
+      const int R = 8 * q + lr;
+      const uint16_t *src = R < NR * 16 ? w0 + (size_t)min(R, nw - 1) * wld + 64 * j + 8 * wd
+                                        : a0 + (size_t)min(R - NR * 16, na - 1) * ald + 64 * j + 8 * wd;
+      v[q] = ld16(src);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the chunk is in LDS
+  };
+  auto use = [&](int j, const uint4 (&v)[NI]) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      if (4 * j + s4 < nks) {
+    for (int q = 0; q < NI; ++q) {
+      const int R = 8 * q + lr;
+      ws[R * 8 + (lw ^ ((R >> 1) & 7))] = v[q];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows are written
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (2 * j + s2 < nks) {
         uint4 wv[NR], av[NC];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) wv[r] = buf[stg_slot(16 * r + n, 4 * s4 + g)];
+        for (int r = 0; r < NR; ++r) {
+          const int R = 16 * r + n;
+          wv[r] = ws[R * 8 + ((4 * s2 + g) ^ ((R >> 1) & 7))];
+        }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) av[c] = buf[stg_slot(NR * 16 + 16 * c + n, 4 * s4 + g)];
+        for (int c = 0; c < NC; ++c) {
+          const int R = NR * 16 + 16 * c + n;
+          av[c] = ws[R * 8 + ((4 * s2 + g) ^ ((R >> 1) & 7))];
+        }
 #pragma unroll
         for (int r = 0; r < NR; ++r)
 #pragma unroll
           for (int c = 0; c < NC; ++c) acc[r][c] = mfma_bf16(av[c], wv[r], acc[r][c]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this chunk's LDS reads are done before the next overwrites it
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next chunk overwrites the rows
+    __builtin_amdgcn_wave_barrier();
+  };
+  uint4 va[NI], vb[NI];
+  load(0, va);
+  for (int j = 0; j < nch; j += 2) {
+    load(j + 1, vb);
+    use(j, va);
+    if (j + 1 >= nch) break;
+    load(j + 2, va);
+    use(j + 1, vb);
   }
 }
 
@@ -222,10 +243,10 @@ __device__ __forceinline__ void mfma_tiles_lds(const uint16_t *w0, size_t wld, i
 // red[w][token][row]: wave w's partial sum.
 constexpr int kProjRows = 64;
 __global__ void __launch_bounds__(kBlock) proj_b(BatchArgs a, int n_wo) {
-  // staging buffers of the main loop, then the per-wave partial sums
-  __shared__ __align__(16) uint4 lds_raw[kWavesPerBlock * kStgWords];
+  // each wave's relayout rows during the main loop, then the per-wave partial sums
+  __shared__ __align__(16) uint4 lds_raw[kWavesPerBlock * kPjRowWords];
   float (*red)[kMaxBatch][kProjRows] = reinterpret_cast<float (*)[kMaxBatch][kProjRows]>(lds_raw);
-  static_assert(sizeof(float) * kWavesPerBlock * kMaxBatch * kProjRows <= sizeof(uint4) * kWavesPerBlock * kStgWords, "red fits");
+  static_assert(sizeof(float) * kWavesPerBlock * kMaxBatch * kProjRows <= sizeof(uint4) * kWavesPerBlock * kPjRowWords, "red fits");
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int B = a.B;
   const bool wo = (int)blockIdx.x < n_wo;
@@ -271,8 +292,8 @@ __global__ void __launch_bounds__(kBlock) proj_b(BatchArgs a, int n_wo) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     // rows r0.. of the weights and tokens 0.. from this wave's K start
-    mfma_tiles_lds<NR, NC>(wbase - 8 * g + (size_t)r0 * wld, wld, nrow - r0, abase - 8 * g, (size_t)ld, B, nks,
-                           lds_raw + wv * kStgWords, acc);
+    mfma_tiles_reg<NR, NC>(wbase - 8 * g + (size_t)r0 * wld, wld, nrow - r0, abase - 8 * g, (size_t)ld, B, nks,
+                           lds_raw + wv * kPjRowWords, acc);
     __syncthreads();  // the partial sums below overwrite other waves' staging buffers
 #pragma unroll
     for (int r = 0; r < NR; ++r)
