@@ -88,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.decode_layer_trace_points.restype = ctypes.c_int
         L.decode_layer_grid.argtypes = [ctypes.c_void_p]
         L.decode_layer_grid.restype = ctypes.c_int
+        L.decode_layer_set_spin_limit.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        L.decode_layer_set_spin_limit.restype = ctypes.c_int
+        L.decode_layer_set_step_counter.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
+        L.decode_layer_set_step_counter.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -129,6 +133,58 @@ def _ptr(t, dtype, shape, name):
     return t.data_ptr() if t.numel() else None
 
 
+def make_weights(cfg: Config, weights: dict) -> Weights:
+    """The C weights block for `cfg` from a dict of GPU tensors: w_qkv, w_o,
+    norm_gain, w_router, w1, w3, w2, s1, s3, s2 (bf16 except w_router fp32;
+    s1/s3/s2 absent iff shared_ffn 0).  Checks dtype, shape, contiguity and
+    device; the tensors are referenced, not copied."""
+    import torch
+    H, Dq, Do, E, F, Fs = (cfg.hidden, cfg.qkv_out, cfg.attn_dim, cfg.n_experts,
+                           cfg.expert_ffn, cfg.shared_ffn)
+    bf = torch.bfloat16
+    return Weights(
+        _ptr(weights["w_qkv"], bf, (Dq, H), "w_qkv"), _ptr(weights["w_o"], bf, (H, Do), "w_o"),
+        _ptr(weights["norm_gain"], bf, (H,), "norm_gain"),
+        _ptr(weights["w_router"], torch.float32, (E, H), "w_router"),
+        _ptr(weights["w1"], bf, (E, F, H), "w1"), _ptr(weights["w3"], bf, (E, F, H), "w3"),
+        _ptr(weights["w2"], bf, (E, H, F), "w2"),
+        _ptr(weights.get("s1"), bf, (Fs, H), "s1") if Fs else None,
+        _ptr(weights.get("s3"), bf, (Fs, H), "s3") if Fs else None,
+        _ptr(weights.get("s2"), bf, (H, Fs), "s2") if Fs else None)
+
+
+def make_io(cfg: Config, x, attn, resid_in, out) -> IO:
+    """The C per-step block from GPU tensors (see DecodeLayer.make_io)."""
+    import torch
+    B = x.shape[0]
+    bf, f32 = torch.bfloat16, torch.float32
+    return IO(B, _ptr(x, bf, (B, cfg.hidden), "x"), _ptr(attn, bf, (B, cfg.attn_dim), "attn"),
+              _ptr(resid_in, f32, (B, cfg.hidden), "resid_in"),
+              _ptr(out.qkv, f32, (B, cfg.qkv_out), "qkv"),
+              _ptr(out.resid_out, f32, (B, cfg.hidden), "resid_out"),
+              _ptr(out.router_logits, f32, (B, cfg.n_experts), "router_logits"),
+              _ptr(out.topk_idx, torch.int32, (B, cfg.top_k), "topk_idx"),
+              _ptr(out.topk_w, f32, (B, cfg.top_k), "topk_w"),
+              _ptr(out.moe_out, f32, (B, cfg.hidden), "moe_out"),
+              _ptr(out.h_out, f32, (B, cfg.hidden), "h_out"))
+
+
+def alloc_outputs(cfg: Config, batch: int, device="cuda", with_h: bool = False,
+                  with_logits: bool = True):
+    import torch
+    f32 = torch.float32
+    return StepOutputs(
+        torch.empty(batch, cfg.qkv_out, dtype=f32, device=device),
+        torch.empty(batch, cfg.hidden, dtype=f32, device=device),
+        torch.empty(batch, cfg.n_experts, dtype=f32, device=device) if with_logits else None,
+        torch.empty(batch, cfg.top_k, dtype=torch.int32, device=device),
+        torch.empty(batch, cfg.top_k, dtype=f32, device=device),
+        torch.empty(batch, cfg.hidden, dtype=f32, device=device),
+        torch.empty(batch, cfg.hidden, dtype=f32, device=device) if with_h else None)
+
+
+
+
 @dataclass
 class StepOutputs:
     qkv: object
@@ -146,24 +202,16 @@ class DecodeLayer:
     `weights` maps w_qkv, w_o, norm_gain, w_router, w1, w3, w2, s1, s3, s2 to
     GPU tensors (bf16 except w_router fp32; s1/s3/s2 absent iff shared_ffn 0).
     The tensors are referenced, not copied, and must stay unchanged.
+    With debug=True every step synchronises its stream and raises if the
+    device status word reports an expired hand-off wait.
     """
 
-    def __init__(self, cfg: Config, weights: dict, device: int = 0):
-        import torch
+    def __init__(self, cfg: Config, weights: dict, device: int = 0, debug: bool = False):
         self.cfg = cfg
+        self.debug = debug
         self._keep = dict(weights)
-        H, Dq, Do, E, F, Fs = (cfg.hidden, cfg.qkv_out, cfg.attn_dim, cfg.n_experts,
-                               cfg.expert_ffn, cfg.shared_ffn)
-        bf = torch.bfloat16
-        w = Weights(
-            _ptr(weights["w_qkv"], bf, (Dq, H), "w_qkv"), _ptr(weights["w_o"], bf, (H, Do), "w_o"),
-            _ptr(weights["norm_gain"], bf, (H,), "norm_gain"),
-            _ptr(weights["w_router"], torch.float32, (E, H), "w_router"),
-            _ptr(weights["w1"], bf, (E, F, H), "w1"), _ptr(weights["w3"], bf, (E, F, H), "w3"),
-            _ptr(weights["w2"], bf, (E, H, F), "w2"),
-            _ptr(weights.get("s1"), bf, (Fs, H), "s1") if Fs else None,
-            _ptr(weights.get("s3"), bf, (Fs, H), "s3") if Fs else None,
-            _ptr(weights.get("s2"), bf, (H, Fs), "s2") if Fs else None)
+        w = make_weights(cfg, weights)
+        self.weights_c = w
         h = ctypes.c_void_p()
         rc = lib().decode_layer_init(ctypes.byref(cfg), ctypes.byref(w), device, ctypes.byref(h))
         if rc != DL_OK:
@@ -210,13 +258,25 @@ class DecodeLayer:
         return lib().decode_layer_grid(self._h)
 
     def status(self, clear: bool = False) -> int:
-        """Device status word (synchronise first): bit 0 a hand-off wait expired,
-        bit 1 the step counter is exhausted."""
+        """Device status word (synchronise first): bit 0 a single-launch hand-off
+        wait expired since the last clear."""
         v = ctypes.c_uint32()
         rc = lib().decode_layer_status(self._h, ctypes.byref(v), int(clear))
         if rc != DL_OK:
             raise DecodeLayerError(rc, last_error(self._h))
         return int(v.value)
+
+    def set_spin_limit(self, rounds: int):
+        """Test support: polling rounds before a hand-off wait gives up."""
+        rc = lib().decode_layer_set_spin_limit(self._h, int(rounds))
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error(self._h))
+
+    def set_step_counter(self, last_tag: int):
+        """Test support: the device step counter (tag of the last step)."""
+        rc = lib().decode_layer_set_step_counter(self._h, int(last_tag))
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error(self._h))
 
     def set_profiling(self, enable: bool):
         rc = lib().decode_layer_set_profiling(self._h, int(enable))
@@ -233,32 +293,10 @@ class DecodeLayer:
 
     def alloc_outputs(self, batch: int, device="cuda", with_h: bool = False,
                       with_logits: bool = True) -> StepOutputs:
-        import torch
-        c = self.cfg
-        f32 = torch.float32
-        return StepOutputs(
-            torch.empty(batch, c.qkv_out, dtype=f32, device=device),
-            torch.empty(batch, c.hidden, dtype=f32, device=device),
-            torch.empty(batch, c.n_experts, dtype=f32, device=device) if with_logits else None,
-            torch.empty(batch, c.top_k, dtype=torch.int32, device=device),
-            torch.empty(batch, c.top_k, dtype=f32, device=device),
-            torch.empty(batch, c.hidden, dtype=f32, device=device),
-            torch.empty(batch, c.hidden, dtype=f32, device=device) if with_h else None)
+        return alloc_outputs(self.cfg, batch, device, with_h, with_logits)
 
     def make_io(self, x, attn, resid_in, out: StepOutputs) -> IO:
-        import torch
-        c = self.cfg
-        B = x.shape[0]
-        bf, f32 = torch.bfloat16, torch.float32
-        return IO(B, _ptr(x, bf, (B, c.hidden), "x"), _ptr(attn, bf, (B, c.attn_dim), "attn"),
-                  _ptr(resid_in, f32, (B, c.hidden), "resid_in"),
-                  _ptr(out.qkv, f32, (B, c.qkv_out), "qkv"),
-                  _ptr(out.resid_out, f32, (B, c.hidden), "resid_out"),
-                  _ptr(out.router_logits, f32, (B, c.n_experts), "router_logits"),
-                  _ptr(out.topk_idx, torch.int32, (B, c.top_k), "topk_idx"),
-                  _ptr(out.topk_w, f32, (B, c.top_k), "topk_w"),
-                  _ptr(out.moe_out, f32, (B, c.hidden), "moe_out"),
-                  _ptr(out.h_out, f32, (B, c.hidden), "h_out"))
+        return make_io(self.cfg, x, attn, resid_in, out)
 
     def step_io(self, io: IO, stream=None):
         """Enqueue one step from a prepared IO block on `stream` (default: current)."""
@@ -268,6 +306,12 @@ class DecodeLayer:
         rc = lib().decode_layer_step(self._h, ctypes.byref(io), ctypes.c_void_p(stream.cuda_stream))
         if rc != DL_OK:
             raise DecodeLayerError(rc, last_error(self._h))
+        if self.debug:
+            stream.synchronize()
+            st = self.status(clear=True)
+            if st:
+                raise DecodeLayerError(DL_ERR_HIP, f"device status {st:#x}: a hand-off wait expired "
+                                                   "(the step's dependent outputs are NaN)")
 
     def step(self, x, attn, resid_in, out: StepOutputs | None = None, stream=None,
              with_h: bool = False) -> StepOutputs:

@@ -587,11 +587,10 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
     else if (E <= 384) pick(std::integral_constant<int, 6>{});
     else if (E <= 512) pick(std::integral_constant<int, 8>{});
     else pick(std::integral_constant<int, kMaxExperts / kWave>{});
-    const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
-    const float ssum = wave_sum(s);
+    const float wgt = pick_weights(my_l, K);
     if (lane < K) {  // written through: the last workgroup reads them back
       __hip_atomic_store(a.topk_idx + (size_t)t * K + lane, my_idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.topk_w + (size_t)t * K + lane, s / ssum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.topk_w + (size_t)t * K + lane, wgt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (!arrive_last_wt(a.counter, B, &last_flag)) return;
@@ -989,7 +988,7 @@ __global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
       else gu_unit<2>(a, cur, lds[b], gws[tid >> 6]);
       if (more) gu_stage_store(st, nx, lds[b ^ 1]);
       // arrival: this workgroup's slot stores have completed before it is counted
-      __builtin_amdgcn_s_waitcnt(0);
+      wt_stores_complete();
       __syncthreads();
       if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(cur.arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1275,7 +1274,7 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(v4u, *reinterpret_cast<const f32x4 *>(ytile + 4 * q)), rs,
             (slot * tile_f + 4 * q) * 4, 0, kGuSc1);
-      __builtin_amdgcn_s_waitcnt(0);
+      wt_stores_complete();
       __syncthreads();
       if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(a.dn_cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -334,7 +334,33 @@ __device__ __forceinline__ void wave_topk(const float (&lv)[NC], int E, int K, i
 
 __device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }
 
+// Renormalised sigmoid weights of the k picks of one token, over one wave:
+// lane j < K holds the logit l_j of pick j (lane 0 the largest).  Returns, in
+// lane j < K, w_j = s_j / sum_i s_i with s = sigmoid(l), evaluated as
+// exp(ls_j - ls_0) / sum_i exp(ls_i - ls_0) with ls = log sigmoid(l)
+// = min(l, 0) - log1p(exp(-|l|)): the same value, but finite for logits whose
+// sigmoid underflows fp32 (below about -87), where s_j / sum s would be 0/0.
+// Every term of the sum lies in (0, 1] and the first is 1.
+__device__ __forceinline__ float pick_weights(float l, int K) {
+  const int lane = threadIdx.x & 63;
+  const float ls = fminf(l, 0.f) - log1pf(expf(-fabsf(l)));
+  const float ls0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ls)));
+  const float r = lane < K ? expf(ls - ls0) : 0.f;
+  return r / wave_sum(r);
+}
+
 // ---- cross-workgroup hand-off ------------------------------------------------
+// Waits until every memory operation this wave has issued has completed; for
+// stores written through to the device's coherence point (agent-scope atomic
+// stores, or buffer stores with the write-through bit), completion means the
+// value is visible to every other workgroup of the device.  The signal fences
+// keep the compiler from moving memory operations across the wait.
+__device__ __forceinline__ void wt_stores_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Every workgroup of a phase publishes its partial results, then counts
 // itself in `counter`; the workgroup that arrives last sees every other
 // workgroup's results.  Release (before the count) and acquire (after it)
@@ -366,7 +392,7 @@ __device__ __forceinline__ bool arrive_last(unsigned *counter, unsigned nblocks,
 // workgroup is counted.  An agent-scope fence would instead write back and
 // invalidate the whole L2 of the XCD, once per workgroup.
 __device__ __forceinline__ bool arrive_last_wt(unsigned *counter, unsigned nblocks, int *lds_flag) {
-  __builtin_amdgcn_s_waitcnt(0);
+  wt_stores_complete();
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -557,12 +557,12 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   const int st = tid - kCtl;  // stream-thread index (valid when !ctl)
   const int w = blockIdx.x, G = gridDim.x;
   const int B = a.B, E = a.E, K = a.K, H = a.H;
+  // this step's tag: the last step's tag + 1, skipping 0 (the tag of a slot
+  // never written); the step with the last tag clears every hand-off slot at
+  // its end, so after the wrap no slot holds a tag of the new round
   const unsigned epoch = *a.epoch;
-  if (epoch == 0xffffffffu) {  // tag space exhausted: refuse (status 2)
-    if (w == 0 && tid == 0) atomicOr(a.status, 2u);
-    return;
-  }
-  const unsigned tag = epoch + 1;
+  const unsigned tag = epoch == 0xffffffffu ? 1u : epoch + 1u;
+  const float kNaN = __builtin_nanf("");
   if (tid == 0) {
     L.bad = 0;
     L.arrive = 0;
@@ -579,9 +579,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     // the 8 partials in wave order and publishes them (no workgroup barrier).
     float sq = 0.f;
     if (ni > 0) by_tokens(B, [&](auto nt) { sq = oproj_rows<decltype(nt)::value>(a, L, i0, ni); });
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's device-scope hg stores have completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wt_stores_complete();  // this wave's device-scope hg stores have completed
     if (lane < B) L.sqw[wv][lane] = sq;
     int arrived = 0;
     if (lane == 0) arrived = __hip_atomic_fetch_add(&L.arrive, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -691,12 +689,17 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   stamp(a, 4);
+  // After a wait of this workgroup has expired, every value it publishes and
+  // every output it writes from then on is NaN (an index -1): the failure
+  // reaches the outputs instead of leaving stale values behind.  Indices used
+  // inside the kernel still come from the top-k, so they stay valid.
+  const bool poison_b = L.bad != 0;
 
   // ================= phase B: router logits and shared-expert rows ==========
   if (a.h_out && ni > 0)
     for (int q = tid; q < B * ni; q += kFT) {
       const int t = q / ni, il = q % ni;
-      a.h_out[(size_t)t * H + i0 + il] = L.hg[t][il] * L.inv_rms[t];
+      a.h_out[(size_t)t * H + i0 + il] = poison_b ? kNaN : L.hg[t][il] * L.inv_rms[t];
     }
   if (kind[0] || kind[1]) by_tokens(B, [&](auto tgc) {  // uniform over the workgroup
     const int nc = H >> 3;    // 8-element chunks c = tid + kFT*j
@@ -763,12 +766,13 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         sp[1] += L.red[((v * kFusedMaxB + t) * 2 + q) * 2 + 1];
       }
       if (kind[q] == 1) {
-        const float l = sp[0] * L.inv_rms[t];
+        const float l = poison_b ? kNaN : sp[0] * L.inv_rms[t];
         put_tagged(a.logit + (size_t)t * E + er[q], l, tag);
         if (a.logits_out) a.logits_out[(size_t)t * E + er[q]] = l;
       } else if (kind[q] == 2) {
         const int f = er[q] - E;
-        put_tagged(a.act_s + (size_t)t * a.Fs + f, silu_mul(sp[0] * L.inv_rms[t], sp[1] * L.inv_rms[t]), tag);
+        put_tagged(a.act_s + (size_t)t * a.Fs + f,
+                   poison_b ? kNaN : silu_mul(sp[0] * L.inv_rms[t], sp[1] * L.inv_rms[t]), tag);
       }
     }
   });
@@ -780,6 +784,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   else by_tokens(B, [&](auto nt) { qkv_rows<decltype(nt)::value>(a, L, w, G); });
   __syncthreads();
   stamp(a, 7);
+  const bool poison_c = L.bad != 0;
   for (int q = tid; q < kFusedQkvRows * B; q += kFT) {
     const int r = q / B, t = q % B, j = w + G * r;
     if (j < a.Dq)
@@ -806,15 +811,13 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     else pick(std::integral_constant<int, kFusedMaxE / 64>{});
     stamp(a, 15);
     // scores of the k picks, renormalised (lane j holds pick j)
-    const float s = lane < K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
-    const float ssum = wave_sum(s);
-    const float wgt = s / ssum;
+    const float wgt = pick_weights(my_l, K);
     if (lane < K) {
       L.sel[t * K + lane] = my_idx;
       L.selw[t * K + lane] = wgt;
       if (w == 0) {
-        a.topk_idx[(size_t)t * K + lane] = my_idx;
-        a.topk_w[(size_t)t * K + lane] = wgt;
+        a.topk_idx[(size_t)t * K + lane] = poison_c ? -1 : my_idx;
+        a.topk_w[(size_t)t * K + lane] = poison_c ? kNaN : wgt;
       }
     }
     if (B == 1) {
@@ -1016,11 +1019,12 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
           const int c2 = L.act_cnt[sk], o2 = L.act_off[sk];
           if (j < c2) {
             const int t = L.pair_tok[o2 + j];
-            put_tagged(a.act + (size_t)(o2 + j) * a.F + f2, silu_mul(su * L.inv_rms[t], sv * L.inv_rms[t]), tag);
+            put_tagged(a.act + (size_t)(o2 + j) * a.F + f2,
+                       poison_c ? kNaN : silu_mul(su * L.inv_rms[t], sv * L.inv_rms[t]), tag);
           }
         } else if (j < B) {
           put_tagged(a.act_s + (size_t)j * a.Fs + (fs_b + it - n_rt),
-                     silu_mul(su * L.inv_rms[j], sv * L.inv_rms[j]), tag);
+                     poison_c ? kNaN : silu_mul(su * L.inv_rms[j], sv * L.inv_rms[j]), tag);
         }
       }
       __syncthreads();
@@ -1048,15 +1052,35 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       d.compute();
     });
     __syncthreads();
+    const bool poison_d = L.bad != 0;
     for (int q = tid; q < B * ni; q += kFT) {
       const int t = q / ni, il = q % ni;
       float y = a.Fs > 0 ? L.u.d.contrib[t * kFusedMaxSlice + il] : 0.f;
       for (int r = 0; r < K; ++r) y += L.u.d.contrib[(B + L.pos[t * K + r]) * kFusedMaxSlice + il];
-      a.moe_out[(size_t)t * H + i0 + il] = y;
+      a.moe_out[(size_t)t * H + i0 + il] = poison_d ? kNaN : y;
     }
   }
   stamp(a, 11);
   __syncthreads();
+  if (tag == 0xffffffffu) {
+    // the last tag before the wrap: once every workgroup is past its last
+    // read of this step (a grid barrier on a monotonic arrival count), each
+    // clears its share of the hand-off slots back to tag 0
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(a.wrap, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned target = (prev / (unsigned)G + 1u) * (unsigned)G;
+      for (int n = 0; __hip_atomic_load(a.wrap, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++n) {
+        if (n >= a.spin_limit) {
+          L.bad = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();
+    for (size_t i = (size_t)w * kFT + tid; i < a.tag_words; i += (size_t)G * kFT)
+      __hip_atomic_store(a.tag_base + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   stamp(a, 3);
   if (tid == 0) {
     if (L.bad) atomicOr(a.status, 1u);

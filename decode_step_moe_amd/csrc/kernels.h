@@ -54,8 +54,11 @@ struct FusedArgs {
   uint64_t *logit;    // [B][E]
   uint64_t *act;      // [B*k][F]   routed SwiGLU activations, pairs grouped by expert
   uint64_t *act_s;    // [B][Fs]    shared SwiGLU activations
-  unsigned *epoch;    // steps completed on this handle
-  unsigned *status;   // bit 0: a hand-off wait expired; bit 1: step counter exhausted
+  unsigned *epoch;    // tag of the last step on this handle (0: none yet)
+  unsigned *status;   // bit 0: a hand-off wait expired
+  uint64_t *tag_base; // the hand-off slots (pss .. act_s, contiguous), cleared at the tag wrap
+  size_t tag_words;
+  unsigned *wrap;     // arrivals at the wrap step's grid barrier (monotonic)
   int B, H, Dq, Do, E, K, F, Fs;
   int slice;          // rows of H per workgroup, a multiple of 4
   float eps;

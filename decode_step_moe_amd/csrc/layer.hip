@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/decode_layer.h: validation,
-// the handle (scratch, second stream, events) and the launch sequence of one
-// step.  Nothing here computes layer math; every step of the layer runs in
-// the kernels of proj.hip, router.hip and experts.hip.
+// the handle (scratch, second stream, events), the static scratch of the
+// entry point that allocates nothing, and the launch sequence of one step.
+// Nothing here computes layer math; every step of the layer runs in the
+// kernels of fused.hip, batched.hip, proj.hip, router.hip and experts.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -9,24 +10,21 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <string>
 
 #include "../../include/decode_layer.h"
 #include "kernels.h"
+#include "layer_host.h"
 
 using namespace dl;
 
-namespace {
+namespace dl {
+namespace host {
 
 thread_local std::string g_thread_err = "no error";
-
-// Single-launch path: grid size and the largest batch its LDS layout allows.
-struct SinglePlan {
-  int grid = 0;       // workgroups = CUs
-  int slice = 0;      // rows of H per workgroup
-  int max_batch = 0;  // 0: path unavailable
-};
 
 int single_max_batch_for(const decode_layer_config &c, int grid, int slice) {
   if (grid < 1 || grid > kFusedMaxGrid || slice > kFusedMaxSlice) return 0;
@@ -65,37 +63,6 @@ bool batched_used(const decode_layer_config &c, const SinglePlan &sp) {
   return c.path == DL_PATH_AUTO && batched_ok(c) && c.max_batch > sp.max_batch;
 }
 
-struct Scratch {
-  float *hg = nullptr;        // [maxB][H]   g * r1
-  float *ss_part = nullptr;   // [nblk_o][maxB]
-  float *inv_rms = nullptr;   // [maxB]
-  float *logits = nullptr;    // [maxB][E]
-  int *pair_tok = nullptr;    // [maxB*k]
-  float *pair_w = nullptr;    // [maxB*k]
-  int *act_exp = nullptr;     // [E]
-  int *act_cnt = nullptr;     // [E]
-  int *act_off = nullptr;     // [E]
-  int *n_active = nullptr;    // [1]
-  float *act = nullptr;       // [maxB*k][F]
-  float *act_s = nullptr;     // [maxB][Fs]
-  unsigned *counters = nullptr;  // [3]: out-projection, router, batched top-k
-  // single-launch hand-off arrays (tagged 64-bit values)
-  uint64_t *pss = nullptr, *logit = nullptr, *act64 = nullptr, *act_s64 = nullptr;
-  unsigned *epoch = nullptr;     // [1] steps completed
-  unsigned *status = nullptr;    // [1]
-  // batched path (empty when no step can take it)
-  float *qkv_part = nullptr;     // [kBatchQkvSplit][maxB][Dq]
-  float *rlog_part = nullptr;    // [H/kBatchRtrK][maxB][E]
-  float *hn = nullptr;           // [maxB][H]
-  uint16_t *hp = nullptr;        // [2][maxB][H]
-  int *gu_q = nullptr;           // [4 E] gate/up work lists
-  int *n_q = nullptr;            // [2]
-  float *gu_part = nullptr;      // routed group slots, then shared group slots
-  unsigned *gu_cnt = nullptr;    // routed group counters, then shared group counters
-  float *dn_part = nullptr;      // [H/64][dn slots][64][64] partial y tiles
-  unsigned *dn_cnt = nullptr;    // [H/64]
-};
-
 // Batched gate/up matrix-core groups: 16-token chunks of the routed experts
 // with >= 16 tokens (at most B*k/8 chunks) times the row groups of one
 // expert, and the shared expert's 16-token chunks (at most 4) times its row
@@ -106,39 +73,67 @@ size_t gu_groups_routed(const decode_layer_config &c) {
 size_t gu_groups_shared(const decode_layer_config &c) {
   return c.shared_ffn > 0 ? (size_t)(c.max_batch + 15) / 16 * (c.shared_ffn / std::min(kBatchGuRows, c.shared_ffn)) : 0;
 }
-
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
-
-constexpr int kNumBuf = 29;
-struct Layout {
-  size_t off[kNumBuf];
-  size_t total;
-};
 
 int nblk_o_of(const decode_layer_config &c) { return (c.hidden + kORowsPerBlock - 1) / kORowsPerBlock; }
 
 Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
   const size_t B = c.max_batch, H = c.hidden, E = c.n_experts, K = c.top_k;
-  const size_t Bs = sp.max_batch, G = sp.grid;
   const size_t Bb = batched_used(c, sp) ? B : 0;
+  (void)sp;
   const size_t sizes[kNumBuf] = {
+      // hand-off state
+      (size_t)kFusedMaxGrid * kFusedMaxB * 8, (size_t)kFusedBig * 8, (size_t)kFusedBig * 8, (size_t)kFusedActS * 8,
+      4, 4, 4, 3 * 4, kMaxGuGroups * 4, kMaxDnGroups * 4,
+      // step data
       B * H * 4, (size_t)nblk_o_of(c) * B * 4, B * 4, B * E * 4, B * K * 4, B * K * 4,
       E * 4, E * 4, E * 4, 4, B * K * (size_t)c.expert_ffn * 4, B * (size_t)(c.shared_ffn > 0 ? c.shared_ffn : 1) * 4,
-      3 * 4,
-      // single-launch arrays (empty when the path is unavailable)
-      G * Bs * 8, Bs * E * 8, Bs * K * (size_t)c.expert_ffn * 8, Bs * (size_t)c.shared_ffn * 8,
-      4, 4,
       // batched arrays
       (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2,
       Bb ? 4 * E * 4 : size_t(0), Bb ? size_t(8) : size_t(0),
       Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * batch_gu_chunks(c.hidden) * kGuSlotFloatsR * 4 : size_t(0),
-      Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * 4 : size_t(0),
-      Bb ? (H / 64) * batch_dn_slots(c.hidden) * kMaxBatch * 64 * 4 : size_t(0), Bb ? (H / 64) * 4 : size_t(0)};
+      Bb ? (H / 64) * batch_dn_slots(c.hidden) * kMaxBatch * 64 * 4 : size_t(0)};
   Layout L;
   size_t o = 0;
   for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
   L.total = o;
   return L;
+}
+
+Scratch bind_scratch(char *b, const Layout &L) {
+  Scratch s;
+  s.pss = (uint64_t *)(b + L.off[kBPss]);
+  s.logit = (uint64_t *)(b + L.off[kBLogit64]);
+  s.act64 = (uint64_t *)(b + L.off[kBAct64]);
+  s.act_s64 = (uint64_t *)(b + L.off[kBActS64]);
+  s.epoch = (unsigned *)(b + L.off[kBEpoch]);
+  s.status = (unsigned *)(b + L.off[kBStatus]);
+  s.wrap = (unsigned *)(b + L.off[kBWrap]);
+  s.counters = (unsigned *)(b + L.off[kBCounters]);
+  s.gu_cnt = (unsigned *)(b + L.off[kBGuCnt]);
+  s.dn_cnt = (unsigned *)(b + L.off[kBDnCnt]);
+  s.tag_words = (L.off[kBEpoch] - L.off[kBPss]) / 8;
+  s.hg = (float *)(b + L.off[kBHg]);
+  s.ss_part = (float *)(b + L.off[kBSsPart]);
+  s.inv_rms = (float *)(b + L.off[kBInvRms]);
+  s.logits = (float *)(b + L.off[kBLogits]);
+  s.pair_tok = (int *)(b + L.off[kBPairTok]);
+  s.pair_w = (float *)(b + L.off[kBPairW]);
+  s.act_exp = (int *)(b + L.off[kBActExp]);
+  s.act_cnt = (int *)(b + L.off[kBActCnt]);
+  s.act_off = (int *)(b + L.off[kBActOff]);
+  s.n_active = (int *)(b + L.off[kBNActive]);
+  s.act = (float *)(b + L.off[kBAct]);
+  s.act_s = (float *)(b + L.off[kBActS]);
+  s.qkv_part = (float *)(b + L.off[kBQkvPart]);
+  s.rlog_part = (float *)(b + L.off[kBRlogPart]);
+  s.hn = (float *)(b + L.off[kBHn]);
+  s.hp = (uint16_t *)(b + L.off[kBHp]);
+  s.gu_q = (int *)(b + L.off[kBGuQ]);
+  s.n_q = (int *)(b + L.off[kBNQ]);
+  s.gu_part = (float *)(b + L.off[kBGuPart]);
+  s.dn_part = (float *)(b + L.off[kBDnPart]);
+  return s;
 }
 
 int cu_count(int device) {
@@ -150,7 +145,10 @@ int cu_count(int device) {
 bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-}  // namespace
+}  // namespace host
+}  // namespace dl
+
+using namespace dl::host;
 
 struct decode_layer {
   decode_layer_config cfg;
@@ -160,6 +158,7 @@ struct decode_layer {
   Scratch s;
   SinglePlan single;
   int gu_grid = 0;         // workgroups of the batched gate/up launch
+  int spin_limit = kDefaultSpinLimit;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   void *trace = nullptr;   // caller's device buffer for the phase trace
@@ -170,20 +169,23 @@ struct decode_layer {
   std::string err = "no error";
 };
 
-// Event pair around launch `i` when profiling is on.
+namespace dl {
+namespace host {
+
+// Event pair around launch `i` when profiling is on (h may be NULL: no profiling).
 struct ProfScope {
   decode_layer *h;
   int i;
   hipStream_t s;
   hipError_t begin() {
-    if (!h->profiling) return hipSuccess;
+    if (!h || !h->profiling) return hipSuccess;
     h->launched[i] = true;
     return hipEventRecord(h->ev_prof[i][0], s);
   }
-  hipError_t end() { return h->profiling ? hipEventRecord(h->ev_prof[i][1], s) : hipSuccess; }
+  hipError_t end() { return h && h->profiling ? hipEventRecord(h->ev_prof[i][1], s) : hipSuccess; }
 };
 
-static int fail(decode_layer *h, int code, const char *fmt, ...) {
+int fail(decode_layer *h, int code, const char *fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -194,7 +196,7 @@ static int fail(decode_layer *h, int code, const char *fmt, ...) {
   return code;
 }
 
-static int check_config(const decode_layer_config *c, decode_layer *h) {
+int check_config(const decode_layer_config *c, decode_layer *h) {
   if (!c) return fail(h, DL_ERR_INVALID_ARG, "config is NULL");
   if (c->hidden < 8 || c->hidden > 16384 || c->hidden % 8)
     return fail(h, DL_ERR_UNSUPPORTED, "hidden=%d: need 8..16384 and a multiple of 8", c->hidden);
@@ -223,7 +225,7 @@ static int check_config(const decode_layer_config *c, decode_layer *h) {
   return DL_OK;
 }
 
-static int check_weights(const decode_layer_config *c, const decode_layer_weights *w, decode_layer *h) {
+int check_weights(const decode_layer_config *c, const decode_layer_weights *w, decode_layer *h) {
   if (!w) return fail(h, DL_ERR_INVALID_ARG, "weights is NULL");
   const void *req[] = {w->w_qkv, w->w_o, w->norm_gain, w->w_router, w->w1, w->w3, w->w2};
   const char *names[] = {"w_qkv", "w_o", "norm_gain", "w_router", "w1", "w3", "w2"};
@@ -240,7 +242,7 @@ static int check_weights(const decode_layer_config *c, const decode_layer_weight
   return DL_OK;
 }
 
-static int check_io(const decode_layer_config *c, const decode_layer_io *io, decode_layer *h) {
+int check_io(const decode_layer_config *c, const decode_layer_io *io, decode_layer *h) {
   if (!io) return fail(h, DL_ERR_INVALID_ARG, "io is NULL");
   if (io->batch < 0) return fail(h, DL_ERR_INVALID_ARG, "batch=%d is negative", io->batch);
   if (io->batch > c->max_batch)
@@ -264,11 +266,274 @@ static int check_io(const decode_layer_config *c, const decode_layer_io *io, dec
   return DL_OK;
 }
 
+}  // namespace host
+}  // namespace dl
+
 #define HIP_TRY(h, expr)                                                                         \
   do {                                                                                           \
     hipError_t e_ = (expr);                                                                      \
     if (e_ != hipSuccess) return fail(h, DL_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
+
+namespace dl {
+namespace host {
+
+int enqueue_step(const StepCtx &x, const decode_layer_io *io, hipStream_t st) {
+  decode_layer *h = x.h;
+  const decode_layer_config &c = *x.c;
+  const decode_layer_weights &W = *x.w;
+  const Scratch &S = *x.s;
+  const int B = io->batch;
+  const bool single = (c.path == DL_PATH_AUTO || c.path == DL_PATH_SINGLE) && B <= x.single->max_batch;
+  if (c.path == DL_PATH_SINGLE && !single)
+    return fail(h, DL_ERR_UNSUPPORTED, "batch=%d exceeds the single-launch limit %d", B, x.single->max_batch);
+  const bool batched = !single && batched_used(c, *x.single);
+  const bool prof = h && h->profiling;
+  if (prof)
+    for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i) h->launched[i] = false;
+  if (single) {
+    FusedArgs fa{};
+    fa.x = (const uint16_t *)io->x;
+    fa.w_qkv = (const uint16_t *)W.w_qkv;
+    fa.qkv = io->qkv;
+    fa.attn = (const uint16_t *)io->attn;
+    fa.w_o = (const uint16_t *)W.w_o;
+    fa.gain = (const uint16_t *)W.norm_gain;
+    fa.resid_in = io->resid_in;
+    fa.resid_out = io->resid_out;
+    fa.w_router = W.w_router;
+    fa.logits_out = io->router_logits;
+    fa.topk_idx = io->topk_idx;
+    fa.topk_w = io->topk_w;
+    fa.w1 = (const uint16_t *)W.w1;
+    fa.w3 = (const uint16_t *)W.w3;
+    fa.w2 = (const uint16_t *)W.w2;
+    fa.s1 = (const uint16_t *)W.s1;
+    fa.s3 = (const uint16_t *)W.s3;
+    fa.s2 = (const uint16_t *)W.s2;
+    fa.moe_out = io->moe_out;
+    fa.h_out = io->h_out;
+    fa.hg = S.hg;
+    fa.pss = S.pss;
+    fa.logit = S.logit;
+    fa.act = S.act64;
+    fa.act_s = S.act_s64;
+    fa.epoch = S.epoch;
+    fa.status = S.status;
+    fa.tag_base = S.pss;
+    fa.tag_words = S.tag_words;
+    fa.wrap = S.wrap;
+    fa.B = B;
+    fa.H = c.hidden;
+    fa.Dq = c.qkv_out;
+    fa.Do = c.attn_dim;
+    fa.E = c.n_experts;
+    fa.K = c.top_k;
+    fa.F = c.expert_ffn;
+    fa.Fs = c.shared_ffn;
+    fa.slice = x.single->slice;
+    fa.eps = c.rms_eps;
+    fa.spin_limit = x.spin_limit;
+    fa.trace = (uint64_t *)x.trace;
+    ProfScope p5{h, 5, st};
+    HIP_TRY(h, p5.begin());
+    HIP_TRY(h, launch_fused(fa, x.single->grid, st));
+    HIP_TRY(h, p5.end());
+    if (prof) h->profiled_step = true;
+    return DL_OK;
+  }
+  if (batched) {
+    BatchArgs ba{};
+    ba.x = (const uint16_t *)io->x;
+    ba.w_qkv = (const uint16_t *)W.w_qkv;
+    ba.qkv = io->qkv;
+    ba.attn = (const uint16_t *)io->attn;
+    ba.w_o = (const uint16_t *)W.w_o;
+    ba.gain = (const uint16_t *)W.norm_gain;
+    ba.resid_in = io->resid_in;
+    ba.resid_out = io->resid_out;
+    ba.w_router = W.w_router;
+    ba.logits_out = io->router_logits;
+    ba.topk_idx = io->topk_idx;
+    ba.topk_w = io->topk_w;
+    ba.w1 = (const uint16_t *)W.w1;
+    ba.w3 = (const uint16_t *)W.w3;
+    ba.w2 = (const uint16_t *)W.w2;
+    ba.s1 = (const uint16_t *)W.s1;
+    ba.s3 = (const uint16_t *)W.s3;
+    ba.s2 = (const uint16_t *)W.s2;
+    ba.moe_out = io->moe_out;
+    ba.h_out = io->h_out;
+    ba.hg = S.hg;
+    ba.ss_part = S.ss_part;
+    ba.qkv_part = S.qkv_part;
+    ba.rlog_part = S.rlog_part;
+    ba.hn = S.hn;
+    ba.hp = S.hp;
+    ba.act = S.act;
+    ba.act_s = S.act_s;
+    ba.n_active = S.n_active;
+    ba.act_exp = S.act_exp;
+    ba.act_cnt = S.act_cnt;
+    ba.act_off = S.act_off;
+    ba.pair_tok = S.pair_tok;
+    ba.pair_w = S.pair_w;
+    ba.gu_q = S.gu_q;
+    ba.n_q = S.n_q;
+    ba.gu_part = S.gu_part;
+    ba.gu_part_s = S.gu_part + gu_groups_routed(c) * batch_gu_chunks(c.hidden) * kGuSlotFloatsR;
+    ba.gu_cnt = S.gu_cnt;
+    ba.gu_cnt_s = S.gu_cnt + gu_groups_routed(c);
+    ba.gu_grid = x.gu_grid;
+    ba.qkv_split = c.hidden % 1024 == 0 ? kBatchQkvSplit : kBatchQkvSplit / 2;
+    ba.dn_part = S.dn_part;
+    ba.dn_cnt = S.dn_cnt;
+    ba.dn_slots = batch_dn_slots(c.hidden);
+    ba.counter = S.counters + 2;
+    ba.B = B;
+    ba.H = c.hidden;
+    ba.Dq = c.qkv_out;
+    ba.Do = c.attn_dim;
+    ba.E = c.n_experts;
+    ba.K = c.top_k;
+    ba.F = c.expert_ffn;
+    ba.Fs = c.shared_ffn;
+    ba.eps = c.rms_eps;
+    if (prof)
+      for (int i = 0; i < kBatchLaunches; ++i) h->launched[6 + i] = true;
+    HIP_TRY(h, launch_batched(ba, st, prof ? &h->ev_prof[6] : nullptr));
+    if (prof) h->profiled_step = true;
+    return DL_OK;
+  }
+
+  ProjArgs pa{};
+  pa.x = (const uint16_t *)io->x;
+  pa.w_qkv = (const uint16_t *)W.w_qkv;
+  pa.qkv = io->qkv;
+  pa.attn = (const uint16_t *)io->attn;
+  pa.w_o = (const uint16_t *)W.w_o;
+  pa.gain = (const uint16_t *)W.norm_gain;
+  pa.resid_in = io->resid_in;
+  pa.resid_out = io->resid_out;
+  pa.hg = S.hg;
+  pa.ss_part = S.ss_part;
+  pa.inv_rms = S.inv_rms;
+  pa.counter = S.counters + 0;
+  pa.B = B;
+  pa.H = c.hidden;
+  pa.Dq = c.qkv_out;
+  pa.Do = c.attn_dim;
+  pa.eps = c.rms_eps;
+  pa.nblk_o = nblk_o_of(c);
+  pa.nblk_qkv = (c.qkv_out + kQkvRowsPerBlock - 1) / kQkvRowsPerBlock;
+  ProfScope p0{h, 0, st};
+  HIP_TRY(h, p0.begin());
+  HIP_TRY(h, launch_proj(pa, st));
+  HIP_TRY(h, p0.end());
+
+  // the shared expert's gate/up on the second stream (forked from and joined
+  // back into the caller's stream), or in order on the caller's stream
+  const hipStream_t sst = x.side ? x.side : st;
+  if (c.shared_ffn > 0) {
+    if (x.side) {
+      HIP_TRY(h, hipEventRecord(x.ev_fork, st));
+      HIP_TRY(h, hipStreamWaitEvent(x.side, x.ev_fork, 0));
+    }
+    GateUpArgs ga{};
+    ga.w1 = (const uint16_t *)W.s1;
+    ga.w3 = (const uint16_t *)W.s3;
+    ga.hg = S.hg;
+    ga.inv_rms = S.inv_rms;
+    ga.act = S.act_s;
+    ga.B = B;
+    ga.H = c.hidden;
+    ga.F = c.shared_ffn;
+    ga.shared = 1;
+    ProfScope p1{h, 1, sst};
+    HIP_TRY(h, p1.begin());
+    HIP_TRY(h, launch_gateup(ga, c.shared_ffn / kGateRowsPerBlock, sst));
+    HIP_TRY(h, p1.end());
+    if (x.side) HIP_TRY(h, hipEventRecord(x.ev_join, x.side));
+  }
+
+  RouterArgs ra{};
+  ra.w_router = W.w_router;
+  ra.hg = S.hg;
+  ra.inv_rms = S.inv_rms;
+  ra.logits = S.logits;
+  ra.logits_out = io->router_logits;
+  ra.h_out = io->h_out;
+  ra.topk_idx = io->topk_idx;
+  ra.topk_w = io->topk_w;
+  ra.n_active = S.n_active;
+  ra.act_exp = S.act_exp;
+  ra.act_cnt = S.act_cnt;
+  ra.act_off = S.act_off;
+  ra.pair_tok = S.pair_tok;
+  ra.pair_w = S.pair_w;
+  ra.counter = S.counters + 1;
+  ra.B = B;
+  ra.H = c.hidden;
+  ra.E = c.n_experts;
+  ra.K = c.top_k;
+  ProfScope p2{h, 2, st};
+  HIP_TRY(h, p2.begin());
+  HIP_TRY(h, launch_router(ra, st));
+  HIP_TRY(h, p2.end());
+
+  GateUpArgs ga{};
+  ga.w1 = (const uint16_t *)W.w1;
+  ga.w3 = (const uint16_t *)W.w3;
+  ga.hg = S.hg;
+  ga.inv_rms = S.inv_rms;
+  ga.act = S.act;
+  ga.n_active = S.n_active;
+  ga.act_exp = S.act_exp;
+  ga.act_cnt = S.act_cnt;
+  ga.act_off = S.act_off;
+  ga.pair_tok = S.pair_tok;
+  ga.B = B;
+  ga.H = c.hidden;
+  ga.F = c.expert_ffn;
+  ga.shared = 0;
+  {
+    int max_active = B * c.top_k < c.n_experts ? B * c.top_k : c.n_experts;
+    long items = (long)max_active * (c.expert_ffn / kGateRowsPerBlock);
+    int grid = (int)(items < 2048 ? items : 2048);
+    ProfScope p3{h, 3, st};
+    HIP_TRY(h, p3.begin());
+    HIP_TRY(h, launch_gateup(ga, grid, st));
+    HIP_TRY(h, p3.end());
+  }
+
+  if (c.shared_ffn > 0 && x.side) HIP_TRY(h, hipStreamWaitEvent(st, x.ev_join, 0));
+
+  DownArgs da{};
+  da.w2 = (const uint16_t *)W.w2;
+  da.s2 = (const uint16_t *)W.s2;
+  da.act = S.act;
+  da.act_s = S.act_s;
+  da.pair_w = S.pair_w;
+  da.n_active = S.n_active;
+  da.act_exp = S.act_exp;
+  da.act_cnt = S.act_cnt;
+  da.act_off = S.act_off;
+  da.pair_tok = S.pair_tok;
+  da.y = io->moe_out;
+  da.B = B;
+  da.H = c.hidden;
+  da.F = c.expert_ffn;
+  da.Fs = c.shared_ffn;
+  ProfScope p4{h, 4, st};
+  HIP_TRY(h, p4.begin());
+  HIP_TRY(h, launch_down(da, st));
+  HIP_TRY(h, p4.end());
+  if (prof) h->profiled_step = true;
+  return DL_OK;
+}
+
+}  // namespace host
+}  // namespace dl
 
 extern "C" {
 
@@ -325,40 +590,11 @@ int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights
     h->scratch_base = nullptr;
     return cleanup(fail(h, DL_ERR_OOM, "hipMalloc of %zu scratch bytes failed", L.total));
   }
-  char *b = (char *)h->scratch_base;
-  h->s.hg = (float *)(b + L.off[0]);
-  h->s.ss_part = (float *)(b + L.off[1]);
-  h->s.inv_rms = (float *)(b + L.off[2]);
-  h->s.logits = (float *)(b + L.off[3]);
-  h->s.pair_tok = (int *)(b + L.off[4]);
-  h->s.pair_w = (float *)(b + L.off[5]);
-  h->s.act_exp = (int *)(b + L.off[6]);
-  h->s.act_cnt = (int *)(b + L.off[7]);
-  h->s.act_off = (int *)(b + L.off[8]);
-  h->s.n_active = (int *)(b + L.off[9]);
-  h->s.act = (float *)(b + L.off[10]);
-  h->s.act_s = (float *)(b + L.off[11]);
-  h->s.counters = (unsigned *)(b + L.off[12]);
-  h->s.pss = (uint64_t *)(b + L.off[13]);
-  h->s.logit = (uint64_t *)(b + L.off[14]);
-  h->s.act64 = (uint64_t *)(b + L.off[15]);
-  h->s.act_s64 = (uint64_t *)(b + L.off[16]);
-  h->s.epoch = (unsigned *)(b + L.off[17]);
-  h->s.status = (unsigned *)(b + L.off[18]);
-  h->s.qkv_part = (float *)(b + L.off[19]);
-  h->s.rlog_part = (float *)(b + L.off[20]);
-  h->s.hn = (float *)(b + L.off[21]);
-  h->s.hp = (uint16_t *)(b + L.off[22]);
-  h->s.gu_q = (int *)(b + L.off[23]);
-  h->s.n_q = (int *)(b + L.off[24]);
-  h->s.gu_part = (float *)(b + L.off[25]);
-  h->s.gu_cnt = (unsigned *)(b + L.off[26]);
-  h->s.dn_part = (float *)(b + L.off[27]);
-  h->s.dn_cnt = (unsigned *)(b + L.off[28]);
+  h->s = bind_scratch((char *)h->scratch_base, L);
   h->gu_grid = 2 * std::max(1, cu_count(device));
   // The hand-off counters start at zero and are re-armed by the kernels
   // themselves, and the tagged hand-off values start with tag 0, which no
-  // step uses (tags are the step counter + 1), so no step ever needs a memset.
+  // step uses, so no step ever needs a memset.
   if (hipMemset(h->scratch_base, 0, L.total) != hipSuccess) return cleanup(fail(h, DL_ERR_HIP, "hipMemset failed"));
   if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) {
     h->side = nullptr;
@@ -382,247 +618,10 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
   int rc = check_io(&h->cfg, io, h);
   if (rc != DL_OK) return rc;
   if (io->batch == 0) return DL_OK;
-  const decode_layer_config &c = h->cfg;
-  hipStream_t st = (hipStream_t)hip_stream;
-  const int B = io->batch;
-  const bool single = (c.path == DL_PATH_AUTO || c.path == DL_PATH_SINGLE) && B <= h->single.max_batch;
-  if (c.path == DL_PATH_SINGLE && !single)
-    return fail(h, DL_ERR_UNSUPPORTED, "batch=%d exceeds the single-launch limit %d", B, h->single.max_batch);
-  const bool batched = !single && batched_used(c, h->single);
   HIP_TRY(h, hipSetDevice(h->device));
-  if (h->profiling)
-    for (int i = 0; i < DECODE_LAYER_N_LAUNCHES; ++i) h->launched[i] = false;
-  if (single) {
-    FusedArgs fa{};
-    fa.x = (const uint16_t *)io->x;
-    fa.w_qkv = (const uint16_t *)h->w.w_qkv;
-    fa.qkv = io->qkv;
-    fa.attn = (const uint16_t *)io->attn;
-    fa.w_o = (const uint16_t *)h->w.w_o;
-    fa.gain = (const uint16_t *)h->w.norm_gain;
-    fa.resid_in = io->resid_in;
-    fa.resid_out = io->resid_out;
-    fa.w_router = h->w.w_router;
-    fa.logits_out = io->router_logits;
-    fa.topk_idx = io->topk_idx;
-    fa.topk_w = io->topk_w;
-    fa.w1 = (const uint16_t *)h->w.w1;
-    fa.w3 = (const uint16_t *)h->w.w3;
-    fa.w2 = (const uint16_t *)h->w.w2;
-    fa.s1 = (const uint16_t *)h->w.s1;
-    fa.s3 = (const uint16_t *)h->w.s3;
-    fa.s2 = (const uint16_t *)h->w.s2;
-    fa.moe_out = io->moe_out;
-    fa.h_out = io->h_out;
-    fa.hg = h->s.hg;
-    fa.pss = h->s.pss;
-    fa.logit = h->s.logit;
-    fa.act = h->s.act64;
-    fa.act_s = h->s.act_s64;
-    fa.epoch = h->s.epoch;
-    fa.status = h->s.status;
-    fa.B = B;
-    fa.H = c.hidden;
-    fa.Dq = c.qkv_out;
-    fa.Do = c.attn_dim;
-    fa.E = c.n_experts;
-    fa.K = c.top_k;
-    fa.F = c.expert_ffn;
-    fa.Fs = c.shared_ffn;
-    fa.slice = h->single.slice;
-    fa.eps = c.rms_eps;
-    fa.spin_limit = 1 << 20;   // about a second of polling per wait
-    fa.trace = (uint64_t *)h->trace;
-    ProfScope p5{h, 5, st};
-    HIP_TRY(h, p5.begin());
-    HIP_TRY(h, launch_fused(fa, h->single.grid, st));
-    HIP_TRY(h, p5.end());
-    if (h->profiling) h->profiled_step = true;
-    return DL_OK;
-  }
-  if (batched) {
-    BatchArgs ba{};
-    ba.x = (const uint16_t *)io->x;
-    ba.w_qkv = (const uint16_t *)h->w.w_qkv;
-    ba.qkv = io->qkv;
-    ba.attn = (const uint16_t *)io->attn;
-    ba.w_o = (const uint16_t *)h->w.w_o;
-    ba.gain = (const uint16_t *)h->w.norm_gain;
-    ba.resid_in = io->resid_in;
-    ba.resid_out = io->resid_out;
-    ba.w_router = h->w.w_router;
-    ba.logits_out = io->router_logits;
-    ba.topk_idx = io->topk_idx;
-    ba.topk_w = io->topk_w;
-    ba.w1 = (const uint16_t *)h->w.w1;
-    ba.w3 = (const uint16_t *)h->w.w3;
-    ba.w2 = (const uint16_t *)h->w.w2;
-    ba.s1 = (const uint16_t *)h->w.s1;
-    ba.s3 = (const uint16_t *)h->w.s3;
-    ba.s2 = (const uint16_t *)h->w.s2;
-    ba.moe_out = io->moe_out;
-    ba.h_out = io->h_out;
-    ba.hg = h->s.hg;
-    ba.ss_part = h->s.ss_part;
-    ba.qkv_part = h->s.qkv_part;
-    ba.rlog_part = h->s.rlog_part;
-    ba.hn = h->s.hn;
-    ba.hp = h->s.hp;
-    ba.act = h->s.act;
-    ba.act_s = h->s.act_s;
-    ba.n_active = h->s.n_active;
-    ba.act_exp = h->s.act_exp;
-    ba.act_cnt = h->s.act_cnt;
-    ba.act_off = h->s.act_off;
-    ba.pair_tok = h->s.pair_tok;
-    ba.pair_w = h->s.pair_w;
-    ba.gu_q = h->s.gu_q;
-    ba.n_q = h->s.n_q;
-    ba.gu_part = h->s.gu_part;
-    ba.gu_part_s = h->s.gu_part + gu_groups_routed(c) * batch_gu_chunks(c.hidden) * kGuSlotFloatsR;
-    ba.gu_cnt = h->s.gu_cnt;
-    ba.gu_cnt_s = h->s.gu_cnt + gu_groups_routed(c);
-    ba.gu_grid = h->gu_grid;
-    ba.qkv_split = c.hidden % 1024 == 0 ? kBatchQkvSplit : kBatchQkvSplit / 2;
-    ba.dn_part = h->s.dn_part;
-    ba.dn_cnt = h->s.dn_cnt;
-    ba.dn_slots = batch_dn_slots(c.hidden);
-    ba.counter = h->s.counters + 2;
-    ba.B = B;
-    ba.H = c.hidden;
-    ba.Dq = c.qkv_out;
-    ba.Do = c.attn_dim;
-    ba.E = c.n_experts;
-    ba.K = c.top_k;
-    ba.F = c.expert_ffn;
-    ba.Fs = c.shared_ffn;
-    ba.eps = c.rms_eps;
-    if (h->profiling)
-      for (int i = 0; i < kBatchLaunches; ++i) h->launched[6 + i] = true;
-    HIP_TRY(h, launch_batched(ba, st, h->profiling ? &h->ev_prof[6] : nullptr));
-    if (h->profiling) h->profiled_step = true;
-    return DL_OK;
-  }
-
-  ProjArgs pa{};
-  pa.x = (const uint16_t *)io->x;
-  pa.w_qkv = (const uint16_t *)h->w.w_qkv;
-  pa.qkv = io->qkv;
-  pa.attn = (const uint16_t *)io->attn;
-  pa.w_o = (const uint16_t *)h->w.w_o;
-  pa.gain = (const uint16_t *)h->w.norm_gain;
-  pa.resid_in = io->resid_in;
-  pa.resid_out = io->resid_out;
-  pa.hg = h->s.hg;
-  pa.ss_part = h->s.ss_part;
-  pa.inv_rms = h->s.inv_rms;
-  pa.counter = h->s.counters + 0;
-  pa.B = B;
-  pa.H = c.hidden;
-  pa.Dq = c.qkv_out;
-  pa.Do = c.attn_dim;
-  pa.eps = c.rms_eps;
-  pa.nblk_o = nblk_o_of(c);
-  pa.nblk_qkv = (c.qkv_out + kQkvRowsPerBlock - 1) / kQkvRowsPerBlock;
-  ProfScope p0{h, 0, st};
-  HIP_TRY(h, p0.begin());
-  HIP_TRY(h, launch_proj(pa, st));
-  HIP_TRY(h, p0.end());
-
-  if (c.shared_ffn > 0) {
-    HIP_TRY(h, hipEventRecord(h->ev_fork, st));
-    HIP_TRY(h, hipStreamWaitEvent(h->side, h->ev_fork, 0));
-    GateUpArgs ga{};
-    ga.w1 = (const uint16_t *)h->w.s1;
-    ga.w3 = (const uint16_t *)h->w.s3;
-    ga.hg = h->s.hg;
-    ga.inv_rms = h->s.inv_rms;
-    ga.act = h->s.act_s;
-    ga.B = B;
-    ga.H = c.hidden;
-    ga.F = c.shared_ffn;
-    ga.shared = 1;
-    ProfScope p1{h, 1, h->side};
-    HIP_TRY(h, p1.begin());
-    HIP_TRY(h, launch_gateup(ga, c.shared_ffn / kGateRowsPerBlock, h->side));
-    HIP_TRY(h, p1.end());
-    HIP_TRY(h, hipEventRecord(h->ev_join, h->side));
-  }
-
-  RouterArgs ra{};
-  ra.w_router = h->w.w_router;
-  ra.hg = h->s.hg;
-  ra.inv_rms = h->s.inv_rms;
-  ra.logits = h->s.logits;
-  ra.logits_out = io->router_logits;
-  ra.h_out = io->h_out;
-  ra.topk_idx = io->topk_idx;
-  ra.topk_w = io->topk_w;
-  ra.n_active = h->s.n_active;
-  ra.act_exp = h->s.act_exp;
-  ra.act_cnt = h->s.act_cnt;
-  ra.act_off = h->s.act_off;
-  ra.pair_tok = h->s.pair_tok;
-  ra.pair_w = h->s.pair_w;
-  ra.counter = h->s.counters + 1;
-  ra.B = B;
-  ra.H = c.hidden;
-  ra.E = c.n_experts;
-  ra.K = c.top_k;
-  ProfScope p2{h, 2, st};
-  HIP_TRY(h, p2.begin());
-  HIP_TRY(h, launch_router(ra, st));
-  HIP_TRY(h, p2.end());
-
-  GateUpArgs ga{};
-  ga.w1 = (const uint16_t *)h->w.w1;
-  ga.w3 = (const uint16_t *)h->w.w3;
-  ga.hg = h->s.hg;
-  ga.inv_rms = h->s.inv_rms;
-  ga.act = h->s.act;
-  ga.n_active = h->s.n_active;
-  ga.act_exp = h->s.act_exp;
-  ga.act_cnt = h->s.act_cnt;
-  ga.act_off = h->s.act_off;
-  ga.pair_tok = h->s.pair_tok;
-  ga.B = B;
-  ga.H = c.hidden;
-  ga.F = c.expert_ffn;
-  ga.shared = 0;
-  {
-    int max_active = B * c.top_k < c.n_experts ? B * c.top_k : c.n_experts;
-    long items = (long)max_active * (c.expert_ffn / kGateRowsPerBlock);
-    int grid = (int)(items < 2048 ? items : 2048);
-    ProfScope p3{h, 3, st};
-    HIP_TRY(h, p3.begin());
-    HIP_TRY(h, launch_gateup(ga, grid, st));
-    HIP_TRY(h, p3.end());
-  }
-
-  if (c.shared_ffn > 0) HIP_TRY(h, hipStreamWaitEvent(st, h->ev_join, 0));
-
-  DownArgs da{};
-  da.w2 = (const uint16_t *)h->w.w2;
-  da.s2 = (const uint16_t *)h->w.s2;
-  da.act = h->s.act;
-  da.act_s = h->s.act_s;
-  da.pair_w = h->s.pair_w;
-  da.n_active = h->s.n_active;
-  da.act_exp = h->s.act_exp;
-  da.act_cnt = h->s.act_cnt;
-  da.act_off = h->s.act_off;
-  da.pair_tok = h->s.pair_tok;
-  da.y = io->moe_out;
-  da.B = B;
-  da.H = c.hidden;
-  da.F = c.expert_ffn;
-  da.Fs = c.shared_ffn;
-  ProfScope p4{h, 4, st};
-  HIP_TRY(h, p4.begin());
-  HIP_TRY(h, launch_down(da, st));
-  HIP_TRY(h, p4.end());
-  if (h->profiling) h->profiled_step = true;
-  return DL_OK;
+  const StepCtx x{&h->cfg, &h->w, &h->s, &h->single, h->gu_grid, h->side, h->ev_fork, h->ev_join,
+                  h->spin_limit, h->trace, h};
+  return enqueue_step(x, io, (hipStream_t)hip_stream);
 }
 
 int decode_layer_single_max_batch(const decode_layer *h) { return h ? h->single.max_batch : 0; }
@@ -633,10 +632,25 @@ int decode_layer_status(decode_layer *h, uint32_t *status, int clear) {
   unsigned v = 0;
   HIP_TRY(h, hipMemcpy(&v, h->s.status, sizeof v, hipMemcpyDeviceToHost));
   *status = v;
-  if (clear && (v & 1u)) {
-    unsigned keep = v & ~1u;
-    HIP_TRY(h, hipMemcpy(h->s.status, &keep, sizeof keep, hipMemcpyHostToDevice));
+  if (clear && v) {
+    unsigned zero = 0;
+    HIP_TRY(h, hipMemcpy(h->s.status, &zero, sizeof zero, hipMemcpyHostToDevice));
   }
+  return DL_OK;
+}
+
+int decode_layer_set_spin_limit(decode_layer *h, int rounds) {
+  if (!h) return fail(nullptr, DL_ERR_INVALID_ARG, "handle is NULL");
+  if (rounds < 0) return fail(h, DL_ERR_INVALID_ARG, "rounds=%d is negative", rounds);
+  h->spin_limit = rounds;
+  return DL_OK;
+}
+
+int decode_layer_set_step_counter(decode_layer *h, uint32_t last_tag) {
+  if (!h) return fail(nullptr, DL_ERR_INVALID_ARG, "handle is NULL");
+  HIP_TRY(h, hipSetDevice(h->device));
+  HIP_TRY(h, hipDeviceSynchronize());
+  HIP_TRY(h, hipMemcpy(h->s.epoch, &last_tag, sizeof last_tag, hipMemcpyHostToDevice));
   return DL_OK;
 }
 

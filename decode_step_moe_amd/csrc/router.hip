@@ -89,10 +89,8 @@ __device__ void topk_token(const RouterArgs &a, int t, int *s_sel, float *s_w) {
   int my_idx;
   float my_l;
   wave_topk<NC>(lv, a.E, a.K, my_idx, my_l);
-  const float my_s = lane < a.K ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
-  const float ssum = wave_sum(my_s);
+  const float w = pick_weights(my_l, a.K);
   if (lane < a.K) {
-    float w = my_s / ssum;
     a.topk_idx[(size_t)t * a.K + lane] = my_idx;
     a.topk_w[(size_t)t * a.K + lane] = w;
     s_sel[t * a.K + lane] = my_idx;

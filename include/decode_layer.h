@@ -46,6 +46,9 @@
 extern "C" {
 #endif
 
+/* Symbols of the C ABI (the library is built with hidden visibility). */
+#define DL_API __attribute__((visibility("default")))
+
 enum {
   DL_OK = 0,
   DL_ERR_INVALID_ARG = -1, /* NULL or misaligned pointer, negative size        */
@@ -63,6 +66,12 @@ enum {
  *   top_k k       : 1..min(E, 32)
  *   expert_ffn F  : 32, 64, 128 or 256
  *   shared_ffn Fs : 0 (no shared expert) or 32, 64, 128 or 256
+ *     (k and F are narrower than a generic MoE layer would need: the kernels
+ *     give each of the k picks of a token one lane of a wave-wide top-k and
+ *     size their per-token pick lists for 32, and they map an expert's ffn
+ *     row onto F/8 lanes of 16-byte loads, specialised for these four widths;
+ *     the shapes this library is measured on use k = 2 or 8 and F = 128 or
+ *     256.  Other values return DL_ERR_UNSUPPORTED, the pages' fallback case.)
  *   max_batch     : 1..64
  *   rms_eps       : > 0 and finite
  *   score_fn      : 0 = sigmoid (the only value supported)
@@ -156,60 +165,101 @@ typedef struct {
 typedef struct decode_layer decode_layer; /* opaque handle */
 
 /* Validate `cfg` and `w`, then create a handle on HIP device `device`:
- * allocates the handle's device scratch (a few MB at most), a second HIP
- * stream for the shared expert and the events that fork and join it.
- * No kernel runs.  On success *out receives the handle; on failure *out is
- * set to NULL.  Errors: DL_ERR_INVALID_ARG (NULL pointers, misaligned
- * weights), DL_ERR_UNSUPPORTED (shape outside the envelope), DL_ERR_HIP
- * (no such device), DL_ERR_OOM. */
-int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights *w,
-                      int device, decode_layer **out);
+ * allocates the handle's device scratch (decode_layer_scratch_bytes: under
+ * 1 MB at batch 1 on the single-launch path, tens of MB when the batched path
+ * can run at 64 tokens), a second HIP stream for the shared expert and the
+ * events that fork and join it.  No kernel runs.  The weights stay the
+ * caller's: the library reads them in place and never changes them (the
+ * pages' backend leaves weights, scheduling, sampling and the KV cache as
+ * they are: bigchange.ai "Kimi K3 vLLM GPU inference benchmark", opening
+ * section; wireai.ir "vLLM's speed jump on NVIDIA Blackwell servers; record
+ * 842 tokens/s for Kimi K3", "Conditions and limits for production
+ * deployment").
+ * On success *out receives the handle; on failure *out is set to NULL.
+ * Errors: DL_ERR_INVALID_ARG (NULL pointers, misaligned weights),
+ * DL_ERR_UNSUPPORTED (shape outside the envelope, or a forced path that
+ * cannot run it), DL_ERR_HIP (no such device), DL_ERR_OOM. */
+DL_API int decode_layer_init(const decode_layer_config *cfg, const decode_layer_weights *w,
+                             int device, decode_layer **out);
 
-/* Enqueue one layer-step on `hip_stream` (a hipStream_t; NULL = the null
- * stream) and return without synchronising.  Device work: on the single-launch
- * path one persistent kernel on `hip_stream`; on the batched path five kernel
- * launches on `hip_stream`; on the multi-launch path up to five kernel
- * launches, four on `hip_stream` and one (the shared expert's gate/up
- * projection) on the handle's second stream, which is forked from and joined
- * back into `hip_stream` with events.  Either can be captured in a HIP graph.
- * No allocation, no host copy, no memset.
- * The single-launch kernel needs all of its workgroups (one per CU) resident
- * at once; work on other streams may delay it but cannot deadlock it.  Its
- * waits are bounded: if one expires (about a second) the step's outputs are
- * undefined and decode_layer_status() reports it.
+/* Enqueue one layer-step - the attention input projection, the out-projection
+ * fused with the residual add and RMSNorm, the router with top-k, and the
+ * shared and routed SwiGLU experts (wireai.ir "vLLM's speed jump on NVIDIA
+ * Blackwell servers; record 842 tokens/s for Kimi K3", "Four key changes
+ * behind the jump", bullets 1-3; bigchange.ai "Kimi K3 vLLM GPU inference
+ * benchmark", "Where the time was going") - on `hip_stream` (a hipStream_t;
+ * NULL = the null stream) and return without synchronising.  Device work: on
+ * the single-launch path one persistent kernel on `hip_stream`; on the
+ * batched path five kernel launches on `hip_stream`; on the multi-launch path
+ * up to five kernel launches, four on `hip_stream` and one (the shared
+ * expert's gate/up projection) on the handle's second stream, which is forked
+ * from and joined back into `hip_stream` with events.  Either can be captured
+ * in a HIP graph.  No allocation, no host copy, no memset.
+ * The single-launch kernel is correct only when all of its workgroups (one
+ * per CU) are resident at once: it needs every CU of the device.  Work on
+ * other streams that finishes on its own (ordinary kernels, copies) only
+ * delays it.  Two single-launch steps in flight at once on one device (two
+ * handles stepped on different streams, or a graph replayed on two streams)
+ * can each hold part of the device while waiting for the rest: their
+ * hand-off waits then expire (about a second each).  A caller that steps
+ * handles concurrently must create them with DL_PATH_BATCHED or
+ * DL_PATH_MULTI, whose kernels need no co-residency.
+ * When a hand-off wait expires, the step still runs to completion, every
+ * output it computes from a value it did not receive is written as NaN (a
+ * topk_idx entry as -1), and decode_layer_status() reports bit 0; qkv and
+ * resid_out depend on no hand-off and stay exact.
  * `io` is validated on the host first (DL_ERR_INVALID_ARG /
  * DL_ERR_UNSUPPORTED, nothing enqueued).  A failed launch returns DL_ERR_HIP;
  * faults inside kernels surface at the caller's next synchronisation.
  * One step per handle may be in flight at a time (the scratch is per
- * handle); distinct handles may run concurrently. */
-int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stream);
+ * handle). */
+DL_API int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stream);
 
 /* Largest batch the single-launch path accepts with this handle (0 if none). */
-int decode_layer_single_max_batch(const decode_layer *h);
+DL_API int decode_layer_single_max_batch(const decode_layer *h);
 
 /* Device-side status of the handle, read synchronously (synchronise the
- * step's stream first).  Bits: 1 = a single-launch hand-off wait expired (that
- * step's outputs are undefined); 2 = the handle's 32-bit step counter is
- * exhausted (after 2^32 - 1 single-launch steps; the kernel then does nothing
- * and the handle must be re-created).  `clear` != 0 resets bit 1 afterwards.
+ * step's stream first).  Bit 0 (value 1): a single-launch hand-off wait
+ * expired in some step since the last clear (that step's affected outputs
+ * are NaN, see decode_layer_step).  The single-launch step counter is 32-bit
+ * and wraps: the step that uses its last value clears every hand-off slot,
+ * so the handle works indefinitely.  `clear` != 0 resets the word afterwards.
  * Returns DL_OK or DL_ERR_HIP / DL_ERR_INVALID_ARG. */
-int decode_layer_status(decode_layer *h, uint32_t *status, int clear);
+DL_API int decode_layer_status(decode_layer *h, uint32_t *status, int clear);
 
-/* Wait for the handle's streams, free its scratch, stream and events. NULL is a no-op. */
-int decode_layer_destroy(decode_layer *h);
+/* Wait for the handle's streams, free its scratch, stream and events (the
+ * resources decode_layer_init took; the caller's weights are untouched).
+ * NULL is a no-op.  Always returns DL_OK. */
+DL_API int decode_layer_destroy(decode_layer *h);
 
 /* Host-only check of a configuration (the validation decode_layer_init does
  * before touching the GPU).  Returns DL_OK, DL_ERR_INVALID_ARG or DL_ERR_UNSUPPORTED. */
-int decode_layer_check_config(const decode_layer_config *cfg);
+DL_API int decode_layer_check_config(const decode_layer_config *cfg);
 
 /* Host-only check of one step's arguments against a configuration (the
  * validation decode_layer_step does before enqueuing anything). */
-int decode_layer_check_io(const decode_layer_config *cfg, const decode_layer_io *io);
+DL_API int decode_layer_check_io(const decode_layer_config *cfg, const decode_layer_io *io);
 
 /* Text of the last error on `h`, or of the calling thread's last error when
- * `h` is NULL (e.g. a failed decode_layer_init).  Never NULL; the string is
- * owned by the library and valid until the next call on the same handle or thread. */
-const char *decode_layer_last_error(const decode_layer *h);
+ * `h` is NULL (e.g. a failed decode_layer_init): the reason a caller falls
+ * back to another backend for an unsupported step (wireai.ir "vLLM's speed
+ * jump on NVIDIA Blackwell servers; record 842 tokens/s for Kimi K3",
+ * "Conditions and limits for production deployment").  Never NULL; the
+ * string is owned by the library and valid until the next call on the same
+ * handle or thread. */
+DL_API const char *decode_layer_last_error(const decode_layer *h);
+
+/* Test support.  decode_layer_set_spin_limit sets the number of polling
+ * rounds after which a single-launch hand-off wait gives up (default 2^20,
+ * about a second); 0 makes every wait give up at its first unsatisfied poll,
+ * so the failure behaviour of decode_layer_step can be exercised while every
+ * kernel still finishes normally.  decode_layer_set_step_counter
+ * synchronises the device and sets the handle's single-launch step counter
+ * (the tag of the last step; the next step uses last_tag + 1, skipping 0),
+ * e.g. to run the counter's wrap.  Both return DL_OK or DL_ERR_INVALID_ARG /
+ * DL_ERR_HIP. */
+DL_API int decode_layer_set_spin_limit(decode_layer *h, int rounds);
+DL_API int decode_layer_set_step_counter(decode_layer *h, uint32_t last_tag);
 
 /* Measurement support, not needed for normal use.  While profiling is
  * enabled on a handle, every decode_layer_step also records a HIP event pair
@@ -226,8 +276,8 @@ const char *decode_layer_last_error(const decode_layer *h);
  * if profiling is off or no step ran since it was enabled).  Enabling creates
  * the events (DL_ERR_HIP on failure); do not enable it while capturing a graph. */
 #define DECODE_LAYER_N_LAUNCHES 11
-int decode_layer_set_profiling(decode_layer *h, int enable);
-int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
+DL_API int decode_layer_set_profiling(decode_layer *h, int enable);
+DL_API int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
 
 /* Phase trace of the single-launch kernel, for measurement.  With a non-NULL
  * device buffer of decode_layer_grid(h) * decode_layer_trace_points() uint64
@@ -241,17 +291,17 @@ int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
  * 9 routed SwiGLU activations published, 10 activations read, 11 y written,
  * 3 end; others unused.
  * NULL turns it off.  Returns DL_OK or DL_ERR_INVALID_ARG. */
-int decode_layer_set_trace(decode_layer *h, void *device_buffer);
-int decode_layer_trace_points(void);
+DL_API int decode_layer_set_trace(decode_layer *h, void *device_buffer);
+DL_API int decode_layer_trace_points(void);
 /* Workgroups of the single-launch kernel (the device's CU count; 0 if the path is unavailable). */
-int decode_layer_grid(const decode_layer *h);
+DL_API int decode_layer_grid(const decode_layer *h);
 
 /* Bytes of device scratch a handle with this configuration allocates on a
  * device with `n_cu` compute units (0 if the configuration is invalid).  The
  * single-launch path's hand-off arrays grow with n_cu; n_cu = 0 gives the size
  * without them.  The batched path's arrays are included when a step of this
  * configuration can take that path.  Host-only. */
-size_t decode_layer_scratch_bytes(const decode_layer_config *cfg, int n_cu);
+DL_API size_t decode_layer_scratch_bytes(const decode_layer_config *cfg, int n_cu);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ class LayerShape:
     top_k: int        # k
     expert_ffn: int   # F, routed expert ffn width on this shard
     shared_ffn: int   # Fs, shared expert ffn width on this shard
-    routing: str      # "natural" | "hot" | "zipf"
+    routing: str      # "natural" | "hot" | "zipf" | "skewed"
 
 
 SHAPES = {
@@ -106,20 +106,23 @@ class RawLayer:
 
 
 def draw(cfg: int, seed: int | None = None, batch: int | None = None,
-         top_k: int | None = None, shared_ffn: int | None = None) -> RawLayer:
+         top_k: int | None = None, shared_ffn: int | None = None,
+         routing: str | None = None) -> RawLayer:
     """Draw every tensor of workload `cfg` (default seed = cfg).
 
-    `batch`, `top_k` and `shared_ffn` override the workload's values (edge-case
-    tests); activations for a smaller batch are the leading rows of the full
-    draw, and every other tensor is drawn exactly as for the workload.
+    `batch`, `top_k`, `shared_ffn` and `routing` override the workload's
+    values (edge-case tests); activations for a smaller batch are the leading
+    rows of the full draw, and every other tensor is drawn exactly as for the
+    workload.
     """
     s = SHAPES[cfg]
-    if batch is not None or top_k is not None or shared_ffn is not None:
+    if batch is not None or top_k is not None or shared_ffn is not None or routing is not None:
         b = s.batch if batch is None else batch
         k = s.top_k if top_k is None else top_k
         fs = s.shared_ffn if shared_ffn is None else shared_ffn
-        s = LayerShape(s.name + f"_b{b}_k{k}_fs{fs}", s.hidden, b, s.qkv_out, s.attn_dim,
-                       s.n_experts, k, s.expert_ffn, fs, s.routing)
+        rt = s.routing if routing is None else routing
+        s = LayerShape(s.name + f"_b{b}_k{k}_fs{fs}_{rt}", s.hidden, b, s.qkv_out, s.attn_dim,
+                       s.n_experts, k, s.expert_ffn, fs, rt)
     if seed is None:
         seed = cfg
     H, B = s.hidden, s.batch

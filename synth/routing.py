@@ -25,7 +25,18 @@ Targets per routing mode:
             the order inside T[t] is shuffled.
   zipf    - expert popularity proportional to rank^-1.1 over a random expert
             permutation; T[t] = k draws without replacement.
-  For hot and zipf: L[t, T[t][j]] = max_e L0[t, e] + 0.5 + DELTA*(k-j).
+  skewed  - experts with the token counts SKEW_COUNTS (clipped to the batch),
+            the rest of the B*k picks spread over other experts with 1 to 8
+            tokens each; realised by giving each expert, largest count first,
+            the tokens with the most free slots (ties at random), which fills
+            every token's k slots exactly.  It puts routed experts on both
+            sides of the 16-token matrix-core threshold and at every chunk
+            shape a 64-token batch can produce (a partial second chunk, two
+            full chunks, all tokens).
+  For hot, zipf and skewed: L[t, T[t][j]] = max_e L0[t, e] + 0.5 + DELTA*(k-j).
+
+shape_router(..., shift=s) adds s[t] to every logit of token t (sigmoid
+saturation cases); the margins are unchanged.
 """
 from __future__ import annotations
 
@@ -39,6 +50,7 @@ from .gen import RawLayer, rng, S_ROUTE
 DELTA = 2e-2
 HOT_EXPERTS = 32
 ZIPF_S = 1.1
+SKEW_COUNTS = (64, 48, 33, 32, 31, 17, 16, 15, 9, 1)
 
 _DATA = os.path.join(os.path.dirname(os.path.abspath(__file__)), "data")
 # workloads whose h is stored (default seed = workload index)
@@ -91,7 +103,34 @@ def _zipf_targets(B: int, E: int, k: int, g: np.random.Generator) -> np.ndarray:
         if B > 0 else np.zeros((0, k), np.int64)
 
 
-def shape_router(raw: RawLayer, h: np.ndarray) -> RoutedLayer:
+def _skewed_targets(B: int, E: int, k: int, g: np.random.Generator) -> np.ndarray:
+    experts = g.permutation(E)
+    counts = [min(c, B) for c in SKEW_COUNTS]
+    while sum(counts) > B * k:
+        counts.pop()
+    load = list(zip(experts[:len(counts)].tolist(), counts))
+    rest, i = B * k - sum(counts), len(counts)
+    while rest > 0:
+        c = int(min(rest, g.integers(1, 9), B))
+        load.append((int(experts[i]), c))
+        rest -= c
+        i += 1
+    if i > E:
+        raise ValueError("not enough experts for the skewed loads")
+    free = np.full(B, k)
+    rows = [[] for _ in range(B)]
+    for e, c in sorted(load, key=lambda ec: -ec[1]):
+        order = np.lexsort((g.random(B), -free))   # most free slots first, ties at random
+        for t in order[:c]:
+            if free[t] == 0:
+                raise ValueError("skewed loads not realisable")
+            rows[t].append(e)
+            free[t] -= 1
+    assert np.all(free == 0)
+    return np.stack([g.permutation(np.asarray(r, np.int64)) for r in rows])
+
+
+def shape_router(raw: RawLayer, h: np.ndarray, shift=None) -> RoutedLayer:
     s = raw.shape
     B, E, k, H = s.batch, s.n_experts, s.top_k, s.hidden
     h = np.asarray(h, dtype=np.float64).reshape(B, H)
@@ -108,9 +147,12 @@ def shape_router(raw: RawLayer, h: np.ndarray) -> RoutedLayer:
         for t in range(B):
             L[t, T[t]] += bumps
     else:
-        T = _hot_targets(B, E, k, g) if s.routing == "hot" else _zipf_targets(B, E, k, g)
+        make = {"hot": _hot_targets, "zipf": _zipf_targets, "skewed": _skewed_targets}[s.routing]
+        T = make(B, E, k, g)
         for t in range(B):
             L[t, T[t]] = L0[t].max() + 0.5 + bumps
+    if shift is not None:
+        L += np.asarray(shift, np.float64).reshape(B, 1)
     M = np.linalg.lstsq(h @ h.T, L - L0, rcond=None)[0]      # [B][E]
     w_router = (N + M.T @ h).astype(np.float32)
     return RoutedLayer(raw, np.ascontiguousarray(w_router), T.astype(np.int32), L)

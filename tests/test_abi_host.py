@@ -65,32 +65,46 @@ def test_shared_expert_optional_and_scratch_size():
     assert dl.scratch_bytes(good()) > 0
 
 
-def test_single_launch_scratch_follows_the_plan():
-    """The single-launch hand-off arrays are sized by CU count and by the
-    largest batch that path takes (8 tokens here: 8 * top_k * F = 8192)."""
-    c = good()                       # TP16 shard shapes, max_batch 64
-    base = dl.scratch_bytes(c, 0)
-    with_single = dl.scratch_bytes(c, 256)
-    G, B, E, K, F, Fs = 256, 8, 384, 8, 128, 128
-    tagged = 8 * (G * B + B * E + B * K * F + B * Fs)
-    assert tagged <= with_single - base <= tagged + 8 * 256
-    c.path = dl.DL_PATH_MULTI        # multi-launch only: no single-launch arrays
-    assert dl.scratch_bytes(c, 256) == dl.scratch_bytes(c, 0)
-    big_h = dl.make_config(16384, 512, 512, 384, 8, 128, 128, 8)   # hidden above 8192
-    assert dl.scratch_bytes(big_h, 256) == dl.scratch_bytes(big_h, 0)
-    many_e = dl.make_config(7168, 512, 512, 1024, 8, 128, 128, 8)  # more than 512 experts
-    assert dl.scratch_bytes(many_e, 256) == dl.scratch_bytes(many_e, 0)
-    odd_fs = dl.make_config(7168, 512, 512, 384, 8, 128, 256, 8)   # shared ffn != expert ffn
-    assert dl.scratch_bytes(odd_fs, 256) == dl.scratch_bytes(odd_fs, 0)
-
-
 def _a256(n):
     return (n + 255) // 256 * 256
 
 
+# The hand-off region at the front of every scratch area: tagged words of the
+# single-launch path (norm partials [256][8], logits [8192], routed and shared
+# activations [8192], [4096]), the step counter, the status word, the wrap
+# barrier count, three arrival counters, and the batched path's gate/up group
+# and down row-group counters, all sized for the whole envelope.
+MAX_GU_GROUPS = (64 * 32 + 7) // 8 * (256 // 32) + (64 + 15) // 16 * (256 // 32)
+HANDOFF = (_a256(8 * 256 * 8) + 2 * _a256(8 * 8192) + _a256(8 * 4096) + 3 * 256 + _a256(12)
+           + _a256(4 * MAX_GU_GROUPS) + _a256(4 * (16384 // 64)))
+
+
+def _step_data(B, H, E, K, F, Fs):
+    nblk_o = -(-H // 16)
+    return (_a256(4 * B * H) + _a256(4 * nblk_o * B) + _a256(4 * B) + _a256(4 * B * E) + 2 * _a256(4 * B * K)
+            + 3 * _a256(4 * E) + 256 + _a256(4 * B * K * F) + _a256(4 * B * max(Fs, 1)))
+
+
+def test_handoff_region_is_configuration_independent():
+    """Every scratch area starts with the same hand-off region (so calls with
+    different configurations that share one area, as the static area of
+    decode_layer_step_noalloc is shared, never read each other's tagged
+    words or counters), followed by the step data of the configuration."""
+    cases = [(7168, 512, 512, 384, 8, 128, 128, 64), (7168, 1024, 1024, 384, 8, 256, 256, 64),
+             (512, 768, 768, 8, 2, 256, 0, 1), (16384, 512, 512, 1024, 32, 32, 64, 3)]
+    for (H, Dq, Do, E, K, F, Fs, B) in cases:
+        c = dl.make_config(H, Dq, Do, E, K, F, Fs, B, path=dl.DL_PATH_MULTI)
+        assert dl.scratch_bytes(c, 256) == HANDOFF + _step_data(B, H, E, K, F, Fs), (H, E, K, F, B)
+    # the single-launch path adds nothing beyond the hand-off region
+    small = dl.make_config(7168, 512, 512, 384, 8, 128, 128, 8)
+    small_multi = dl.make_config(7168, 512, 512, 384, 8, 128, 128, 8, path=dl.DL_PATH_MULTI)
+    assert dl.scratch_bytes(small, 256) == dl.scratch_bytes(small_multi, 256)
+
+
 def test_batched_scratch_follows_the_path():
     """The batched path's arrays (qkv and router partial sums, h in fp32 and
-    as bf16 hi + lo planes) exist exactly when some step can take that path."""
+    as bf16 hi + lo planes, gate/up and down partial tiles) exist exactly when
+    some step can take that path."""
     c = good()                       # TP16 shard shapes, max_batch 64
     B, H, Dq, E = 64, 7168, 512, 384
     F = Fs = 128
@@ -99,22 +113,20 @@ def test_batched_scratch_follows_the_path():
     chunks = (H // 32 + 13) // 14             # K chunks of 14 steps of 32: one partial slot each
     batched = (_a256(8 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
                + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(8)
-               + _a256((groups_r + groups_s) * chunks * 2048 * 4) + _a256((groups_r + groups_s) * 4)
-               + _a256((H // 64) * (-(-512 // (H // 64)) + 2) * 64 * 64 * 4) + _a256((H // 64) * 4))
+               + _a256((groups_r + groups_s) * chunks * 2048 * 4)
+               + _a256((H // 64) * (-(-512 // (H // 64)) + 2) * 64 * 64 * 4))
     auto = dl.scratch_bytes(c, 256)
     c.path = dl.DL_PATH_MULTI
     multi = dl.scratch_bytes(c, 256)
     c.path = dl.DL_PATH_BATCHED
     forced = dl.scratch_bytes(c, 256)
-    assert forced == dl.scratch_bytes(c, 0)     # no single-launch arrays when forced
-    assert auto - batched > multi               # AUTO: single-launch arrays on top
-    assert forced - batched == multi
+    assert forced == dl.scratch_bytes(c, 0)
+    assert auto == forced == multi + batched
     # a batch the single-launch path covers entirely: no batched arrays under AUTO
     small = dl.make_config(7168, 512, 512, 384, 8, 128, 128, 8)
-    small_multi = dl.make_config(7168, 512, 512, 384, 8, 128, 128, 8, path=dl.DL_PATH_MULTI)
-    G, Bs, K, F, Fs = 256, 8, 8, 128, 128
-    tagged = 8 * (G * Bs + Bs * E + Bs * K * F + Bs * Fs)
-    assert tagged <= dl.scratch_bytes(small, 256) - dl.scratch_bytes(small_multi, 256) <= tagged + 8 * 256
+    assert dl.scratch_bytes(small, 256) == HANDOFF + _step_data(8, 7168, 384, 8, 128, 128)
+    # without a single-launch plan (no CU count) AUTO takes the batched path for every batch
+    assert dl.scratch_bytes(small, 0) > dl.scratch_bytes(small, 256)
     # shapes the batched tiling cannot take: AUTO never allocates its arrays
     odd_h = dl.make_config(7168 + 256, 512, 512, 384, 8, 128, 128, 64)
     odd_h_multi = dl.make_config(7168 + 256, 512, 512, 384, 8, 128, 128, 64, path=dl.DL_PATH_MULTI)
@@ -168,6 +180,18 @@ def test_step_and_destroy_null_handle():
     assert lib.decode_layer_step(None, ctypes.byref(_io()), None) == dl.DL_ERR_INVALID_ARG
     assert lib.decode_layer_destroy(None) == dl.DL_OK
     assert lib.decode_layer_set_profiling(None, 1) == dl.DL_ERR_INVALID_ARG
+    assert lib.decode_layer_set_spin_limit(None, 0) == dl.DL_ERR_INVALID_ARG
+    assert lib.decode_layer_set_step_counter(None, 5) == dl.DL_ERR_INVALID_ARG
+
+
+def test_library_exports_only_the_abi():
+    """Built with hidden visibility: the dynamic symbol table holds the C ABI
+    of include/decode_layer.h and nothing else of the library's own."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", dl.binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    text_syms = sorted({ln.split()[-1] for ln in out.splitlines() if ln.split()[1:2] == ["T"]})
+    assert text_syms == header_functions(), set(text_syms) ^ set(header_functions())
 
 
 def test_init_without_gpu_fails_cleanly():

@@ -197,24 +197,31 @@ def test_batch_equals_single_token_steps():
             assert parity.max_abs(v, ref) <= 1e-5 * max(1.0, np.abs(ref).max()), key
 
 
-def test_repeated_steps_are_stable_under_concurrency():
-    """200 back-to-back steps with unrelated work on another stream: indices
+@pytest.mark.parametrize("cfg,path", [(2, AUTO), (3, AUTO), (2, BATCHED)])
+def test_repeated_steps_are_stable_under_concurrency(cfg, path):
+    """1000 back-to-back steps with unrelated work on another stream: indices
     and every output must be bit-identical each time (the kernels are
-    deterministic), which catches a hand-off read before its acquire."""
-    say("[stress 200 steps, cfg 2 shapes] start")
+    deterministic), which catches a hand-off read before its acquire.  The
+    single-launch path (batch 8) and the batched path (batch 64 with hot
+    experts on the matrix cores, and batch 8) each run it; the first
+    mismatching step ends the test."""
     from decode_step_moe_amd import DecodeLayer
-    layer = workload.build(2, h_source="stored")
-    cfg = sdev.config_of(layer)
-    obj = DecodeLayer(cfg, sdev.upload_weights(layer))
-    assert used_single(obj, 8, AUTO)
+    layer = workload.build(cfg, h_source="stored")
+    obj = DecodeLayer(sdev.config_of(layer, path=path), sdev.upload_weights(layer))
+    B = layer.shape.batch
+    say(f"[stress 1000 steps, cfg {cfg} batch {B}, {used_name(obj, B, path)} path] start")
+    assert used_single(obj, B, path) == (cfg == 2 and path == AUTO)
     x, attn, resid = sdev.upload_inputs(layer)
     first = obj.step(x, attn, resid)
     torch.cuda.synchronize()
+    got = {k: getattr(first, k).cpu().numpy() for k in ("qkv", "resid_out", "topk_idx", "topk_w", "moe_out")}
+    got["logits"] = first.router_logits.cpu().numpy()
+    check(layer, got, f"stress_first_cfg{cfg}")
     ref = {k: getattr(first, k).clone() for k in ("qkv", "resid_out", "topk_idx", "topk_w", "moe_out")}
     other = torch.cuda.Stream()
     junk = torch.randn(4096, 4096, device="cuda")
-    outs = [obj.alloc_outputs(layer.shape.batch) for _ in range(4)]
-    for it in range(200):
+    outs = [obj.alloc_outputs(B) for _ in range(4)]
+    for it in range(1000):
         with torch.cuda.stream(other):
             junk.mul_(1.0001)
         o = outs[it % 4]
@@ -224,6 +231,7 @@ def test_repeated_steps_are_stable_under_concurrency():
             for oo in outs:
                 for k, v in ref.items():
                     assert torch.equal(getattr(oo, k), v), (it, k)
+                    getattr(oo, k).fill_(-1)
     torch.cuda.synchronize()
     assert obj.status() == 0
 
@@ -364,3 +372,66 @@ def test_residual_scale_extremes(scale):
     fails = [f for f in m["fails"] if not f.startswith("resid_out")]
     assert not fails, fails
     assert m["resid_out_rel_l2"] <= parity.OUT_REL_L2
+
+
+_EXPECTED = {}
+
+
+def _skewed(batch):
+    key = ("skewed", batch)
+    if key not in _EXPECTED:
+        raw = gen.draw(3, batch=batch, routing="skewed")
+        layer = routing.shape_router(raw, workload.oracle_h(raw))
+        _EXPECTED[key] = (layer, workload.expected(layer))
+    return _EXPECTED[key]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("batch", [64, 33])
+def test_skewed_expert_loads(batch, path):
+    """TP8 shard shapes (ffn 256) with routed experts holding 1, 9, 15, 16,
+    17, 31, 32, 33, 48 and 64 tokens (clipped to the batch): both sides of the
+    16-token matrix-core threshold, a partial second 16-token chunk, two or
+    more full chunks, and an expert every token picked."""
+    say(f"[skewed expert loads, TP8 shapes, batch={batch} path={PATH_NAMES[path]}] start")
+    layer, ref = _skewed(batch)
+    loads = layer.expert_load()
+    say(f"[skewed b{batch}] loads: " + ",".join(str(v) for v in sorted(loads[loads > 0].tolist(), reverse=True)[:12]))
+    got, obj = run_gpu(layer, path=path)
+    m = parity.compare(got, ref)
+    tag = f"skewed_b{batch}_{used_name(obj, batch, path)}"
+    say(f"[{tag}] " + ", ".join(f"{k}={v:.3e}" for k, v in m.items() if k != "fails"))
+    assert not m["fails"], f"{tag}: {m['fails']}"
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_saturating_logits(path):
+    """Router logits shifted per token by +-30, +-60, +90, -100 and -200
+    (batch 8, TP16 shard): the sigmoid saturates at 1 or underflows fp32
+    (below about -87), and the renormalised weights must still match the
+    oracle's."""
+    say(f"[saturating logits, TP16 shard batch 8, path={PATH_NAMES[path]}] start")
+    raw = gen.draw(2)
+    shift = np.array([30.0, -30.0, 60.0, -60.0, 90.0, -100.0, 0.0, -200.0])
+    layer = routing.shape_router(raw, workload.oracle_h(raw), shift=shift)
+    ref = workload.expected(layer)
+    assert np.all(np.abs(ref["logits"].max(axis=1) - shift) < 8.0)
+    got, obj = run_gpu(layer, path=path)
+    assert np.all(np.isfinite(got["topk_w"]))
+    check(layer, got, f"saturating_{used_name(obj, 8, path)}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_negative_and_zero_gain(path):
+    """RMSNorm gain drawn N(0, 1) (about half negative) with some entries
+    exactly zero and some exactly -1 (speculative-verify shapes, Zipf routing)."""
+    say(f"[negative / zero gain, spec-verify shapes, path={PATH_NAMES[path]}] start")
+    raw = gen.draw(4)
+    g = gen.rng(1234, 7).normal(0.0, 1.0, size=raw.shape.hidden).astype(np.float32)
+    g[::97] = 0.0
+    g[5::101] = -1.0
+    raw.gain = gen.f32_to_bf16_bits(g)
+    assert np.mean(gen.bf16_bits_to_f32(raw.gain) < 0) > 0.4
+    layer = routing.shape_router(raw, workload.oracle_h(raw))
+    got, obj = run_gpu(layer, path=path)
+    check(layer, got, f"neg_gain_{used_name(obj, 8, path)}")
