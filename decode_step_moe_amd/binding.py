@@ -92,6 +92,13 @@ def lib() -> ctypes.CDLL:
         L.decode_layer_set_spin_limit.restype = ctypes.c_int
         L.decode_layer_set_step_counter.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
         L.decode_layer_set_step_counter.restype = ctypes.c_int
+        # -- no-alloc entry point: begin
+        L.decode_layer_step_noalloc.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
+                                                ctypes.POINTER(IO), ctypes.c_void_p]
+        L.decode_layer_step_noalloc.restype = ctypes.c_int
+        L.decode_layer_noalloc_max_scratch.argtypes = []
+        L.decode_layer_noalloc_max_scratch.restype = ctypes.c_size_t
+        # -- no-alloc entry point: end
         _lib = L
     return _lib
 
@@ -183,6 +190,23 @@ def alloc_outputs(cfg: Config, batch: int, device="cuda", with_h: bool = False,
         torch.empty(batch, cfg.hidden, dtype=f32, device=device) if with_h else None)
 
 
+# -- no-alloc entry point: begin
+def noalloc_max_scratch() -> int:
+    """Bytes of the static scratch area decode_layer_step_noalloc uses per device."""
+    return lib().decode_layer_noalloc_max_scratch()
+
+
+def step_noalloc(cfg: Config, weights: Weights, io: IO, stream=None):
+    """decode_layer_step_noalloc: one step with no handle and no device
+    allocation, on the current device (scratch in the library's static area)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = lib().decode_layer_step_noalloc(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(io),
+                                         ctypes.c_void_p(stream.cuda_stream))
+    if rc != DL_OK:
+        raise DecodeLayerError(rc, last_error())
+# -- no-alloc entry point: end
 
 
 @dataclass

@@ -303,6 +303,34 @@ DL_API int decode_layer_grid(const decode_layer *h);
  * configuration can take that path.  Host-only. */
 DL_API size_t decode_layer_scratch_bytes(const decode_layer_config *cfg, int n_cu);
 
+/* ---- one step with no handle and no allocation ----------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * decode_layer_step_noalloc validates `cfg`, `w` and `io` exactly as
+ * decode_layer_init and decode_layer_step do, then enqueues the same kernels
+ * as decode_layer_step would on a handle made from `cfg` and `w`, on the
+ * current HIP device (`hip_stream` must belong to it).  Instead of a handle's
+ * scratch it uses a static device area of decode_layer_noalloc_max_scratch()
+ * bytes (32 MiB), which every device the library runs on holds until the
+ * process ends; a configuration whose scratch (decode_layer_scratch_bytes)
+ * exceeds it returns DL_ERR_UNSUPPORTED with nothing enqueued (a smaller
+ * max_batch or DL_PATH_MULTI needs less; the batched path at 64 tokens needs
+ * more).  It calls no hipMalloc, hipFree or other allocating routine; the
+ * multi-launch path runs its shared-expert projection on `hip_stream` itself
+ * (there is no second stream).  The first call on a device looks up the
+ * area's address and, unless the stream is being captured, clears its
+ * hand-off state with a small kernel on `hip_stream`.
+ * Every call on a device shares that device's area, which keeps the last
+ * call's contents: calls whose work overlaps on one device (different
+ * streams, threads or graphs in flight together) race and give undefined
+ * results; calls ordered on one stream, or synchronised, are safe with any
+ * mix of configurations.  Wait expiries are not reported through a status
+ * word here; they show as NaN outputs (decode_layer_step).  Errors go to the
+ * calling thread's decode_layer_last_error(NULL). */
+DL_API int decode_layer_step_noalloc(const decode_layer_config *cfg, const decode_layer_weights *w,
+                                     const decode_layer_io *io, void *hip_stream);
+DL_API size_t decode_layer_noalloc_max_scratch(void);
+
 #ifdef __cplusplus
 }
 #endif
