@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.decode_layer_trace_points.restype = ctypes.c_int
         L.decode_layer_grid.argtypes = [ctypes.c_void_p]
         L.decode_layer_grid.restype = ctypes.c_int
+        L.decode_layer_set_prefetch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.decode_layer_set_prefetch.restype = ctypes.c_int
         L.decode_layer_set_spin_limit.argtypes = [ctypes.c_void_p, ctypes.c_int]
         L.decode_layer_set_spin_limit.restype = ctypes.c_int
         L.decode_layer_set_step_counter.argtypes = [ctypes.c_void_p, ctypes.c_uint32]
@@ -289,6 +291,13 @@ class DecodeLayer:
         if rc != DL_OK:
             raise DecodeLayerError(rc, last_error(self._h))
         return int(v.value)
+
+    def set_prefetch(self, next_layer: "DecodeLayer | None"):
+        """Prefetch `next_layer`'s dense weights during this layer's steps (None: off)."""
+        rc = lib().decode_layer_set_prefetch(self._h, next_layer._h if next_layer is not None else None)
+        if rc != DL_OK:
+            raise DecodeLayerError(rc, last_error(self._h))
+        self._next = next_layer   # keeps the next handle alive while this one prefetches it
 
     def set_spin_limit(self, rounds: int):
         """Test support: polling rounds before a hand-off wait gives up."""

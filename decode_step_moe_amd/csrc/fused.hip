@@ -197,15 +197,17 @@ __device__ float oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
   const int nch = a.Do >> 3;
   const uint16_t *rows[NR];
   int il[NR];
-  float res[NR], gn[NR];
+  float res[NR];
+  uint16_t gn[NR];
+  // every load unconditional (token and row clamped), so that none of them
+  // is waited for before the weight loads are issued
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     il[r] = wv + kFWaves * r;
     const int i = i0 + min(il[r], ni - 1);
     rows[r] = a.w_o + (size_t)i * a.Do;
-    const bool mine = lane < B && il[r] < ni;
-    res[r] = mine ? a.resid_in[(size_t)lane * a.H + i] : 0.f;
-    gn[r] = mine ? bf16_lo(a.gain[i]) : 0.f;
+    res[r] = a.resid_in[(size_t)min(lane, B - 1) * a.H + i];
+    gn[r] = a.gain[i];
   }
   float o[NR][NT];
   wave_rows_dot<NR, NT, (NT >= 8 ? 1 : 2)>(rows, 0, nch, act, o);
@@ -221,7 +223,7 @@ __device__ float oproj_rows(const FusedArgs &a, Lds &L, int i0, int ni) {
       const size_t ix = (size_t)lane * a.H + i;
       const float r1 = res[r] + mine;
       a.resid_out[ix] = r1;
-      const float hgv = gn[r] * r1;
+      const float hgv = bf16_lo(gn[r]) * r1;
       __hip_atomic_store(a.hg + ix, hgv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       L.hg[lane][il[r]] = hgv;
       sq += r1 * r1;
@@ -526,6 +528,54 @@ __device__ __forceinline__ void by_lpg(int F, Fn fn) {
 
 }  // namespace
 
+// ---- cross-layer prefetch ------------------------------------------------------
+// The dense weights that workgroup w of the next layer reads in its phases A-C
+// (the out-projection and shared down-projection rows of its slice, its unit
+// rows - router row or shared-expert row pair - and its input-projection
+// rows) are touched once per 64-byte sector by the stream threads, so that
+// they sit in this XCD's L2 (workgroup w of the next launch runs on the same
+// XCD) and in the memory-side cache when that layer starts.  The values are
+// folded into a word that is written only under a condition that never holds,
+// which keeps the loads without using them.
+// Threads [t0, kFT) touch the 64-byte sectors of [base, base + nbytes).
+__device__ __forceinline__ unsigned touch_range(const void *base, unsigned nbytes, int t0) {
+  const int tt = (int)threadIdx.x - t0, nt = kFT - t0;
+  const char *p = reinterpret_cast<const char *>(base);
+  const unsigned ns = (nbytes + 63u) >> 6;  // 64-byte sectors
+  unsigned acc = 0;
+  for (unsigned s0 = 0; s0 < ns; s0 += 4u * nt) {
+    unsigned v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned sct = min(s0 + tt + (unsigned)nt * j, ns - 1u);
+      v[j] = *reinterpret_cast<const unsigned *>(p + 64u * sct);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc ^= v[j];
+  }
+  return acc;
+}
+
+// The next layer's rows that its workgroup w reads before its first hand-off:
+// the out-projection rows of the slice and the two unit rows (router row, or
+// shared-expert row pair).  Touched by threads [t0, kFT).
+__device__ __forceinline__ unsigned prefetch_next(const FusedArgs &a, int w, int G, int i0, int ni, int t0) {
+  const int E = a.E, H = a.H;
+  const int fs_b = max(0, min(a.Fs, 2 * G - E));
+  unsigned acc = 0;
+  if (ni > 0) acc ^= touch_range(a.pf_w_o + (size_t)i0 * a.Do, (unsigned)ni * a.Do * 2u, t0);
+  for (int q = 0; q < 2; ++q) {
+    const int u = w + G * q;
+    if (u < E) {
+      acc ^= touch_range(a.pf_w_router + (size_t)u * H, (unsigned)H * 4u, t0);
+    } else if (u < E + fs_b) {
+      acc ^= touch_range(a.pf_s1 + (size_t)(u - E) * H, (unsigned)H * 2u, t0);
+      acc ^= touch_range(a.pf_s3 + (size_t)(u - E) * H, (unsigned)H * 2u, t0);
+    }
+  }
+  return acc;
+}
+
 // ---- phase C, stream waves: the attention input projection ------------------
 // It depends on nothing else in the step, so it fills the logits hand-off:
 // this workgroup's rows are j = w + G q (q < kFusedQkvRows), taken two at a
@@ -560,7 +610,9 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   // this step's tag: the last step's tag + 1, skipping 0 (the tag of a slot
   // never written); the step with the last tag clears every hand-off slot at
   // its end, so after the wrap no slot holds a tag of the new round
-  const unsigned epoch = *a.epoch;
+  // (a vector load: it completes under the first weight loads instead of
+  // holding the start-of-kernel barrier for a memory round trip)
+  const unsigned epoch = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const unsigned tag = epoch == 0xffffffffu ? 1u : epoch + 1u;
   const float kNaN = __builtin_nanf("");
   if (tid == 0) {
@@ -780,6 +832,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   stamp(a, 5);
 
   // ================= phase C =================
+  unsigned pf_acc = 0;
   if (ctl) gather_tagged(a.logit, L.u.logits, tid, kCtl, B * E, tag, a.spin_limit, &L.bad);
   else by_tokens(B, [&](auto nt) { qkv_rows<decltype(nt)::value>(a, L, w, G); });
   __syncthreads();
@@ -790,6 +843,9 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     if (j < a.Dq)
       a.qkv[(size_t)t * a.Dq + j] = ((L.qkvp[0][r][t] + L.qkvp[1][r][t]) + L.qkvp[2][r][t]) + L.qkvp[3][r][t];
   }
+  // The waves the top-k leaves idle (waves B..7) touch the next layer's
+  // first rows meanwhile: no wave polls during the top-k, so HBM is idle.
+  if (a.pf_w_o && B < kFWaves && wv >= B) pf_acc = prefetch_next(a, w, G, i0, ni, B * kWave);
   // top-k per token, one wave per token: lane l holds experts l, l+64, ...
   for (int t = wv; t < B; t += kFWaves) {
     int my_idx;
@@ -1082,6 +1138,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       __hip_atomic_store(a.tag_base + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   stamp(a, 3);
+  if (pf_acc == 0x9e3779b9u && a.B < 0) a.status[0] = pf_acc;  // never true: keeps the prefetch loads
   if (tid == 0) {
     if (L.bad) atomicOr(a.status, 1u);
     if (w == 0) *a.epoch = tag;   // every workgroup has read this step's epoch (all pss seen)

@@ -64,6 +64,10 @@ struct FusedArgs {
   float eps;
   int spin_limit;
   uint64_t *trace;    // optional [G][kTracePoints] wall-clock stamps (nullptr: off)
+  // cross-layer prefetch: the dense weights of the next layer (same shapes);
+  // pf_w_o == nullptr: off
+  const uint16_t *pf_w_o, *pf_w_qkv, *pf_s1, *pf_s3, *pf_s2;
+  const float *pf_w_router;
 };
 constexpr int kTracePoints = 16;
 

@@ -162,6 +162,8 @@ struct decode_layer {
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   void *trace = nullptr;   // caller's device buffer for the phase trace
+  bool has_next = false;   // cross-layer prefetch of next_w
+  decode_layer_weights next_w{};
   bool profiling = false;
   bool profiled_step = false;
   hipEvent_t ev_prof[DECODE_LAYER_N_LAUNCHES][2] = {};
@@ -335,6 +337,14 @@ int enqueue_step(const StepCtx &x, const decode_layer_io *io, hipStream_t st) {
     fa.eps = c.rms_eps;
     fa.spin_limit = x.spin_limit;
     fa.trace = (uint64_t *)x.trace;
+    if (x.prefetch) {
+      fa.pf_w_o = (const uint16_t *)x.prefetch->w_o;
+      fa.pf_w_qkv = (const uint16_t *)x.prefetch->w_qkv;
+      fa.pf_s1 = (const uint16_t *)x.prefetch->s1;
+      fa.pf_s3 = (const uint16_t *)x.prefetch->s3;
+      fa.pf_s2 = (const uint16_t *)x.prefetch->s2;
+      fa.pf_w_router = x.prefetch->w_router;
+    }
     ProfScope p5{h, 5, st};
     HIP_TRY(h, p5.begin());
     HIP_TRY(h, launch_fused(fa, x.single->grid, st));
@@ -620,7 +630,7 @@ int decode_layer_step(decode_layer *h, const decode_layer_io *io, void *hip_stre
   if (io->batch == 0) return DL_OK;
   HIP_TRY(h, hipSetDevice(h->device));
   const StepCtx x{&h->cfg, &h->w, &h->s, &h->single, h->gu_grid, h->side, h->ev_fork, h->ev_join,
-                  h->spin_limit, h->trace, h};
+                  h->spin_limit, h->trace, h->has_next ? &h->next_w : nullptr, h};
   return enqueue_step(x, io, (hipStream_t)hip_stream);
 }
 
@@ -651,6 +661,19 @@ int decode_layer_set_step_counter(decode_layer *h, uint32_t last_tag) {
   HIP_TRY(h, hipSetDevice(h->device));
   HIP_TRY(h, hipDeviceSynchronize());
   HIP_TRY(h, hipMemcpy(h->s.epoch, &last_tag, sizeof last_tag, hipMemcpyHostToDevice));
+  return DL_OK;
+}
+
+int decode_layer_set_prefetch(decode_layer *h, const decode_layer *next) {
+  if (!h) return fail(nullptr, DL_ERR_INVALID_ARG, "handle is NULL");
+  if (!next) {
+    h->has_next = false;
+    return DL_OK;
+  }
+  if (next->device != h->device || std::memcmp(&next->cfg, &h->cfg, sizeof h->cfg) != 0)
+    return fail(h, DL_ERR_INVALID_ARG, "the next layer's handle must have the same configuration and device");
+  h->next_w = next->w;
+  h->has_next = true;
   return DL_OK;
 }
 

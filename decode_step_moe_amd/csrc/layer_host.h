@@ -88,6 +88,7 @@ struct StepCtx {
   hipEvent_t ev_fork, ev_join;
   int spin_limit;
   void *trace;
+  const decode_layer_weights *prefetch;  // next layer's weights to prefetch (nullptr: none)
   decode_layer *h;             // error text and profiling (nullptr: thread-local error, no profiling)
 };
 

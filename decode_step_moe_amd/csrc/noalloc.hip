@@ -127,7 +127,7 @@ int decode_layer_step_noalloc(const decode_layer_config *cfg, const decode_layer
   }
   const Scratch S = bind_scratch(base, L);
   const StepCtx x{cfg, w, &S, &sp, 2 * std::max(1, d->n_cu), nullptr, nullptr, nullptr,
-                  kDefaultSpinLimit, nullptr, nullptr};
+                  kDefaultSpinLimit, nullptr, nullptr, nullptr};
   return enqueue_step(x, io, st);
 }
 

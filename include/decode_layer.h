@@ -279,6 +279,23 @@ DL_API int decode_layer_set_step_counter(decode_layer *h, uint32_t last_tag);
 DL_API int decode_layer_set_profiling(decode_layer *h, int enable);
 DL_API int decode_layer_kernel_times(decode_layer *h, float *ms, int capacity);
 
+/* Cross-layer weight prefetch.  In a decode step the layers of the model run
+ * one after another; while one layer's single-launch step waits for its
+ * router logits (a hand-off that leaves HBM mostly idle), the weights of the
+ * next layer are already known.  After this call every single-launch step of
+ * `h` also reads, once per 64-byte sector, the dense weights that the
+ * workgroups of `next` read first in their own step (out-projection, router
+ * and shared-expert rows, attention input projection, shared down-projection
+ * rows), so that `next` finds them in this device's caches (the XCD's L2 and
+ * the memory-side Infinity Cache).  The results are unchanged; only where
+ * the next layer's reads are served from changes.  This is the single-GPU
+ * form of the pages' weight prefetch during communication (wireai.ir "vLLM's
+ * speed jump on NVIDIA Blackwell servers; record 842 tokens/s for Kimi K3",
+ * "Four key changes behind the jump", bullet 4).  `next` must have the same
+ * configuration and device (DL_ERR_INVALID_ARG otherwise) and must stay alive
+ * while `h` steps; NULL turns the prefetch off.  Host-only. */
+DL_API int decode_layer_set_prefetch(decode_layer *h, const decode_layer *next);
+
 /* Phase trace of the single-launch kernel, for measurement.  With a non-NULL
  * device buffer of decode_layer_grid(h) * decode_layer_trace_points() uint64
  * values (caller-owned, 16-byte aligned), every later single-launch step has
