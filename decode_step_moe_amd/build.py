@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdecode_layer.so")
-SOURCES = ["proj.hip", "router.hip", "experts.hip", "fused.hip", "batched.hip", "layer.hip", "noalloc.hip"]
+SOURCES = ["proj.hip", "router.hip", "experts.hip", "fused.hip", "batched.hip", "layer.hip", "noalloc.hip", "attn.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -46,14 +46,21 @@ def _codes(g, shape):
 
 
 def draw(R: int, T: int, Hq: int, Hkv: int, C: int, min_past: int, max_past: int, seed: int = 0,
-         D: int = 128) -> AttnStep:
+         D: int = 128, past=None) -> AttnStep:
+    """`past` (length R) replaces the drawn past lengths when given."""
     if max_past + T > C:
         raise ValueError("the cache cannot hold the step's tokens")
     ga, gc, gl = rng(seed, 10, 0), rng(seed, 10, 1), rng(seed, 10, 2)
     q = f32_to_bf16_bits(ga.normal(0, 1, size=(R, T, Hq, D)).astype(np.float32))
     k_new = f32_to_bf16_bits(ga.normal(0, 1, size=(R, T, Hkv, D)).astype(np.float32))
     v_new = f32_to_bf16_bits(ga.normal(0, 1, size=(R, T, Hkv, D)).astype(np.float32))
-    past = gl.integers(min_past, max_past + 1, size=R).astype(np.int32)
+    drawn = gl.integers(min_past, max_past + 1, size=R).astype(np.int32)
+    if past is None:
+        past = drawn
+    else:
+        past = np.asarray(past, dtype=np.int32).reshape(R)
+        if past.min(initial=0) < 0 or past.max(initial=0) + T > C:
+            raise ValueError("past lengths outside the cache")
     k_cache = gc.integers(0, 256, size=(R, Hkv, C, D), dtype=np.int64).astype(np.uint8)
     v_cache = gc.integers(0, 256, size=(R, Hkv, C, D), dtype=np.int64).astype(np.uint8)
     for r in range(R):
@@ -63,3 +70,20 @@ def draw(R: int, T: int, Hq: int, Hkv: int, C: int, min_past: int, max_past: int
     k_scale = (gl.uniform(0.75, 1.25, size=Hkv) / 64.0).astype(np.float32)
     v_scale = (gl.uniform(0.75, 1.25, size=Hkv) / 64.0).astype(np.float32)
     return AttnStep(q, k_new, v_new, k_cache, v_cache, past, k_scale, v_scale, float(np.float32(D ** -0.5)))
+
+
+# Named attention workloads on one TP16 shard (4 query heads sharing 1 KV head
+# of 128): (R requests, T tokens each, Hq, Hkv, cache_len C, min_past, max_past).
+WORKLOADS = {
+    # small: several chunks and a ragged tail, the oracle finishes in seconds
+    "attn_small": (4, 8, 4, 1, 1024, 200, 1000),
+    # speculative verify: 1 request, 1 verified token + 7 drafts, long context
+    "attn_verify_ctx8k": (1, 8, 4, 1, 8192, 8184, 8184),
+    # batch-64 decode: one token per request, contexts mixed over 1k .. 4k
+    "attn_b64_ctx4k": (64, 1, 4, 1, 4096, 1024, 4095),
+}
+
+
+def draw_workload(name: str, seed: int = 0) -> AttnStep:
+    R, T, Hq, Hkv, C, lo, hi = WORKLOADS[name]
+    return draw(R, T, Hq, Hkv, C, lo, hi, seed=seed)

@@ -17,14 +17,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "decode_layer.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(decode_layer_\w+)\s*\(", text)))
+    """Every function the headers under include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(decode_(?:layer|attention)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert "decode_layer_init" in names and "decode_layer_step" in names
+    assert "decode_layer_init" in names and "decode_layer_step" in names and "decode_attention_step" in names
     lib = ctypes.CDLL(dl.binding.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -204,3 +209,45 @@ def test_init_without_gpu_fails_cleanly():
     rc = lib.decode_layer_init(ctypes.byref(good()), ctypes.byref(w), 0, ctypes.byref(out))
     assert rc == dl.DL_ERR_HIP and not out.value
     assert len(dl.last_error()) > 0
+
+
+# ---------------------------------------------------------------- attention core
+def _attn_cfg(**kw):
+    from decode_step_moe_amd import attention as at
+    c = dict(n_q_heads=4, n_kv_heads=1, max_tokens=8, max_requests=64, cache_len=4096, softmax_scale=128 ** -0.5)
+    c.update(kw)
+    return at.make_attn_config(**c)
+
+
+def test_attention_workspace_and_validation():
+    from decode_step_moe_amd import attention as at
+    c = _attn_cfg()
+    chunks = -(-4096 // 256)
+    slots = 64 * 1 * chunks * (32 * 128 + 64) * 4
+    assert at.workspace_bytes(c) == _a256(slots) + _a256(64 * 4)
+    for field, value in (("head_dim", 64), ("max_tokens", 9), ("max_tokens", 0), ("n_kv_heads", 3),
+                         ("n_q_heads", 40), ("cache_len", 0), ("softmax_scale", 0.0), ("max_requests", 2000)):
+        bad = _attn_cfg(**{field: value}) if field != "head_dim" else at.make_attn_config(4, 1, 8, 64, 4096, 0.1, 64)
+        assert at.workspace_bytes(bad) == 0, field
+    # (Hq / Hkv) * T must fit 32 query rows per KV head
+    assert at.workspace_bytes(_attn_cfg(n_q_heads=8, max_tokens=8)) == 0
+    assert at.workspace_bytes(_attn_cfg(n_q_heads=8, n_kv_heads=2, max_tokens=8)) > 0
+
+    def io(**kw):
+        p = dict(past_len=0x1000, q=0x2000, k_new=0x3000, v_new=0x4000, k_cache=0x5000, v_cache=0x6000,
+                 k_scale=0x7000, v_scale=0x8000, out=0x9000, workspace=0x10000)
+        n = dict(n_requests=2, n_tokens=8, max_past=100)
+        p.update({k: v for k, v in kw.items() if k in p})
+        n.update({k: v for k, v in kw.items() if k in n})
+        return at.AttnIO(n["n_requests"], n["n_tokens"], n["max_past"],
+                         *[p[k] for k in ("past_len", "q", "k_new", "v_new", "k_cache", "v_cache", "k_scale",
+                                          "v_scale", "out", "workspace")])
+    assert at.check(c, io()) == dl.DL_OK
+    assert at.check(c, io(n_requests=0, q=None)) == dl.DL_OK
+    assert at.check(c, io(n_requests=65)) == dl.DL_ERR_UNSUPPORTED
+    assert at.check(c, io(n_tokens=9)) == dl.DL_ERR_UNSUPPORTED
+    assert at.check(c, io(max_past=4089)) == dl.DL_ERR_UNSUPPORTED      # max_past + T > cache_len
+    assert at.check(c, io(q=None)) == dl.DL_ERR_INVALID_ARG
+    assert at.check(c, io(out=0x9004)) == dl.DL_ERR_INVALID_ARG
+    assert at.check(c, io(workspace=0x10010)) == dl.DL_ERR_INVALID_ARG  # 256-byte alignment
+    assert "workspace" in dl.last_error()
