@@ -39,6 +39,7 @@ METRIC = "µs per decode layer-step & achieved HBM GB/s (% of peak), batch 1/8/6
 HBM_PEAK_GBPS = 8000.0
 HEADLINE_CFG = 1
 BATCH_CFGS = (2, 4, 3)
+ATTN_WORKLOADS = ("attn_verify_ctx8k", "attn_b64_ctx4k")
 
 
 def log(*a):
@@ -272,6 +273,100 @@ def time_config(cfg_id, steps, warmup, n_copies, want_kernels=True, path=0, chai
     return res, layer
 
 
+def attn_bytes(st) -> dict:
+    """Algorithmic HBM bytes of one attention step: every cached key and value
+    the step's queries can see read once (one byte each, the step's own
+    tokens included), the appended codes written, the new keys and values,
+    the queries and the outputs moved once."""
+    R, T, Hq, Hkv, D, C = st.shape
+    kv = int(sum(int(L) + T for L in st.past_len)) * Hkv * D * 2
+    append = R * T * Hkv * D * (2 * 2 + 2)      # bf16 k, v in; E4M3 k, v out
+    qo = R * T * Hq * D * (2 + 4)               # bf16 queries in, fp32 outputs out
+    return {"kv_read": kv, "append": append, "q_out": qo, "step": kv + append + qo}
+
+
+def time_attention(name, steps, warmup):
+    """One attention step (one launch: the step's keys and values appended, then
+    attention over the cache in tiles of 256 positions) of a named
+    workload, rotated over device-side copies of its KV cache (>= 1 GB in
+    total, so no step finds its cache in the Infinity Cache), timed by
+    replaying one HIP graph holding one step of every copy."""
+    import torch
+    from decode_step_moe_amd import attention as at
+    from synth import attn_gen
+    from synth.device import bf16_tensor, f32_tensor
+
+    st = attn_gen.draw_workload(name, seed=3)
+    R, T, Hq, Hkv, D, C = st.shape
+    nb = attn_bytes(st)
+    per_copy = 2 * R * Hkv * C * D
+    n = max(4, int(np.ceil(1.0e9 / per_copy)))
+    log(f"[bench] attention {name}: {nb['step'] / 1e6:.2f} MB/step, {n} cache copies")
+    cfg = at.make_attn_config(Hq, Hkv, T, R, C, st.softmax_scale)
+    d = "cuda"
+    q, kn, vn = (bf16_tensor(a, d) for a in (st.q, st.k_new, st.v_new))
+    kc0 = torch.from_numpy(np.ascontiguousarray(st.k_cache)).to(d)
+    vc0 = torch.from_numpy(np.ascontiguousarray(st.v_cache)).to(d)
+    kc = kc0.repeat(n, 1, 1, 1)
+    vc = vc0.repeat(n, 1, 1, 1)
+    ks, vs = f32_tensor(st.k_scale, d), f32_tensor(st.v_scale, d)
+    past = torch.from_numpy(np.ascontiguousarray(st.past_len)).to(d)
+    outs = [torch.empty((R, T, Hq, D), device=d) for _ in range(n)]
+    ws = torch.zeros(at.workspace_bytes(cfg), dtype=torch.uint8, device=d)
+    mp = int(st.past_len.max())
+    ios = [at.make_io(cfg, past, mp, q, kn, vn, kc[i * R:(i + 1) * R], vc[i * R:(i + 1) * R], ks, vs, outs[i], ws)
+           for i in range(n)]
+    stream = torch.cuda.current_stream()
+    for i in range(n):
+        at.step_io(cfg, ios[i], stream)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    assert bool(torch.isfinite(outs[0]).all())
+
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(warmup):
+        at.step_io(cfg, ios[i % n], stream)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        at.step_io(cfg, ios[i % n], stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = t0.elapsed_time(t1) / steps * 1e3
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(n):
+            at.step_io(cfg, ios[i], side)
+    torch.cuda.synchronize()
+    reps = max(2, -(-steps // n))
+    g.replay()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = t0.elapsed_time(t1) / (reps * n) * 1e3
+    ref = outs[0].clone()
+    assert torch.equal(outs[0], ref)
+    del g
+    gbps = nb["step"] / (graph_us * 1e-6) / 1e9
+    res = {"workload": name, "requests": R, "tokens": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+           "cache_len": C, "mean_context": round(float(np.mean(st.past_len)) + T, 1), "copies": n,
+           "graph_us": round(graph_us, 3), "eager_us": round(eager_us, 3), "launches_per_step": 1,
+           "bytes": nb,
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "timing": "graph-replayed steps (one launch each), HIP events on the launching stream"}}
+    del kc, vc, outs, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def _launch_probe(h, layer):
     """Names of the launches one step of this batch makes on handle `h`."""
     import torch
@@ -351,6 +446,9 @@ def main():
                     help="skip the rotation with cross-layer prefetch (so that a kernel trace holds "
                          "only standalone steps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-attention", action="store_true", help="skip the attention-core workloads")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="measure only the attention-core workloads and print their results")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a few eager headline steps and a 1 GiB negate of known size "
                          "(for hardware-counter runs under rocprofv3 --pmc), then exit")
@@ -367,6 +465,10 @@ def main():
 
     if args.counter_pass:
         counter_pass(args.steps)
+        return
+    if args.attention_only:
+        print(json.dumps({"attention": {n: time_attention(n, args.steps, args.warmup) for n in ATTN_WORKLOADS}}),
+              flush=True)
         return
     head, layer = time_config(HEADLINE_CFG, args.steps, args.warmup, args.copies, chain=not args.no_chain)
     multi, _ = time_config(HEADLINE_CFG, args.steps, args.warmup, args.copies, want_kernels=False,
@@ -424,6 +526,8 @@ def main():
         "kernels_us": {k_: round(v, 3) for k_, v in kern.items()},
         "batches": batches,
     }
+    if not args.no_attention:
+        line["attention"] = {n: time_attention(n, args.steps, args.warmup) for n in ATTN_WORKLOADS}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
     print(json.dumps(line), flush=True)

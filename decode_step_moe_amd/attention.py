@@ -15,7 +15,7 @@ from .binding import DL_OK, DecodeLayerError, _ptr, last_error, lib
 class AttnConfig(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("max_requests", ctypes.c_int32), ("cache_len", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("max_splits", ctypes.c_int32)]
 
 
 class AttnIO(ctypes.Structure):
@@ -42,8 +42,9 @@ def _lib():
 
 
 def make_attn_config(n_q_heads, n_kv_heads, max_tokens, max_requests, cache_len, softmax_scale,
-                     head_dim=128) -> AttnConfig:
-    return AttnConfig(n_q_heads, n_kv_heads, head_dim, max_tokens, max_requests, cache_len, softmax_scale)
+                     head_dim=128, max_splits=0) -> AttnConfig:
+    return AttnConfig(n_q_heads, n_kv_heads, head_dim, max_tokens, max_requests, cache_len, softmax_scale,
+                      max_splits)
 
 
 def workspace_bytes(cfg: AttnConfig) -> int:

@@ -9,23 +9,28 @@
 // contexts and by latency at short ones; the cache is read one byte per value
 // and decoded on the fly.
 //
-// Two launches on the caller's stream:
-//  1 attn_append  quantises the step's keys and values (x / scale in fp32,
-//                 nearest E4M3 code, ties to even, clamped to +-448) into
-//                 positions past_len .. past_len + T - 1 of each request.
-//  2 attn_chunk   one workgroup per (chunk of 256 positions, request, KV
-//                 head): S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_bf16;
-//                 queries are bf16 already and every E4M3 value is exact in
-//                 bf16), the causal mask (query token j sees positions up to
-//                 past_len + j), the chunk's row maxima and sums, then
-//                 P V on the matrix cores with P as bf16 hi + lo and V from LDS.
-//                 The chunk's (max, sum, P V) go to its slot; the last
-//                 workgroup of the (request, KV head) to arrive combines the
-//                 slots in chunk order and writes the outputs.
-// Rows: the T tokens x Hq/Hkv heads of one KV head (at most 32), in 16-row
-// matrix-core tiles.
+// One launch on the caller's stream, one workgroup of 4 waves per (split,
+// request, KV head); a split takes tps consecutive tiles of 256 positions,
+// 64 per wave.  Rows are the T tokens x Hq/Hkv query heads of the KV head
+// (at most 32, in 16-row matrix-core tiles).  Per tile, each wave on its own:
+//  - loads its 64 keys' K and V codes (the step's own positions are
+//    quantised from k_new / v_new instead, x / scale in fp32 to the nearest
+//    E4M3 code, and written to the cache by the lane holding them);
+//  - S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16; the codes
+//    are decoded to bf16 by the hardware conversion, exactly, and queries
+//    are bf16 already), the causal mask (token j sees positions up to
+//    past_len + j), an online softmax of its own;
+//  - O^T += V^T P^T on the matrix cores, P as bf16 hi + lo straight from the
+//    S^T registers, V^T from the wave's own LDS slice (byte-transposed in
+//    registers on the way in), so no barrier is needed inside the tile loop.
+// The waves merge through LDS; a request's single workgroup writes its
+// outputs, otherwise each workgroup's partial (max, sum, O) goes to its slot
+// and the last workgroup of the (request, KV head) to arrive combines the
+// slots in slot order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -36,15 +41,20 @@
 namespace dl {
 namespace {
 
-constexpr int kAD = 128;                               // head size
-constexpr int kAChunk = 256;                           // cache positions per workgroup
-constexpr int kAMaxRows = 32;                          // query rows per KV head
-constexpr int kASlot = kAMaxRows * kAD + 2 * kAMaxRows; // floats per chunk slot: P V, max, sum
+constexpr int kAD = 128;                 // head size
+constexpr int kATile = 256;              // cache positions per workgroup tile (64 per wave)
+constexpr int kAMaxRows = 32;            // query rows per KV head
+constexpr int kAMaxSplit = 64;           // workgroups per (request, KV head)
+constexpr int kASlot = kAMaxRows * kAD + 2 * kAMaxRows;  // floats per partial: O [row][d], max, sum
+constexpr int kAVRow = 72;               // LDS bytes per head-dim row of a wave's V^T slice (64 keys + pad)
+constexpr int kAVWave = kAD * kAVRow;    // LDS bytes of one wave's V^T slice
+constexpr unsigned kCoherent = 16;       // buffer cache policy: coherent at agent scope
 
 typedef __bf16 bf16x8a __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2a __attribute__((ext_vector_type(2)));
 typedef float f32x4a __attribute__((ext_vector_type(4)));
 typedef float f32x2a __attribute__((ext_vector_type(2)));
+typedef unsigned v4ua __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   const int32_t *past_len;
@@ -52,52 +62,67 @@ struct AttnArgs {
   uint8_t *k_cache, *v_cache;
   const float *k_scale, *v_scale;
   float *out;
-  float *slots;        // [max_requests * Hkv][n_chunk_max][kASlot]
+  float *slots;        // [max_requests * Hkv][n_split][kASlot]
   unsigned *counters;  // [max_requests * Hkv]
-  int R, T, Hq, Hkv, C, max_past, grp, M, n_chunk_max;
+  int R, T, Hq, Hkv, C, max_past, grp, M, tps, n_split;
   float softmax_scale;
 };
 
 __device__ __forceinline__ f32x4a mfma16(const uint4 &a, const uint4 &b, f32x4a c) {
-  v4u ua = {a.x, a.y, a.z, a.w}, ub = {b.x, b.y, b.z, b.w};
+  v4ua ua = {a.x, a.y, a.z, a.w}, ub = {b.x, b.y, b.z, b.w};
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8a, ua), __builtin_bit_cast(bf16x8a, ub),
                                                  c, 0, 0, 0);
 }
 
 // x (fp32) -> E4M3 code: nearest value, ties to the even code, magnitudes of
-// 448 and above clamped to 448, the sign kept, NaN -> 0x7F.
+// 448 and above clamped to 448, the sign kept, NaN -> 0x7F.  Branch-free: at
+// and above 2^-6 the fp32 pattern is rounded to 3 mantissa bits (to nearest,
+// ties to even, a carry moving into the exponent) and the exponent rebiased
+// from 127 to 7; below 2^-6 the codes are the multiples of 2^-9, a * 512
+// rounded to the nearest integer, ties to even (exact scaling).
 __device__ __forceinline__ unsigned e4m3_encode(float x) {
-  const unsigned u = __float_as_uint(x);
-  const unsigned sign = (u >> 24) & 0x80u;
+  const unsigned u = __float_as_uint(x), ua = u & 0x7FFFFFFFu;
   const float a = fabsf(x);
-  if (a != a) return 0x7Fu;
-  if (a >= 448.f) return sign | 0x7Eu;
-  if (a < 0.015625f) {                            // below the smallest normal 2^-6: steps of 2^-9
-    return sign | (unsigned)rintf(a * 512.f);     // exact scaling, round half to even; 8 is 2^-6
-  }
-  int e = (int)((u >> 23) & 0xFFu) - 127;         // -6 .. 8
-  const unsigned mant = u & 0x7FFFFFu;
-  unsigned m3 = mant >> 20;
-  const unsigned rem = mant & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
-  if (m3 == 8u) {
-    m3 = 0u;
-    ++e;
-  }
-  return sign | ((unsigned)(e + 7) << 3) | m3;
+  const unsigned rn = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
+  const unsigned rs = (unsigned)rintf(a * 512.f);
+  unsigned c = a < 0.015625f ? rs : rn;
+  c = a >= 448.f ? 0x7Eu : c;
+  c |= (u >> 24) & 0x80u;
+  return a != a ? 0x7Fu : c;
 }
 
-// E4M3 code -> bf16 bits of the same value (exact), NaN codes -> a bf16 NaN.
-__device__ __forceinline__ uint16_t e4m3_to_bf16(unsigned c) {
-  const unsigned s = (c & 0x80u) << 8, e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 15u && m == 7u) return (uint16_t)(s | 0x7FC0u);
-  if (e != 0u) return (uint16_t)(s | ((e + 120u) << 7) | (m << 4));
-  if (m == 0u) return (uint16_t)s;
-  // subnormal m * 2^-9: shift the leading bit of m into the implicit one
-  const unsigned lz = m >= 4u ? 0u : m >= 2u ? 1u : 2u;  // leading zeros of m in 3 bits
-  const unsigned ex = 120u - lz;                        // 2^-7 for m >= 4
-  const unsigned mm = ((m << (lz + 1u)) & 7u) << 4;
-  return (uint16_t)(s | (ex << 7) | mm);
+// 8 bf16 values / scale (fp32 division) -> 8 E4M3 codes
+__device__ __forceinline__ uint2 quant8(const uint16_t *src, float scale) {
+  float f[8];
+  unpack8(ld16(src), f);
+  unsigned w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_encode(f[i] / scale) << (8 * (i & 3));
+  return make_uint2(w[0], w[1]);
+}
+
+__device__ __forceinline__ unsigned word(const uint4 &v, int c) {   // c: a compile-time constant after unrolling
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
+// 4 x 4 byte transpose: byte k of o[j] = byte j of a_k
+__device__ __forceinline__ void transpose4(unsigned a0, unsigned a1, unsigned a2, unsigned a3, unsigned (&o)[4]) {
+  // selector bytes 0..3 pick bytes of the second operand, 4..7 of the first
+  const unsigned t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u), t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+  const unsigned t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u), t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+}
+
+// 8 E4M3 codes -> 8 bf16 (exact: the hardware decodes OCP E4M3, scale 1)
+template <bool HI>
+__device__ __forceinline__ unsigned cvt2(unsigned w) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ uint4 fp8x8_bf16(unsigned a, unsigned b) {
+  return make_uint4(cvt2<false>(a), cvt2<true>(a), cvt2<false>(b), cvt2<true>(b));
 }
 
 __device__ __forceinline__ unsigned pack2_bf16(float a, float b) {  // round to nearest even
@@ -118,257 +143,384 @@ __device__ __forceinline__ void split_hi_lo(const float (&x)[8], uint4 &hi, uint
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_mov<kDppXor1>(v));
-  v = fmaxf(v, dpp_mov<kDppXor2>(v));
-  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_mov<kDppMirror>(v));
-  return v;
+__device__ __forceinline__ float max4g(float v) {  // max over the 4 lanes n, n + 16, n + 32, n + 48
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float sum4g(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
 }
 
 __device__ __forceinline__ bool request_bad(const AttnArgs &a, int L) {
   return L < 0 || L > a.max_past || L + a.T > a.C;
 }
 
-// ---- launch 1 ---------------------------------------------------------------
-// Thread: 8 consecutive elements of one (request, token, KV head) row.
-__global__ void __launch_bounds__(256) attn_append(AttnArgs a) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const int row = t >> 4, part = t & 15;           // row = (r T + j) Hkv + g
-  if (row >= a.R * a.T * a.Hkv) return;
-  const int g = row % a.Hkv, rj = row / a.Hkv, j = rj % a.T, r = rj / a.T;
-  const int L = a.past_len[r];
-  if (request_bad(a, L)) return;
-  const size_t src = (size_t)row * kAD + part * 8;
-  float kf[8], vf[8];
-  unpack8(ld16(a.k_new + src), kf);
-  unpack8(ld16(a.v_new + src), vf);
-  const float ks = a.k_scale[g], vs = a.v_scale[g];
-  unsigned kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+// Key order inside a wave's 64-key slice of a tile.  The P V product takes
+// 32 keys per matrix-core step q; lane group g4 supplies 8 of them, element
+// jj.  With this order the scores a lane holds after S^T = K Q^T (keys
+// 16 kt + 4 g4 + i of its query row) are exactly the P^T operand it supplies.
+__device__ __forceinline__ int slice_key(int q, int g4, int jj) { return 32 * q + 16 * (jj >> 2) + 4 * g4 + (jj & 3); }
+
+// A wave's running state for up to 16 NRT query rows: lane (n, g4) holds row
+// 16 rt + n, its max (same in the 4 lane groups), its partial sum over the
+// lane's own keys, and O^T columns d = 16 dt + 4 g4 + i.
+template <int NRT>
+struct WaveAcc {
+  float m[NRT], l[NRT];
+  f32x4a o[NRT][8];
+};
+
+// Merge partial (mb, lb, Ob) of the same rows into a (softmax rescaling;
+// maxima are in log2 units, scores having been scaled by log2 e).
+template <int NRT>
+__device__ __forceinline__ void merge_rows(WaveAcc<NRT> &a, int rt, float mb, float lb, const float *ob_row,
+                                           int g4) {
+  const float mn = fmaxf(a.m[rt], mb);
+  if (mn == -__builtin_inff()) return;     // neither side has seen a visible key of this row
+  const float fa = __builtin_amdgcn_exp2f(a.m[rt] - mn);   // 0 for a side at -inf
+  const float fb = __builtin_amdgcn_exp2f(mb - mn);
+  a.m[rt] = mn;
+  a.l[rt] = a.l[rt] * fa + lb * fb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    kw[i >> 2] |= e4m3_encode(kf[i] / ks) << (8 * (i & 3));
-    vw[i >> 2] |= e4m3_encode(vf[i] / vs) << (8 * (i & 3));
+  for (int dt = 0; dt < 8; ++dt) {
+    const float4 b = *reinterpret_cast<const float4 *>(ob_row + 16 * dt + 4 * g4);
+    a.o[rt][dt][0] = a.o[rt][dt][0] * fa + b.x * fb;
+    a.o[rt][dt][1] = a.o[rt][dt][1] * fa + b.y * fb;
+    a.o[rt][dt][2] = a.o[rt][dt][2] * fa + b.z * fb;
+    a.o[rt][dt][3] = a.o[rt][dt][3] * fa + b.w * fb;
   }
-  const size_t dst = ((size_t)(r * a.Hkv + g) * a.C + L + j) * kAD + part * 8;
-  *reinterpret_cast<uint2 *>(a.k_cache + dst) = make_uint2(kw[0], kw[1]);
-  *reinterpret_cast<uint2 *>(a.v_cache + dst) = make_uint2(vw[0], vw[1]);
 }
 
-// ---- launch 2 ---------------------------------------------------------------
-__global__ void __launch_bounds__(256, 2) attn_chunk(AttnArgs a) {
-  __shared__ uint16_t lut[256];
-  __shared__ __align__(16) uint8_t vsh[kAChunk * kAD];      // V rows of the chunk (E4M3)
-  __shared__ __align__(16) float psh[kAMaxRows][kAChunk];   // P of the chunk
-  __shared__ float redm[4][kAMaxRows], redl[4][kAMaxRows];
-  __shared__ float rowm[kAMaxRows], rowl[kAMaxRows];
+// A partial into LDS as O [row][d], max [32], sum [32] (sums already over the 4 lane groups).
+template <int NRT>
+__device__ __forceinline__ void put_partial(float *part, const WaveAcc<NRT> &a, int n, int g4) {
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = 16 * rt + n;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4 *>(part + row * kAD + 16 * dt + 4 * g4) =
+          make_float4(a.o[rt][dt][0], a.o[rt][dt][1], a.o[rt][dt][2], a.o[rt][dt][3]);
+    if (g4 == 0) {
+      part[kAMaxRows * kAD + row] = a.m[rt];
+      part[kAMaxRows * kAD + kAMaxRows + row] = a.l[rt];
+    }
+  }
+}
+
+// PF: the next tile's loads are issued during this tile's softmax and P V
+// (used when a workgroup takes more than one tile; the registers they hold
+// leave room for one workgroup per CU at 32 rows).
+// One workgroup: tiles [tb, te) of one (request, KV head), 4 waves each
+// taking 64 keys of every tile with a softmax of their own; the waves merge
+// at the end; the workgroup's partial goes to the output directly when it is
+// the request's only one, else to its slot, and the last workgroup of the
+// (request, KV head) to arrive combines the slots.
+template <int NRT, bool PF>
+__global__ void __launch_bounds__(256, (NRT == 2 && PF) ? 1 : 2) attn_step(AttnArgs a) {
+  __shared__ __align__(16) uint8_t lds[4 * kAVWave];   // V^T slices; later partials and combine weights
+  __shared__ __align__(16) uint8_t newc[2 * 8 * kAD];  // this step's K and V codes [K | V][token][d]
   __shared__ int s_last;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g4 = lane >> 4;
-  const int c = blockIdx.x, rg = blockIdx.y, r = rg / a.Hkv, g = rg % a.Hkv;
+  const int s = blockIdx.x, rg = blockIdx.y, r = rg / a.Hkv, g = rg % a.Hkv;
   const int L = a.past_len[r];
-  const int M = a.M, grp = a.grp;
+  const int M = a.M, grp = a.grp, T = a.T;
+  constexpr float kNegInf = -__builtin_inff();
   if (request_bad(a, L)) {
     // an impossible length: this request's outputs are NaN, nothing else runs
-    if (c == 0)
+    if (s == 0)
       for (int q = tid; q < M * kAD; q += 256) {
         const int row = q / kAD, d = q % kAD, j = row / grp, h = g * grp + row % grp;
-        a.out[((size_t)(r * a.T + j) * a.Hq + h) * kAD + d] = __builtin_nanf("");
+        a.out[((size_t)(r * T + j) * a.Hq + h) * kAD + d] = __builtin_nanf("");
       }
     return;
   }
-  const int len = L + a.T;                              // positions after the append
-  const int nch = (len + kAChunk - 1) / kAChunk;
-  if (c >= nch) return;                                 // past this request's end: not counted
-  const int p0 = c * kAChunk;
+  const int len = L + T;                                 // positions after this step's tokens
+  const int ntile = (len + kATile - 1) / kATile;
+  const int tb = s * a.tps;
+  if (tb >= ntile) return;                               // past this request's end: not counted
+  const int te = min(tb + a.tps, ntile), nact = (ntile + a.tps - 1) / a.tps;
   const size_t cbase = (size_t)rg * a.C * kAD;
-  // every load up front (addresses clamped to the request's last position):
-  // this thread's 8 words of the chunk's V rows, its wave's K fragments, its
-  // query fragments
-  uint4 vst[8];
+  const int lr = max(L - 1, 0);                          // cache reads stay below the step's own positions
+  const float ksc = a.k_scale[g], vsc = a.v_scale[g];
+  const size_t new_row0 = (size_t)r * T * a.Hkv + g;    // row (r, j, g) of k_new / v_new is new_row0 + j Hkv
+
+  // ---- loads of one tile: this wave's 64 V rows (lane m = lane / 8 takes
+  // the 8 keys of P V chunk m, 16 head-dim bytes 16 (lane % 8) ..) and its
+  // K fragments (key 16 kt + n, head-dim bytes 64 h + 16 g4 ..).  Reads stay
+  // below the step's own positions (their codes come from LDS, see below).
+  const int vm = lane >> 3, vdg = lane & 7;
+  // plain locals: a lambda must not take the address of the kernel arguments
+  const uint8_t *const kcache = a.k_cache, *const vcache = a.v_cache;
+  uint4 vst[8], kr[4][2];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const int p0 = t * kATile + 64 * wv;
+    if (p0 >= len) return;                               // the wave's keys all lie past the end
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int w = tid + 256 * k, p = min(p0 + (w >> 3), len - 1);
-    vst[k] = ld16(a.v_cache + cbase + (size_t)p * kAD + 16 * (w & 7));
-  }
-  uint2 kr[4][4];  // [key tile][K step]: key p0 + 64 wv + 16 kt + n, elements 32 s + 8 g4 ..
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int p = min(p0 + 64 * wv + 16 * kt + n, len - 1);
-    const uint8_t *kp = a.k_cache + cbase + (size_t)p * kAD + 8 * g4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kr[kt][s] = *reinterpret_cast<const uint2 *>(kp + 32 * s);
-  }
-  uint4 qa[2][4];  // [row tile][K step]: row rt 16 + n
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = min(rt * 16 + n, M - 1), j = row / grp, h = g * grp + row % grp;
-    const uint16_t *qp = a.q + ((size_t)(r * a.T + j) * a.Hq + h) * kAD + 8 * g4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qa[rt][s] = ld16(qp + 32 * s);
-  }
-  lut[tid] = e4m3_to_bf16((unsigned)tid);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int w = tid + 256 * k;
-    reinterpret_cast<uint4 *>(vsh)[w] = p0 + (w >> 3) < len ? vst[k] : make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-  const int nrt = (M + 15) >> 4;
-  // ---- S = Q K^T for this wave's 64 positions
-  f32x4a acc[2][4];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) acc[rt][kt] = f32x4a{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint2 b = kr[kt][s];
-      const uint4 kb = make_uint4(lut[b.x & 255u] | ((unsigned)lut[(b.x >> 8) & 255u] << 16),
-                                  lut[(b.x >> 16) & 255u] | ((unsigned)lut[b.x >> 24] << 16),
-                                  lut[b.y & 255u] | ((unsigned)lut[(b.y >> 8) & 255u] << 16),
-                                  lut[(b.y >> 16) & 255u] | ((unsigned)lut[b.y >> 24] << 16));
-      acc[0][kt] = mfma16(qa[0][s], kb, acc[0][kt]);
-      if (nrt > 1) acc[1][kt] = mfma16(qa[1][s], kb, acc[1][kt]);
+    for (int k = 0; k < 8; ++k) {
+      const int p = min(p0 + slice_key(vm >> 2, vm & 3, k), lr);
+      vst[k] = ld16(vcache + cbase + (size_t)p * kAD + 16 * vdg);
     }
-  // ---- scale, mask, the chunk's row maxima
-  const float sc = a.softmax_scale * a.k_scale[g];
-  const float kNegInf = -__builtin_inff();
-  float mx[2][4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint8_t *kp = kcache + cbase + (size_t)min(p0 + 16 * kt + n, lr) * kAD + 16 * g4;
+      kr[kt][0] = ld16(kp);
+      kr[kt][1] = ld16(kp + 64);
+    }
+  };
+  if (PF) load_tile(tb);
+  // query fragments: row 16 rt + n, head-dim elements in the K fragments' order
+  uint4 qa[NRT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rt * 16 + 4 * g4 + i, lim = L + row / grp;  // last visible position
-      float m = kNegInf;
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = min(16 * rt + n, M - 1), j = row / grp, h = g * grp + row % grp;
+    const uint16_t *qp = a.q + ((size_t)(r * T + j) * a.Hq + h) * kAD + 16 * g4;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int p = p0 + 64 * wv + 16 * kt + n;
-        const float v = row < M && p <= lim ? acc[rt][kt][i] * sc : kNegInf;
-        acc[rt][kt][i] = v;
-        m = fmaxf(m, v);
+    for (int st = 0; st < 4; ++st) qa[rt][st] = ld16(qp + 64 * (st >> 1) + 8 * (st & 1));
+  }
+  WaveAcc<NRT> acc;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    acc.m[rt] = kNegInf;
+    acc.l[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc.o[rt][dt] = f32x4a{0.f, 0.f, 0.f, 0.f};
+  }
+  // ---- this step's own positions that fall in this workgroup's tiles: the
+  // T new keys and values quantised once (x / scale in fp32, nearest E4M3
+  // code) into LDS, where the tile loop takes them from, and written to the
+  // cache by this workgroup, their only owner
+  const int own0 = max(L, tb * kATile), own1 = min(len, te * kATile);
+  if (own0 < own1) {                                     // workgroup-uniform
+    for (int e = tid; e < 2 * T * 16; e += 256) {       // (K or V, token j, 8 head-dim elements)
+      const int kind = e / (T * 16), j = (e >> 4) % T, part = e & 15;
+      const uint16_t *src = (kind ? a.v_new : a.k_new) + (new_row0 + (size_t)j * a.Hkv) * kAD + 8 * part;
+      const uint2 c = quant8(src, kind ? vsc : ksc);
+      *reinterpret_cast<uint2 *>(newc + (kind * 8 + j) * kAD + 8 * part) = c;
+      const int p = L + j;
+      if (p >= own0 && p < own1)
+        *reinterpret_cast<uint2 *>((kind ? a.v_cache : a.k_cache) + cbase + (size_t)p * kAD + 8 * part) = c;
+    }
+    __syncthreads();
+  }
+  uint8_t *vsh = lds + wv * kAVWave;
+  const float sc = a.softmax_scale * ksc * 1.44269504088896340736f;   // scores in log2 units
+
+  for (int t = tb; t < te; ++t) {
+    const int p0 = t * kATile + 64 * wv;
+    const bool live = p0 < len;                          // wave-uniform
+    f32x4a sa[NRT][4];
+    if (!PF) load_tile(t);
+    if (live) {
+      if (p0 + 64 > L) {                                 // wave-uniform: the slice holds new or past-the-end keys
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int p = p0 + slice_key(vm >> 2, vm & 3, k);
+          // past the end: zero (their P is 0, but 0 * NaN is not); new: from LDS
+          if (p >= len) vst[k] = make_uint4(0u, 0u, 0u, 0u);
+          else if (p >= L) vst[k] = *reinterpret_cast<const uint4 *>(newc + (8 + p - L) * kAD + 16 * vdg);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int p = p0 + 16 * kt + n;
+          if (p >= L && p < len) {
+            kr[kt][0] = *reinterpret_cast<const uint4 *>(newc + (p - L) * kAD + 16 * g4);
+            kr[kt][1] = *reinterpret_cast<const uint4 *>(newc + (p - L) * kAD + 64 + 16 * g4);
+          }
+        }
       }
-      mx[rt][i] = row16_max(m);
-    }
-  if (n == 0)
+      // V^T into this wave's slice: head-dim row d holds the 64 keys in slice
+      // order, chunk m (8 bytes) = the keys this lane loaded (the LDS queue of
+      // a wave is in order, so the previous tile's reads are done)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+      for (int c = 0; c < 4; ++c) {
+        unsigned lo[4], hi[4];
+        transpose4(word(vst[0], c), word(vst[1], c), word(vst[2], c), word(vst[3], c), lo);
+        transpose4(word(vst[4], c), word(vst[5], c), word(vst[6], c), word(vst[7], c), hi);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) redm[wv][rt * 16 + 4 * g4 + i] = mx[rt][i];
-  __syncthreads();
-  if (tid < kAMaxRows) rowm[tid] = fmaxf(fmaxf(redm[0][tid], redm[1][tid]), fmaxf(redm[2][tid], redm[3][tid]));
-  __syncthreads();
-  // ---- P = exp(S - max) (0 where masked), the chunk's row sums
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rt * 16 + 4 * g4 + i;
-      const float m = rowm[row];
-      float sum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const float v = acc[rt][kt][i];
-        const float p = v == kNegInf ? 0.f : expf(v - m);
-        psh[row][64 * wv + 16 * kt + n] = p;
-        sum += p;
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint2 *>(vsh + (16 * vdg + 4 * c + j) * kAVRow + 8 * vm) = make_uint2(lo[j], hi[j]);
       }
-      sum = row16_sum(sum);
-      if (n == 0) redl[wv][row] = sum;
+      // S^T = K Q^T: keys 16 kt + 4 g4 + i of query row 16 rt + n
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sa[rt][kt] = f32x4a{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const uint4 &w = kr[kt][st >> 1];
+          const uint4 kb = (st & 1) ? fp8x8_bf16(w.z, w.w) : fp8x8_bf16(w.x, w.y);
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) sa[rt][kt] = mfma16(kb, qa[rt][st], sa[rt][kt]);
+        }
     }
+    if (PF && t + 1 < te) load_tile(t + 1);              // overlaps the softmax and P V below
+    if (live) {
+      uint4 ph[NRT][2], pl[NRT][2];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int row = 16 * rt + n, lim = row < M ? L + row / grp : -1;   // last visible position
+        float mt = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = p0 + 16 * kt + 4 * g4 + i <= lim ? sa[rt][kt][i] * sc : kNegInf;
+            sa[rt][kt][i] = v;
+            mt = fmaxf(mt, v);
+          }
+        mt = max4g(mt);
+        const float mn = fmaxf(acc.m[rt], mt);
+        const float ms = mn == kNegInf ? 0.f : mn;       // nothing visible yet: every p below is 0
+        const float alpha = __builtin_amdgcn_exp2f(acc.m[rt] - ms);   // 0 from -inf, 1 if unchanged
+        acc.m[rt] = mn;
+        acc.l[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc.o[rt][dt] *= alpha;
+        float x[2][8];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sa[rt][kt][i] - ms);   // masked: exp2(-inf) = 0
+            acc.l[rt] += p;
+            x[kt >> 1][4 * (kt & 1) + i] = p;
+          }
+        split_hi_lo(x[0], ph[rt][0], pl[rt][0]);
+        split_hi_lo(x[1], ph[rt][1], pl[rt][1]);
+      }
+      // O^T += V^T P^T: head-dim rows 16 dt + n, chunk 4 q + g4 of the slice
+      __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): this wave's V^T writes are done
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const uint2 c = *reinterpret_cast<const uint2 *>(vsh + (16 * dt + n) * kAVRow + 8 * (4 * q + g4));
+          const uint4 va = fp8x8_bf16(c.x, c.y);
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            acc.o[rt][dt] = mfma16(va, ph[rt][q], acc.o[rt][dt]);
+            acc.o[rt][dt] = mfma16(va, pl[rt][q], acc.o[rt][dt]);
+          }
+        }
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) acc.l[rt] = sum4g(acc.l[rt]);
+
+  // ---- merge the 4 waves through LDS: 3 and 2 into 1 and 0, then 1 into 0
+  float *part = reinterpret_cast<float *>(lds);
+  constexpr int kPart = kASlot;                          // floats of one partial in LDS
   __syncthreads();
-  if (tid < kAMaxRows) rowl[tid] = ((redl[0][tid] + redl[1][tid]) + redl[2][tid]) + redl[3][tid];
-  // ---- O = P V: wave wv takes columns 32 wv .. 32 wv + 31 over the chunk
-  f32x4a o[2][2];
+  if (wv >= 2) put_partial<NRT>(part + (wv - 2) * kPart, acc, n, g4);
+  __syncthreads();
+  if (wv < 2) {
+    const float *pb = part + wv * kPart;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) o[rt][dt] = f32x4a{0.f, 0.f, 0.f, 0.f};
-  for (int ks = 0; ks < kAChunk / 32; ++ks) {
-    uint4 vb[2];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const uint8_t *vp = vsh + (32 * ks + 8 * g4) * kAD + 32 * wv + 16 * dt + n;
-      unsigned h[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) h[jj] = lut[vp[jj * kAD]];
-      vb[dt] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int row = 16 * rt + n;
+      merge_rows<NRT>(acc, rt, pb[kAMaxRows * kAD + row], pb[kAMaxRows * kAD + kAMaxRows + row], pb + row * kAD, g4);
     }
+  }
+  __syncthreads();
+  if (wv == 1) put_partial<NRT>(part, acc, n, g4);
+  __syncthreads();
+  if (wv == 0) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      if (rt >= nrt) break;
-      const float *pp = &psh[rt * 16 + n][32 * ks + 8 * g4];
-      const float4 x0 = *reinterpret_cast<const float4 *>(pp), x1 = *reinterpret_cast<const float4 *>(pp + 4);
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      uint4 hi, lo;
-      split_hi_lo(x, hi, lo);
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int row = 16 * rt + n;
+      merge_rows<NRT>(acc, rt, part[kAMaxRows * kAD + row], part[kAMaxRows * kAD + kAMaxRows + row],
+                      part + row * kAD, g4);
+    }
+    if (nact == 1) {
+      // the request's only workgroup: outputs directly
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        o[rt][dt] = mfma16(hi, vb[dt], o[rt][dt]);
-        o[rt][dt] = mfma16(lo, vb[dt], o[rt][dt]);
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int row = 16 * rt + n;
+        if (row < M) {
+          const int j = row / grp, h = g * grp + row % grp;
+          float *op = a.out + ((size_t)(r * T + j) * a.Hq + h) * kAD + 4 * g4;
+          const float f = vsc / acc.l[rt];
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<float4 *>(op + 16 * dt) = make_float4(acc.o[rt][dt][0] * f, acc.o[rt][dt][1] * f,
+                                                                    acc.o[rt][dt][2] * f, acc.o[rt][dt][3] * f);
+        }
+      }
+    } else {
+      // this workgroup's partial to its slot, written through to the device coherence point
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          a.slots + ((size_t)rg * a.n_split + s) * kASlot, 0, kASlot * 4, 0x00020000);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int row = 16 * rt + n;
+        if (row < M) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4ua, acc.o[rt][dt]), rs,
+                                                   (row * kAD + 16 * dt + 4 * g4) * 4, 0, kCoherent);
+          if (g4 == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.m[rt]), rs, (kAMaxRows * kAD + row) * 4, 0,
+                                                  kCoherent);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.l[rt]), rs,
+                                                  (kAMaxRows * kAD + kAMaxRows + row) * 4, 0, kCoherent);
+          }
+        }
+      }
+      wt_stores_complete();
+      if (lane == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned)nact - 1u;
+        if (s_last) __hip_atomic_store(a.counters + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  // ---- this chunk's slot: P V (row, column), max, sum; written through
-  float *slot = a.slots + ((size_t)rg * a.n_chunk_max + c) * kASlot;
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rt * 16 + 4 * g4 + i, d = 32 * wv + 16 * dt + n;
-        if (row < M) __hip_atomic_store(slot + row * kAD + d, o[rt][dt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-  __syncthreads();
-  if (tid < M) {
-    __hip_atomic_store(slot + kAMaxRows * kAD + tid, rowm[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(slot + kAMaxRows * kAD + kAMaxRows + tid, rowl[tid], __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
-  wt_stores_complete();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(a.counters + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (unsigned)nch - 1u;
-    if (s_last) __hip_atomic_store(a.counters + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (nact == 1) return;
   __syncthreads();
   if (!s_last) return;
-  // ---- the last chunk of (request, KV head): combine the slots in chunk order
-  const float *slots = a.slots + (size_t)rg * a.n_chunk_max * kASlot;
-  for (int q = tid; q < M * (kAD / 16); q += 256) {
-    const int row = q / (kAD / 16), d0 = 16 * (q % (kAD / 16));
-    float m = kNegInf, l = 0.f, acc16[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc16[e] = 0.f;
-    for (int cc = 0; cc < nch; ++cc) {
-      const float *sl = slots + (size_t)cc * kASlot;
-      const float mc = __hip_atomic_load(sl + kAMaxRows * kAD + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (mc == kNegInf) continue;   // no visible position of this row in that chunk
-      const float lc = __hip_atomic_load(sl + kAMaxRows * kAD + kAMaxRows + row, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-      if (mc > m) {
-        const float f = m == kNegInf ? 0.f : expf(m - mc);
-        l *= f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc16[e] *= f;
-        m = mc;
-      }
-      const float f = expf(mc - m);
-      l += lc * f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        acc16[e] += f * __hip_atomic_load(sl + row * kAD + d0 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- the last workgroup of (request, KV head): combine the nact partials
+  // in slot order.  Phase A: every slot's max and sum -> per-row weights
+  // exp(m_c - max) * v_scale / total; phase B: outputs = sum_c weight * O_c.
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      a.slots + (size_t)rg * a.n_split * kASlot, 0, a.n_split * kASlot * 4, 0x00020000);
+  float *wm = reinterpret_cast<float *>(lds), *wl = wm + kAMaxSplit * kAMaxRows;
+  for (int qi = tid; qi < nact * M; qi += 256) {
+    const int c = qi / M, row = qi % M, base = c * kASlot + kAMaxRows * kAD + row;
+    wm[c * kAMaxRows + row] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, base * 4, 0, kCoherent));
+    wl[c * kAMaxRows + row] =
+        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (base + kAMaxRows) * 4, 0, kCoherent));
+  }
+  __syncthreads();
+  if (tid < M) {
+    float mx = kNegInf;
+    for (int c = 0; c < nact; ++c) mx = fmaxf(mx, wm[c * kAMaxRows + tid]);
+    float tot = 0.f;
+    for (int c = 0; c < nact; ++c) {
+      const float mc = wm[c * kAMaxRows + tid];
+      const float f = __builtin_amdgcn_exp2f(mc - mx);   // 0 for a slot at -inf
+      wm[c * kAMaxRows + tid] = f;
+      tot += f * wl[c * kAMaxRows + tid];
+    }
+    const float scl = vsc / tot;
+    for (int c = 0; c < nact; ++c) wm[c * kAMaxRows + tid] *= scl;
+  }
+  __syncthreads();
+  for (int qi = tid; qi < M * (kAD / 4); qi += 256) {
+    const int row = qi / (kAD / 4), d4 = qi % (kAD / 4);
+    f32x4a o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int c = 0; c < nact; ++c) {
+      const f32x4a v = __builtin_bit_cast(
+          f32x4a, __builtin_amdgcn_raw_buffer_load_b128(rs, (c * kASlot + row * kAD + 4 * d4) * 4, 0, kCoherent));
+      o += wm[c * kAMaxRows + row] * v;
     }
     const int j = row / grp, h = g * grp + row % grp;
-    float *op = a.out + ((size_t)(r * a.T + j) * a.Hq + h) * kAD + d0;
-    const float inv = a.v_scale[g] / l;  // V entered as its E4M3 values: scale once here
-#pragma unroll
-    for (int e = 0; e < 16; e += 4)
-      *reinterpret_cast<float4 *>(op + e) = make_float4(acc16[e] * inv, acc16[e + 1] * inv, acc16[e + 2] * inv,
-                                                        acc16[e + 3] * inv);
+    *reinterpret_cast<float4 *>(a.out + ((size_t)(r * T + j) * a.Hq + h) * kAD + 4 * d4) =
+        make_float4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -394,6 +546,7 @@ int check_cfg(const decode_attention_config *c) {
     return fail(nullptr, DL_ERR_UNSUPPORTED, "cache_len=%d: need 1..2^20", c->cache_len);
   if (!(c->softmax_scale > 0.f) || !std::isfinite(c->softmax_scale))
     return fail(nullptr, DL_ERR_UNSUPPORTED, "softmax_scale must be positive and finite");
+  if (c->max_splits < 0) return fail(nullptr, DL_ERR_INVALID_ARG, "max_splits=%d is negative", c->max_splits);
   return DL_OK;
 }
 
@@ -424,8 +577,24 @@ int check_io(const decode_attention_config *c, const decode_attention_io *io) {
   return DL_OK;
 }
 
+int n_split_of(const decode_attention_config *c) {   // partial slots per (request, KV head)
+  return std::min(kAMaxSplit, (c->cache_len + kATile - 1) / kATile);
+}
+
 size_t slot_bytes(const decode_attention_config *c) {
-  return (size_t)c->max_requests * c->n_kv_heads * ((c->cache_len + kAChunk - 1) / kAChunk) * kASlot * 4;
+  return (size_t)c->max_requests * c->n_kv_heads * n_split_of(c) * kASlot * 4;
+}
+
+int cus_of_current_device() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    n = std::max(1, host::cu_count(dev));
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 }  // namespace
@@ -469,14 +638,23 @@ int decode_attention_step(const decode_attention_config *cfg, const decode_atten
   a.max_past = io->max_past;
   a.grp = cfg->n_q_heads / cfg->n_kv_heads;
   a.M = a.grp * a.T;
-  a.n_chunk_max = (cfg->cache_len + kAChunk - 1) / kAChunk;
+  a.n_split = n_split_of(cfg);
   a.softmax_scale = cfg->softmax_scale;
-  const int rows = a.R * a.T * a.Hkv;
-  hipLaunchKernelGGL(attn_append, dim3((rows * 16 + 255) / 256), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return host::fail(nullptr, DL_ERR_HIP, "attention append launch failed: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(attn_chunk, dim3((io->max_past + a.T + kAChunk - 1) / kAChunk, a.R * a.Hkv), dim3(256), 0, st, a);
-  e = hipGetLastError();
+  // splits per (request, KV head): about one workgroup per CU in all (more
+  // workgroups each pay the partial hand-off and the combine again), at most
+  // n_split, each taking tps consecutive tiles of 256 positions
+  const int rg = a.R * a.Hkv;
+  const int tiles = (io->max_past + a.T + kATile - 1) / kATile;
+  const int want = std::max(1, (cus_of_current_device() + rg - 1) / rg);
+  int split = std::min(std::min(tiles, a.n_split), want);
+  if (cfg->max_splits > 0) split = std::min(split, cfg->max_splits);
+  a.tps = (tiles + split - 1) / split;
+  split = (tiles + a.tps - 1) / a.tps;
+  const dim3 grid(split, rg);
+  void (*kern)(AttnArgs) = a.M <= 16 ? (a.tps > 1 ? attn_step<1, true> : attn_step<1, false>)
+                                     : (a.tps > 1 ? attn_step<2, true> : attn_step<2, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return host::fail(nullptr, DL_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return DL_OK;
 }

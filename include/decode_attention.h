@@ -46,7 +46,10 @@ extern "C" {
  *   max_tokens T    : 1..8, with (Hq / Hkv) * T <= 32 query rows per KV head
  *   max_requests R  : 1..1024
  *   cache_len C     : 1..(1 << 20) positions per request and KV head
- *   softmax_scale   : finite and > 0 */
+ *   softmax_scale   : finite and > 0
+ *   max_splits      : 0 (automatic) or a cap on the workgroups that share one
+ *                     request's positions (a caller that shares the GPU with
+ *                     other work can keep the launch small); >= 0 */
 typedef struct {
   int32_t n_q_heads;
   int32_t n_kv_heads;
@@ -55,6 +58,7 @@ typedef struct {
   int32_t max_requests;
   int32_t cache_len;
   float softmax_scale;
+  int32_t max_splits;
 } decode_attention_config;
 
 /* One step.  Caller-owned device memory, valid until the enqueued work ends. */
@@ -77,18 +81,19 @@ typedef struct {
 } decode_attention_io;
 
 /* Bytes of workspace a call site with this configuration needs (0 if invalid).
- * It holds per-chunk partial results (at most ceil(C / 256) chunks of 256
- * positions per request and KV head) and one arrival counter per request and
- * KV head.  Host-only. */
+ * It holds the partial results of the workgroups that share one request's
+ * positions (at most min(64, ceil(C / 256)) per request and KV head) and one
+ * arrival counter per request and KV head.  Host-only. */
 DL_API size_t decode_attention_workspace_bytes(const decode_attention_config *cfg);
 
 /* Host-only validation of a configuration and of one step's arguments. */
 DL_API int decode_attention_check(const decode_attention_config *cfg, const decode_attention_io *io);
 
-/* Enqueue one attention step on `hip_stream` (two kernels: the append, then
- * the attention over chunks of 256 positions with the chunks of each request
- * and KV head combined by the last to finish) and return without
- * synchronising.  No allocation, no host copy, no memset; capturable in a HIP
+/* Enqueue one attention step on `hip_stream` (one kernel: workgroups take
+ * consecutive tiles of 256 positions of one request and KV head, quantise and
+ * write the step's own positions where they fall, and the last workgroup of a
+ * request and KV head to finish combines their partial results) and return
+ * without synchronising.  No allocation, no host copy, no memset; capturable in a HIP
  * graph.  A device-side past_len[r] above max_past, or with
  * past_len[r] + T > cache_len, makes request r's outputs NaN and writes none
  * of its cache positions.  Steps that share a workspace must not overlap. */

@@ -225,8 +225,13 @@ def test_attention_workspace_and_validation():
     chunks = -(-4096 // 256)
     slots = 64 * 1 * chunks * (32 * 128 + 64) * 4
     assert at.workspace_bytes(c) == _a256(slots) + _a256(64 * 4)
+    # at most 64 partial slots per request and KV head, whatever the cache length
+    big = _attn_cfg(cache_len=1 << 20, max_requests=2)
+    assert at.workspace_bytes(big) == _a256(2 * 64 * (32 * 128 + 64) * 4) + _a256(2 * 4)
+    assert at.workspace_bytes(_attn_cfg(max_splits=3)) == at.workspace_bytes(c)
     for field, value in (("head_dim", 64), ("max_tokens", 9), ("max_tokens", 0), ("n_kv_heads", 3),
-                         ("n_q_heads", 40), ("cache_len", 0), ("softmax_scale", 0.0), ("max_requests", 2000)):
+                         ("n_q_heads", 40), ("cache_len", 0), ("softmax_scale", 0.0), ("max_requests", 2000),
+                         ("max_splits", -1)):
         bad = _attn_cfg(**{field: value}) if field != "head_dim" else at.make_attn_config(4, 1, 8, 64, 4096, 0.1, 64)
         assert at.workspace_bytes(bad) == 0, field
     # (Hq / Hkv) * T must fit 32 query rows per KV head

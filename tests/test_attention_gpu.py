@@ -42,10 +42,11 @@ def _at():
 class Dev:
     """One step's device buffers (outputs poisoned with NaN) and its workspace."""
 
-    def __init__(self, st: attn_gen.AttnStep, max_tokens=None, max_requests=None, max_past=None):
+    def __init__(self, st: attn_gen.AttnStep, max_tokens=None, max_requests=None, max_past=None, max_splits=0):
         at = _at()
         R, T, Hq, Hkv, D, C = st.shape
-        self.cfg = at.make_attn_config(Hq, Hkv, max_tokens or T, max_requests or R, C, st.softmax_scale)
+        self.cfg = at.make_attn_config(Hq, Hkv, max_tokens or T, max_requests or R, C, st.softmax_scale,
+                                       max_splits=max_splits)
         d = "cuda"
         self.q, self.k_new, self.v_new = (bf16_tensor(a, d) for a in (st.q, st.k_new, st.v_new))
         self.k_cache = torch.from_numpy(np.ascontiguousarray(st.k_cache)).to(d)
@@ -111,6 +112,24 @@ def run_case(name, st, **kw):
 ])
 def test_parity(name, R, T, Hq, Hkv, C, lo, hi):
     run_case(name, attn_gen.draw(R, T, Hq, Hkv, C, lo, hi, seed=zlib.crc32(name.encode()) % 1000))
+
+
+@pytest.mark.parametrize("name,R,T,Hq,Hkv,C,lo,hi,splits", [
+    ("one_wg_12_tiles", 2, 8, 4, 1, 3000, 2700, 2990, 1),     # one workgroup loops 12 tiles, no combine
+    ("splits_of_3", 3, 8, 4, 1, 3000, 1500, 2990, 5),         # 3 tiles per workgroup, ragged last split
+    ("splits_32rows", 2, 4, 16, 2, 2100, 1000, 2090, 3),      # 32 rows with the prefetching loop
+    ("splits_T1", 4, 1, 4, 1, 2600, 600, 2590, 2),
+])
+def test_multi_tile_splits(name, R, T, Hq, Hkv, C, lo, hi, splits):
+    """Workgroups that take several tiles (forced through max_splits)."""
+    run_case(name, attn_gen.draw(R, T, Hq, Hkv, C, lo, hi, seed=zlib.crc32(name.encode()) % 1000),
+             max_splits=splits)
+
+
+def test_long_context_beyond_64_tiles():
+    """More tiles than partial slots: the automatic split takes 2+ tiles each."""
+    st = attn_gen.draw(1, 8, 4, 1, 20480, 20000, 20470, seed=16)
+    run_case("long_ctx_20k", st)
 
 
 def test_chunk_boundaries():
