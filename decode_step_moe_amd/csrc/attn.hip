@@ -43,11 +43,14 @@ namespace {
 
 constexpr int kAD = 128;                 // head size
 constexpr int kATile = 256;              // cache positions per workgroup tile (64 per wave)
-constexpr int kAMaxRows = 32;            // query rows per KV head
-constexpr int kAMaxSplit = 64;           // workgroups per (request, KV head)
-constexpr int kASlot = kAMaxRows * kAD + 2 * kAMaxRows;  // floats per partial: O [row][d], max, sum
+constexpr int kAMaxRows = 32;            // query rows per KV head (in row splits of 16 per workgroup)
+constexpr int kAMaxSplit = 64;           // workgroups per (request, KV head, row split)
+constexpr int kASlot = 16 * kAD + 2 * 16; // floats per partial: O [row][d], max, sum of 16 rows
 constexpr int kAVRow = 72;               // LDS bytes per head-dim row of a wave's V^T slice (64 keys + pad)
 constexpr int kAVWave = kAD * kAVRow;    // LDS bytes of one wave's V^T slice
+constexpr int kAPoRow = 20;              // floats per head-dim row of a wave's merge area (16 rows + pad)
+constexpr int kALds = (4 * kAVWave > (128 + 4 * kAD * kAPoRow) * 4) ? 4 * kAVWave : (128 + 4 * kAD * kAPoRow) * 4;
+static_assert(2 * kAMaxSplit * 16 * 4 <= kALds, "combine weights");
 constexpr unsigned kCoherent = 16;       // buffer cache policy: coherent at agent scope
 
 typedef __bf16 bf16x8a __attribute__((ext_vector_type(8)));
@@ -63,8 +66,8 @@ struct AttnArgs {
   const float *k_scale, *v_scale;
   float *out;
   float *slots;        // [max_requests * Hkv][n_split][kASlot]
-  unsigned *counters;  // [max_requests * Hkv]
-  int R, T, Hq, Hkv, C, max_past, grp, M, tps, n_split;
+  unsigned *counters;  // [max_requests * Hkv * row splits]
+  int R, T, Hq, Hkv, C, max_past, grp, M, RS, tps, n_split;
   float softmax_scale;
 };
 
@@ -162,77 +165,30 @@ __device__ __forceinline__ bool request_bad(const AttnArgs &a, int L) {
 // 16 kt + 4 g4 + i of its query row) are exactly the P^T operand it supplies.
 __device__ __forceinline__ int slice_key(int q, int g4, int jj) { return 32 * q + 16 * (jj >> 2) + 4 * g4 + (jj & 3); }
 
-// A wave's running state for up to 16 NRT query rows: lane (n, g4) holds row
-// 16 rt + n, its max (same in the 4 lane groups), its partial sum over the
-// lane's own keys, and O^T columns d = 16 dt + 4 g4 + i.
-template <int NRT>
-struct WaveAcc {
-  float m[NRT], l[NRT];
-  f32x4a o[NRT][8];
-};
-
-// Merge partial (mb, lb, Ob) of the same rows into a (softmax rescaling;
-// maxima are in log2 units, scores having been scaled by log2 e).
-template <int NRT>
-__device__ __forceinline__ void merge_rows(WaveAcc<NRT> &a, int rt, float mb, float lb, const float *ob_row,
-                                           int g4) {
-  const float mn = fmaxf(a.m[rt], mb);
-  if (mn == -__builtin_inff()) return;     // neither side has seen a visible key of this row
-  const float fa = __builtin_amdgcn_exp2f(a.m[rt] - mn);   // 0 for a side at -inf
-  const float fb = __builtin_amdgcn_exp2f(mb - mn);
-  a.m[rt] = mn;
-  a.l[rt] = a.l[rt] * fa + lb * fb;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const float4 b = *reinterpret_cast<const float4 *>(ob_row + 16 * dt + 4 * g4);
-    a.o[rt][dt][0] = a.o[rt][dt][0] * fa + b.x * fb;
-    a.o[rt][dt][1] = a.o[rt][dt][1] * fa + b.y * fb;
-    a.o[rt][dt][2] = a.o[rt][dt][2] * fa + b.z * fb;
-    a.o[rt][dt][3] = a.o[rt][dt][3] * fa + b.w * fb;
-  }
-}
-
-// A partial into LDS as O [row][d], max [32], sum [32] (sums already over the 4 lane groups).
-template <int NRT>
-__device__ __forceinline__ void put_partial(float *part, const WaveAcc<NRT> &a, int n, int g4) {
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int row = 16 * rt + n;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4 *>(part + row * kAD + 16 * dt + 4 * g4) =
-          make_float4(a.o[rt][dt][0], a.o[rt][dt][1], a.o[rt][dt][2], a.o[rt][dt][3]);
-    if (g4 == 0) {
-      part[kAMaxRows * kAD + row] = a.m[rt];
-      part[kAMaxRows * kAD + kAMaxRows + row] = a.l[rt];
-    }
-  }
-}
-
 // PF: the next tile's loads are issued during this tile's softmax and P V
-// (used when a workgroup takes more than one tile; the registers they hold
-// leave room for one workgroup per CU at 32 rows).
-// One workgroup: tiles [tb, te) of one (request, KV head), 4 waves each
-// taking 64 keys of every tile with a softmax of their own; the waves merge
-// at the end; the workgroup's partial goes to the output directly when it is
-// the request's only one, else to its slot, and the last workgroup of the
-// (request, KV head) to arrive combines the slots.
-template <int NRT, bool PF>
-__global__ void __launch_bounds__(256, (NRT == 2 && PF) ? 1 : 2) attn_step(AttnArgs a) {
-  __shared__ __align__(16) uint8_t lds[4 * kAVWave];   // V^T slices; later partials and combine weights
+// (used when a workgroup takes more than one tile).
+// One workgroup: tiles [tb, te) of one (request, KV head) and 16 of its query
+// rows (row split rs), 4 waves each taking 64 keys of every tile with a
+// softmax of their own; the waves merge at the end; the workgroup's partial
+// goes to the output directly when it is the request's only one, else to its
+// slot, and the last workgroup of the (request, KV head, row split) to arrive
+// combines the slots.
+template <bool PF>
+__global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
+  __shared__ __align__(16) uint8_t lds[kALds];         // V^T slices; later the wave merge and combine weights
   __shared__ __align__(16) uint8_t newc[2 * 8 * kAD];  // this step's K and V codes [K | V][token][d]
   __shared__ int s_last;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g4 = lane >> 4;
-  const int s = blockIdx.x, rg = blockIdx.y, r = rg / a.Hkv, g = rg % a.Hkv;
+  const int s = blockIdx.x, rgs = blockIdx.y, rg = rgs / a.RS, rs = rgs % a.RS, r = rg / a.Hkv, g = rg % a.Hkv;
   const int L = a.past_len[r];
-  const int M = a.M, grp = a.grp, T = a.T;
+  const int M = a.M, grp = a.grp, T = a.T, row0 = 16 * rs;
   constexpr float kNegInf = -__builtin_inff();
   if (request_bad(a, L)) {
     // an impossible length: this request's outputs are NaN, nothing else runs
     if (s == 0)
-      for (int q = tid; q < M * kAD; q += 256) {
-        const int row = q / kAD, d = q % kAD, j = row / grp, h = g * grp + row % grp;
-        a.out[((size_t)(r * T + j) * a.Hq + h) * kAD + d] = __builtin_nanf("");
+      for (int q = tid; q < 16 * kAD; q += 256) {
+        const int row = row0 + q / kAD, d = q % kAD, j = row / grp, h = g * grp + row % grp;
+        if (row < M) a.out[((size_t)(r * T + j) * a.Hq + h) * kAD + d] = __builtin_nanf("");
       }
     return;
   }
@@ -270,27 +226,24 @@ __global__ void __launch_bounds__(256, (NRT == 2 && PF) ? 1 : 2) attn_step(AttnA
     }
   };
   if (PF) load_tile(tb);
-  // query fragments: row 16 rt + n, head-dim elements in the K fragments' order
-  uint4 qa[NRT][4];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int row = min(16 * rt + n, M - 1), j = row / grp, h = g * grp + row % grp;
+  // query fragments: row row0 + n, head-dim elements in the K fragments' order
+  uint4 qa[4];
+  {
+    const int row = min(row0 + n, M - 1), j = row / grp, h = g * grp + row % grp;
     const uint16_t *qp = a.q + ((size_t)(r * T + j) * a.Hq + h) * kAD + 16 * g4;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) qa[rt][st] = ld16(qp + 64 * (st >> 1) + 8 * (st & 1));
+    for (int st = 0; st < 4; ++st) qa[st] = ld16(qp + 64 * (st >> 1) + 8 * (st & 1));
   }
-  WaveAcc<NRT> acc;
+  // a wave's running state for row row0 + n: its maximum (the same in the 4
+  // lane groups), its sum over the lane's own keys, O^T columns d = 16 dt + 4 g4 + i
+  float am = kNegInf, al = 0.f;
+  f32x4a ao[8];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    acc.m[rt] = kNegInf;
-    acc.l[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc.o[rt][dt] = f32x4a{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int dt = 0; dt < 8; ++dt) ao[dt] = f32x4a{0.f, 0.f, 0.f, 0.f};
   // ---- this step's own positions that fall in this workgroup's tiles: the
   // T new keys and values quantised once (x / scale in fp32, nearest E4M3
   // code) into LDS, where the tile loop takes them from, and written to the
-  // cache by this workgroup, their only owner
+  // cache by row split 0 of the workgroup, their only owner
   const int own0 = max(L, tb * kATile), own1 = min(len, te * kATile);
   if (own0 < own1) {                                     // workgroup-uniform
     for (int e = tid; e < 2 * T * 16; e += 256) {       // (K or V, token j, 8 head-dim elements)
@@ -299,18 +252,19 @@ __global__ void __launch_bounds__(256, (NRT == 2 && PF) ? 1 : 2) attn_step(AttnA
       const uint2 c = quant8(src, kind ? vsc : ksc);
       *reinterpret_cast<uint2 *>(newc + (kind * 8 + j) * kAD + 8 * part) = c;
       const int p = L + j;
-      if (p >= own0 && p < own1)
+      if (rs == 0 && p >= own0 && p < own1)
         *reinterpret_cast<uint2 *>((kind ? a.v_cache : a.k_cache) + cbase + (size_t)p * kAD + 8 * part) = c;
     }
     __syncthreads();
   }
   uint8_t *vsh = lds + wv * kAVWave;
   const float sc = a.softmax_scale * ksc * 1.44269504088896340736f;   // scores in log2 units
+  const int lim = row0 + n < M ? L + (row0 + n) / grp : -1;           // this lane's row's last visible position
 
   for (int t = tb; t < te; ++t) {
     const int p0 = t * kATile + 64 * wv;
     const bool live = p0 < len;                          // wave-uniform
-    f32x4a sa[NRT][4];
+    f32x4a sa[4];
     if (!PF) load_tile(t);
     if (live) {
       if (p0 + 64 > L) {                                 // wave-uniform: the slice holds new or past-the-end keys
@@ -342,56 +296,61 @@ __global__ void __launch_bounds__(256, (NRT == 2 && PF) ? 1 : 2) attn_step(AttnA
         for (int j = 0; j < 4; ++j)
           *reinterpret_cast<uint2 *>(vsh + (16 * vdg + 4 * c + j) * kAVRow + 8 * vm) = make_uint2(lo[j], hi[j]);
       }
-      // S^T = K Q^T: keys 16 kt + 4 g4 + i of query row 16 rt + n
+      // S^T = K Q^T: keys 16 kt + 4 g4 + i of query row row0 + n
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) sa[rt][kt] = f32x4a{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < 4; ++kt) sa[kt] = f32x4a{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const uint4 &w = kr[kt][st >> 1];
           const uint4 kb = (st & 1) ? fp8x8_bf16(w.z, w.w) : fp8x8_bf16(w.x, w.y);
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) sa[rt][kt] = mfma16(kb, qa[rt][st], sa[rt][kt]);
+          sa[kt] = mfma16(kb, qa[st], sa[kt]);
         }
     }
     if (PF && t + 1 < te) load_tile(t + 1);              // overlaps the softmax and P V below
     if (live) {
-      uint4 ph[NRT][2], pl[NRT][2];
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const int row = 16 * rt + n, lim = row < M ? L + row / grp : -1;   // last visible position
-        float mt = kNegInf;
+      uint4 ph[2], pl[2];
+      float mt = kNegInf;
+      if (p0 + 64 > L) {                                 // wave-uniform: only a tile holding a row's end masks
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = p0 + 16 * kt + 4 * g4 + i <= lim ? sa[rt][kt][i] * sc : kNegInf;
-            sa[rt][kt][i] = v;
+            const float v = p0 + 16 * kt + 4 * g4 + i <= lim ? sa[kt][i] * sc : kNegInf;
+            sa[kt][i] = v;
             mt = fmaxf(mt, v);
           }
-        mt = max4g(mt);
-        const float mn = fmaxf(acc.m[rt], mt);
-        const float ms = mn == kNegInf ? 0.f : mn;       // nothing visible yet: every p below is 0
-        const float alpha = __builtin_amdgcn_exp2f(acc.m[rt] - ms);   // 0 from -inf, 1 if unchanged
-        acc.m[rt] = mn;
-        acc.l[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc.o[rt][dt] *= alpha;
-        float x[2][8];
+      } else {
+        const float rowv = lim >= 0 ? 1.f : 0.f;         // rows past M: every key masked
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(sa[rt][kt][i] - ms);   // masked: exp2(-inf) = 0
-            acc.l[rt] += p;
-            x[kt >> 1][4 * (kt & 1) + i] = p;
+            const float v = rowv != 0.f ? sa[kt][i] * sc : kNegInf;
+            sa[kt][i] = v;
+            mt = fmaxf(mt, v);
           }
-        split_hi_lo(x[0], ph[rt][0], pl[rt][0]);
-        split_hi_lo(x[1], ph[rt][1], pl[rt][1]);
       }
+      mt = max4g(mt);
+      const float mn = fmaxf(am, mt);
+      const float ms = mn == kNegInf ? 0.f : mn;         // nothing visible yet: every p below is 0
+      const float alpha = __builtin_amdgcn_exp2f(am - ms);   // 0 from -inf, 1 if unchanged
+      am = mn;
+      al *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) ao[dt] *= alpha;
+      float x[2][8];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sa[kt][i] - ms);   // masked: exp2(-inf) = 0
+          al += p;
+          x[kt >> 1][4 * (kt & 1) + i] = p;
+        }
+      split_hi_lo(x[0], ph[0], pl[0]);
+      split_hi_lo(x[1], ph[1], pl[1]);
       // O^T += V^T P^T: head-dim rows 16 dt + n, chunk 4 q + g4 of the slice
       __builtin_amdgcn_s_waitcnt(0xc07f);                // lgkmcnt(0): this wave's V^T writes are done
 #pragma unroll
@@ -400,127 +359,139 @@ __global__ void __launch_bounds__(256, (NRT == 2 && PF) ? 1 : 2) attn_step(AttnA
         for (int dt = 0; dt < 8; ++dt) {
           const uint2 c = *reinterpret_cast<const uint2 *>(vsh + (16 * dt + n) * kAVRow + 8 * (4 * q + g4));
           const uint4 va = fp8x8_bf16(c.x, c.y);
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            acc.o[rt][dt] = mfma16(va, ph[rt][q], acc.o[rt][dt]);
-            acc.o[rt][dt] = mfma16(va, pl[rt][q], acc.o[rt][dt]);
-          }
+          ao[dt] = mfma16(va, ph[q], ao[dt]);
+          ao[dt] = mfma16(va, pl[q], ao[dt]);
         }
     }
   }
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) acc.l[rt] = sum4g(acc.l[rt]);
+  al = sum4g(al);
 
-  // ---- merge the 4 waves through LDS: 3 and 2 into 1 and 0, then 1 into 0
-  float *part = reinterpret_cast<float *>(lds);
-  constexpr int kPart = kASlot;                          // floats of one partial in LDS
-  __syncthreads();
-  if (wv >= 2) put_partial<NRT>(part + (wv - 2) * kPart, acc, n, g4);
-  __syncthreads();
-  if (wv < 2) {
-    const float *pb = part + wv * kPart;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = 16 * rt + n;
-      merge_rows<NRT>(acc, rt, pb[kAMaxRows * kAD + row], pb[kAMaxRows * kAD + kAMaxRows + row], pb + row * kAD, g4);
-    }
+  // ---- merge the 4 waves: maxima and sums first; then each wave's O^T
+  // scaled to the common maximum into its own area ([d][row], rows padded so
+  // that neither the writes nor the reads below meet a bank conflict), added
+  // in wave order by every thread
+  float *st_m = reinterpret_cast<float *>(lds), *st_l = st_m + 64, *po = st_m + 128;
+  __syncthreads();                                       // every wave is done with its V^T slice
+  if (g4 == 0) {
+    st_m[wv * 16 + n] = am;
+    st_l[wv * 16 + n] = al;
   }
   __syncthreads();
-  if (wv == 1) put_partial<NRT>(part, acc, n, g4);
+  {
+    float mr = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mr = fmaxf(mr, st_m[w * 16 + n]);
+    const float fw = __builtin_amdgcn_exp2f(am - (mr == kNegInf ? 0.f : mr));   // this wave's factor, 0 at -inf
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) po[(wv * kAD + 16 * dt + 4 * g4 + i) * kAPoRow + n] = ao[dt][i] * fw;
+  }
   __syncthreads();
-  if (wv == 0) {
+  // thread: row lrow = tid % 16 of the split, head-dim words d4 = tid / 16 + 16 k
+  const int lrow = tid & 15, grow = row0 + lrow;
+  float mr = kNegInf, lsum = 0.f;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = 16 * rt + n;
-      merge_rows<NRT>(acc, rt, part[kAMaxRows * kAD + row], part[kAMaxRows * kAD + kAMaxRows + row],
-                      part + row * kAD, g4);
+  for (int w = 0; w < 4; ++w) mr = fmaxf(mr, st_m[w * 16 + lrow]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) lsum += st_l[w * 16 + lrow] * __builtin_amdgcn_exp2f(st_m[w * 16 + lrow] - (mr == kNegInf ? 0.f : mr));
+  f32x4a o2[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int d0 = 4 * ((tid >> 4) + 16 * k);
+    o2[k] = f32x4a{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o2[k][i] += po[(w * kAD + d0 + i) * kAPoRow + lrow];
+  }
+  const int gj = grow / grp, gh = g * grp + grow % grp;
+  if (nact == 1) {
+    // the request's only workgroup: outputs directly
+    if (grow < M) {
+      const float f = vsc / lsum;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        *reinterpret_cast<float4 *>(a.out + ((size_t)(r * T + gj) * a.Hq + gh) * kAD + 4 * ((tid >> 4) + 16 * k)) =
+            make_float4(o2[k][0] * f, o2[k][1] * f, o2[k][2] * f, o2[k][3] * f);
     }
-    if (nact == 1) {
-      // the request's only workgroup: outputs directly
+    return;
+  }
+  // this workgroup's partial to its slot, written through to the device coherence point
+  {
+    const __amdgpu_buffer_rsrc_t rs1 = __builtin_amdgcn_make_buffer_rsrc(
+        a.slots + ((size_t)rgs * a.n_split + s) * kASlot, 0, kASlot * 4, 0x00020000);
+    if (grow < M) {
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const int row = 16 * rt + n;
-        if (row < M) {
-          const int j = row / grp, h = g * grp + row % grp;
-          float *op = a.out + ((size_t)(r * T + j) * a.Hq + h) * kAD + 4 * g4;
-          const float f = vsc / acc.l[rt];
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            *reinterpret_cast<float4 *>(op + 16 * dt) = make_float4(acc.o[rt][dt][0] * f, acc.o[rt][dt][1] * f,
-                                                                    acc.o[rt][dt][2] * f, acc.o[rt][dt][3] * f);
-        }
-      }
-    } else {
-      // this workgroup's partial to its slot, written through to the device coherence point
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          a.slots + ((size_t)rg * a.n_split + s) * kASlot, 0, kASlot * 4, 0x00020000);
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const int row = 16 * rt + n;
-        if (row < M) {
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4ua, acc.o[rt][dt]), rs,
-                                                   (row * kAD + 16 * dt + 4 * g4) * 4, 0, kCoherent);
-          if (g4 == 0) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.m[rt]), rs, (kAMaxRows * kAD + row) * 4, 0,
-                                                  kCoherent);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.l[rt]), rs,
-                                                  (kAMaxRows * kAD + kAMaxRows + row) * 4, 0, kCoherent);
-          }
-        }
-      }
-      wt_stores_complete();
-      if (lane == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.counters + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (unsigned)nact - 1u;
-        if (s_last) __hip_atomic_store(a.counters + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int k = 0; k < 2; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4ua, o2[k]), rs1,
+                                               (lrow * kAD + 4 * ((tid >> 4) + 16 * k)) * 4, 0, kCoherent);
+      if (tid < 16) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mr), rs1, (16 * kAD + lrow) * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lsum), rs1, (16 * kAD + 16 + lrow) * 4, 0, kCoherent);
       }
     }
   }
-  if (nact == 1) return;
+  wt_stores_complete();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + rgs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)nact - 1u;
+    if (s_last) __hip_atomic_store(a.counters + rgs, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   if (!s_last) return;
 
-  // ---- the last workgroup of (request, KV head): combine the nact partials
-  // in slot order.  Phase A: every slot's max and sum -> per-row weights
-  // exp(m_c - max) * v_scale / total; phase B: outputs = sum_c weight * O_c.
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      a.slots + (size_t)rg * a.n_split * kASlot, 0, a.n_split * kASlot * 4, 0x00020000);
-  float *wm = reinterpret_cast<float *>(lds), *wl = wm + kAMaxSplit * kAMaxRows;
-  for (int qi = tid; qi < nact * M; qi += 256) {
-    const int c = qi / M, row = qi % M, base = c * kASlot + kAMaxRows * kAD + row;
-    wm[c * kAMaxRows + row] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, base * 4, 0, kCoherent));
-    wl[c * kAMaxRows + row] =
-        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (base + kAMaxRows) * 4, 0, kCoherent));
+  // ---- the last workgroup of (request, KV head, row split): combine the nact
+  // partials in slot order.  Phase A: every slot's max and sum -> per-row
+  // weights exp2(m_c - max) * v_scale / total; phase B: outputs = sum_c
+  // weight * O_c, 16 slots' loads in flight per thread at a time.
+  const int mrows = min(16, M - row0);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      a.slots + (size_t)rgs * a.n_split * kASlot, 0, a.n_split * kASlot * 4, 0x00020000);
+  float *wm = reinterpret_cast<float *>(lds), *wl = wm + kAMaxSplit * 16;
+  for (int qi = tid; qi < nact * 16; qi += 256) {
+    const int c = qi >> 4, row = qi & 15, base = c * kASlot + 16 * kAD + row;
+    wm[qi] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, base * 4, 0, kCoherent));
+    wl[qi] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, (base + 16) * 4, 0, kCoherent));
   }
   __syncthreads();
-  if (tid < M) {
+  if (tid < mrows) {
     float mx = kNegInf;
-    for (int c = 0; c < nact; ++c) mx = fmaxf(mx, wm[c * kAMaxRows + tid]);
+    for (int c = 0; c < nact; ++c) mx = fmaxf(mx, wm[c * 16 + tid]);
     float tot = 0.f;
     for (int c = 0; c < nact; ++c) {
-      const float mc = wm[c * kAMaxRows + tid];
-      const float f = __builtin_amdgcn_exp2f(mc - mx);   // 0 for a slot at -inf
-      wm[c * kAMaxRows + tid] = f;
-      tot += f * wl[c * kAMaxRows + tid];
+      const float f = __builtin_amdgcn_exp2f(wm[c * 16 + tid] - mx);   // 0 for a slot at -inf
+      wm[c * 16 + tid] = f;
+      tot += f * wl[c * 16 + tid];
     }
     const float scl = vsc / tot;
-    for (int c = 0; c < nact; ++c) wm[c * kAMaxRows + tid] *= scl;
+    for (int c = 0; c < nact; ++c) wm[c * 16 + tid] *= scl;
   }
   __syncthreads();
-  for (int qi = tid; qi < M * (kAD / 4); qi += 256) {
-    const int row = qi / (kAD / 4), d4 = qi % (kAD / 4);
-    f32x4a o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int c = 0; c < nact; ++c) {
-      const f32x4a v = __builtin_bit_cast(
-          f32x4a, __builtin_amdgcn_raw_buffer_load_b128(rs, (c * kASlot + row * kAD + 4 * d4) * 4, 0, kCoherent));
-      o += wm[c * kAMaxRows + row] * v;
+  if (grow < M) {
+    f32x4a o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int c0 = 0; c0 < nact; c0 += 16) {
+      f32x4a v[2][16];
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int c = min(c0 + cc, nact - 1);
+          v[k][cc] = __builtin_bit_cast(f32x4a, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rsb, (c * kASlot + lrow * kAD + 4 * ((tid >> 4) + 16 * k)) * 4, 0,
+                                                    kCoherent));
+        }
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc)
+        if (c0 + cc < nact)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) o[k] += wm[(c0 + cc) * 16 + lrow] * v[k][cc];
     }
-    const int j = row / grp, h = g * grp + row % grp;
-    *reinterpret_cast<float4 *>(a.out + ((size_t)(r * T + j) * a.Hq + h) * kAD + 4 * d4) =
-        make_float4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      *reinterpret_cast<float4 *>(a.out + ((size_t)(r * T + gj) * a.Hq + gh) * kAD + 4 * ((tid >> 4) + 16 * k)) =
+          make_float4(o[k][0], o[k][1], o[k][2], o[k][3]);
   }
 }
 
@@ -539,9 +510,10 @@ int check_cfg(const decode_attention_config *c) {
     return fail(nullptr, DL_ERR_UNSUPPORTED, "max_tokens=%d: need 1..8", c->max_tokens);
   if (c->n_q_heads / c->n_kv_heads * c->max_tokens > kAMaxRows)
     return fail(nullptr, DL_ERR_UNSUPPORTED, "(n_q_heads / n_kv_heads) * max_tokens must be <= %d", kAMaxRows);
-  if (c->max_requests < 1 || c->max_requests > 1024 || (long)c->max_requests * c->n_kv_heads > 65535)
-    return fail(nullptr, DL_ERR_UNSUPPORTED, "max_requests=%d: need 1..1024 and max_requests * n_kv_heads <= 65535",
-                c->max_requests);
+  if (c->max_requests < 1 || c->max_requests > 1024 ||
+      (long)c->max_requests * c->n_kv_heads * ((c->n_q_heads / c->n_kv_heads * c->max_tokens + 15) / 16) > 65535)
+    return fail(nullptr, DL_ERR_UNSUPPORTED,
+                "max_requests=%d: need 1..1024 and max_requests * n_kv_heads * row splits <= 65535", c->max_requests);
   if (c->cache_len < 1 || c->cache_len > (1 << 20))
     return fail(nullptr, DL_ERR_UNSUPPORTED, "cache_len=%d: need 1..2^20", c->cache_len);
   if (!(c->softmax_scale > 0.f) || !std::isfinite(c->softmax_scale))
@@ -581,8 +553,12 @@ int n_split_of(const decode_attention_config *c) {   // partial slots per (reque
   return std::min(kAMaxSplit, (c->cache_len + kATile - 1) / kATile);
 }
 
+int rs_of(const decode_attention_config *c) {   // row splits of 16 query rows at max_tokens
+  return (c->n_q_heads / c->n_kv_heads * c->max_tokens + 15) / 16;
+}
+
 size_t slot_bytes(const decode_attention_config *c) {
-  return (size_t)c->max_requests * c->n_kv_heads * n_split_of(c) * kASlot * 4;
+  return (size_t)c->max_requests * c->n_kv_heads * rs_of(c) * n_split_of(c) * kASlot * 4;
 }
 
 int cus_of_current_device() {
@@ -606,7 +582,7 @@ extern "C" {
 
 size_t decode_attention_workspace_bytes(const decode_attention_config *cfg) {
   if (check_cfg(cfg) != DL_OK) return 0;
-  return align256(slot_bytes(cfg)) + align256((size_t)cfg->max_requests * cfg->n_kv_heads * 4);
+  return align256(slot_bytes(cfg)) + align256((size_t)cfg->max_requests * cfg->n_kv_heads * rs_of(cfg) * 4);
 }
 
 int decode_attention_check(const decode_attention_config *cfg, const decode_attention_io *io) {
@@ -638,21 +614,23 @@ int decode_attention_step(const decode_attention_config *cfg, const decode_atten
   a.max_past = io->max_past;
   a.grp = cfg->n_q_heads / cfg->n_kv_heads;
   a.M = a.grp * a.T;
+  a.RS = (a.M + 15) / 16;
   a.n_split = n_split_of(cfg);
   a.softmax_scale = cfg->softmax_scale;
-  // splits per (request, KV head): about one workgroup per CU in all (more
-  // workgroups each pay the partial hand-off and the combine again), at most
-  // n_split, each taking tps consecutive tiles of 256 positions
-  const int rg = a.R * a.Hkv;
+  // splits per (request, KV head, row split): about two workgroups per CU in
+  // all, and at least two tiles of 256 positions per workgroup where the
+  // context has them (every split pays the partial hand-off and adds a slot to
+  // the combine, which one CU reads), at most n_split, each taking tps
+  // consecutive tiles
+  const int rg = a.R * a.Hkv * a.RS;
   const int tiles = (io->max_past + a.T + kATile - 1) / kATile;
-  const int want = std::max(1, (cus_of_current_device() + rg - 1) / rg);
-  int split = std::min(std::min(tiles, a.n_split), want);
+  const int want = std::max(1, (2 * cus_of_current_device() + rg - 1) / rg);
+  int split = std::min(std::min(std::min(tiles, a.n_split), want), std::max(1, (tiles + 1) / 2));
   if (cfg->max_splits > 0) split = std::min(split, cfg->max_splits);
   a.tps = (tiles + split - 1) / split;
   split = (tiles + a.tps - 1) / a.tps;
   const dim3 grid(split, rg);
-  void (*kern)(AttnArgs) = a.M <= 16 ? (a.tps > 1 ? attn_step<1, true> : attn_step<1, false>)
-                                     : (a.tps > 1 ? attn_step<2, true> : attn_step<2, false>);
+  void (*kern)(AttnArgs) = a.tps > 1 ? attn_step<true> : attn_step<false>;
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return host::fail(nullptr, DL_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));

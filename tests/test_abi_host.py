@@ -224,7 +224,8 @@ def test_attention_workspace_and_validation():
     c = _attn_cfg()
     chunks = -(-4096 // 256)
     slots = 64 * 1 * chunks * (32 * 128 + 64) * 4
-    assert at.workspace_bytes(c) == _a256(slots) + _a256(64 * 4)
+    # 4 query heads x 8 tokens = 32 rows per KV head: two row splits of 16, each with its counter
+    assert at.workspace_bytes(c) == _a256(slots) + _a256(64 * 2 * 4)
     # at most 64 partial slots per request and KV head, whatever the cache length
     big = _attn_cfg(cache_len=1 << 20, max_requests=2)
     assert at.workspace_bytes(big) == _a256(2 * 64 * (32 * 128 + 64) * 4) + _a256(2 * 4)
