@@ -957,8 +957,11 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   stamp(a, 8);
   // gate/up items: routed (active slot, ffn row) pairs, then the shared
   // expert's rows f >= fs_b that phase B did not take, in that order.  An
-  // item costs 1, plus its token count when the hg rows of its tokens do not
-  // fit in LDS (its activations then travel with its weights); workgroup w
+  // item costs 3 (in thirds of a one-token item); when the hg rows of its
+  // tokens do not fit in LDS its activations come from the L2 with its
+  // weights, in load batches whose depth falls with the token count, and it
+  // costs 8 (3 or 4 tokens) or 10 (5 to 8), the times measured per item
+  // against a one-token item; workgroup w
   // takes the items whose cost prefix lies in [w C / G, (w + 1) C / G), a
   // contiguous run of about equal cost, mostly rows of one expert.  With 8 or
   // more items in its run a workgroup stages the hg rows of each expert's
@@ -973,7 +976,8 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     const int cap = (int)(sizeof(L.u) / (4 * (size_t)H));  // tokens whose hg rows fit in LDS
     // per-slot item cost and its exclusive prefix over the slots (n_active <= 64 lanes)
     const int ns = L.n_active;
-    const int cl = lane < ns ? 1 + (L.act_cnt[lane] > cap ? L.act_cnt[lane] : 0) : 0;
+    auto item_cost = [&](int cnt) { return cnt <= cap ? 3 : cnt <= 4 ? 8 : 10; };
+    const int cl = lane < ns ? item_cost(L.act_cnt[lane]) : 0;
     int incl = cl * a.F;
     for (int d = 1; d < kWave; d <<= 1) {
       const int v = __shfl_up(incl, d, kWave);
@@ -981,7 +985,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     }
     const int excl = incl - cl * a.F;
     const int c_rt = __shfl(incl, kWave - 1, kWave);
-    const int c_sh = 1 + (B > cap ? B : 0);
+    const int c_sh = item_cost(B);
     const long C = c_rt + (long)(a.Fs - fs_b) * c_sh;
     // the first item whose cost prefix is >= x
     auto first_item = [&](long x) -> int {
