@@ -275,8 +275,10 @@ __device__ __forceinline__ float unrank_bits(unsigned u) {
 }
 template <int CTRL, int ROWS>
 __device__ __forceinline__ unsigned dpp_umax(unsigned v) {
-  // rows outside ROWS (and lanes with no source) compare against themselves
-  const unsigned o = (unsigned)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xf, false);
+  // Rows outside ROWS read 0, the identity of the maximum, so they keep v.
+  // With 0 as the moved value's default the compiler folds the move into
+  // the maximum (one v_max_u32 with a DPP source per step).
+  const unsigned o = (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, ROWS == 0xf);
   return o > v ? o : v;
 }
 // Largest word over the wave; result uniform.
@@ -330,6 +332,67 @@ __device__ __forceinline__ void wave_topk(const float (&lv)[NC], int E, int K, i
   }
   my_idx = mine_idx;
   my_v = unrank_bits(mine_key);
+}
+
+// Top-k over one wave whose candidates are numbered in lane order: lane l
+// holds key[c] for candidate base + 64 c + l (keys from rank_bits, 0 for an
+// absent or taken candidate).  Lane j < K receives the key and the number of
+// the j-th pick, "larger key first, then smaller number".  Each round takes
+// the wave maximum g of the lanes' largest keys; the smallest number holding
+// g is the lowest lane of the first block c whose ballot of key[c] == g is
+// not empty, so equal keys need no second reduction.  Once every present key
+// is taken a round picks a key of 0 (never returned when K does not exceed
+// the number of present candidates).
+template <int NC>
+__device__ __forceinline__ void wave_topk_blocks(unsigned (&key)[NC], int base, int K, unsigned &pick_key,
+                                                 int &pick_idx) {
+  const int lane = threadIdx.x & 63;
+  pick_key = 0u;
+  pick_idx = 0;
+  for (int j = 0; j < K; ++j) {
+    unsigned m = key[0];
+#pragma unroll
+    for (int c = 1; c < NC; ++c) m = key[c] > m ? key[c] : m;
+    const unsigned g = wave_umax(m);
+    unsigned long long hold = 0;
+    int cs = 0;
+#pragma unroll
+    for (int c = NC - 1; c >= 0; --c) {
+      const unsigned long long b = __ballot(key[c] == g);
+      if (b) {
+        hold = b;
+        cs = c;
+      }
+    }
+    const int p = __ffsll((long long)hold) - 1;
+    if (lane == j) {
+      pick_key = g;
+      pick_idx = base + 64 * cs + p;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (c == cs && lane == p) key[c] = 0u;
+  }
+}
+
+// Merge of candidate lists over one wave: lane l holds key and number of
+// candidate l, where among equal keys a lower lane always has the smaller
+// number (for instance, the concatenated pick lists of wave_topk_blocks over
+// consecutive ranges).  Lane j < K receives the j-th pick in the same order.
+__device__ __forceinline__ void wave_topk_merge(unsigned key, int idx, int K, unsigned &pick_key, int &pick_idx) {
+  const int lane = threadIdx.x & 63;
+  pick_key = 0u;
+  pick_idx = 0;
+  for (int j = 0; j < K; ++j) {
+    const unsigned g = wave_umax(key);
+    const int p = __ffsll((long long)__ballot(key == g)) - 1;
+    const int id = __builtin_amdgcn_readlane(idx, p);
+    if (lane == j) {
+      pick_key = g;
+      pick_idx = id;
+    }
+    if (lane == p) key = 0u;
+  }
 }
 
 __device__ __forceinline__ float silu_mul(float u, float v) { return u / (1.0f + expf(-u)) * v; }

@@ -173,6 +173,11 @@ struct Lds {
   int pair_exp[kFusedMaxPairs];
   float pair_w[kFusedMaxPairs];
   int n_active;
+  // split top-k of one token: each wave's picks, and the waves that have
+  // written theirs
+  unsigned tk_key[kWave];
+  int tk_idx[kWave];
+  int tk_arrive;
   // gate/up sums of a round: [item][K half][W1 | W3][token]
   float uv[4][2][2][kFusedMaxB];
   // list building: per-wave partial counts of keys below / of the same expert
@@ -529,49 +534,60 @@ __device__ __forceinline__ void by_lpg(int F, Fn fn) {
 }  // namespace
 
 // ---- cross-layer prefetch ------------------------------------------------------
-// The dense weights that workgroup w of the next layer reads in its phases A-C
-// (the out-projection and shared down-projection rows of its slice, its unit
-// rows - router row or shared-expert row pair - and its input-projection
-// rows) are touched once per 64-byte sector by the stream threads, so that
-// they sit in this XCD's L2 (workgroup w of the next launch runs on the same
-// XCD) and in the memory-side cache when that layer starts.  The values are
-// folded into a word that is written only under a condition that never holds,
-// which keeps the loads without using them.
-// Threads [t0, kFT) touch the 64-byte sectors of [base, base + nbytes).
-__device__ __forceinline__ unsigned touch_range(const void *base, unsigned nbytes, int t0) {
-  const int tt = (int)threadIdx.x - t0, nt = kFT - t0;
-  const char *p = reinterpret_cast<const char *>(base);
-  const unsigned ns = (nbytes + 63u) >> 6;  // 64-byte sectors
-  unsigned acc = 0;
-  for (unsigned s0 = 0; s0 < ns; s0 += 4u * nt) {
-    unsigned v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned sct = min(s0 + tt + (unsigned)nt * j, ns - 1u);
-      v[j] = *reinterpret_cast<const unsigned *>(p + 64u * sct);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc ^= v[j];
-  }
-  return acc;
-}
-
-// The next layer's rows that its workgroup w reads before its first hand-off:
-// the out-projection rows of the slice and the two unit rows (router row, or
-// shared-expert row pair).  Touched by threads [t0, kFT).
+// The rows that workgroup w of the next layer reads before its first
+// hand-off - the out-projection rows of its slice and its two unit rows
+// (router row, or shared-expert row pair): up to five ranges - are touched
+// once per 64-byte sector, so that they sit in this XCD's L2 (workgroup w of
+// the next launch runs on the same XCD) and in the memory-side cache when
+// that layer starts.  The values are folded into a word that is written only
+// under a condition that never holds, which keeps the loads without using
+// them.  Threads [t0, kFT) take the sectors, numbered across the ranges in
+// turn; each issues up to kPfDepth loads before it waits, so that a few waves
+// cover them all in one memory round trip.
+constexpr int kPfDepth = 12;
 __device__ __forceinline__ unsigned prefetch_next(const FusedArgs &a, int w, int G, int i0, int ni, int t0) {
   const int E = a.E, H = a.H;
   const int fs_b = max(0, min(a.Fs, 2 * G - E));
-  unsigned acc = 0;
-  if (ni > 0) acc ^= touch_range(a.pf_w_o + (size_t)i0 * a.Do, (unsigned)ni * a.Do * 2u, t0);
+  const char *p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  unsigned n[5] = {0u, 0u, 0u, 0u, 0u};  // sectors per range
+  if (ni > 0) {
+    p[0] = reinterpret_cast<const char *>(a.pf_w_o + (size_t)i0 * a.Do);
+    n[0] = ((unsigned)ni * a.Do * 2u + 63u) >> 6;
+  }
+#pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int u = w + G * q;
     if (u < E) {
-      acc ^= touch_range(a.pf_w_router + (size_t)u * H, (unsigned)H * 4u, t0);
+      p[1 + 2 * q] = reinterpret_cast<const char *>(a.pf_w_router + (size_t)u * H);
+      n[1 + 2 * q] = ((unsigned)H * 4u + 63u) >> 6;
     } else if (u < E + fs_b) {
-      acc ^= touch_range(a.pf_s1 + (size_t)(u - E) * H, (unsigned)H * 2u, t0);
-      acc ^= touch_range(a.pf_s3 + (size_t)(u - E) * H, (unsigned)H * 2u, t0);
+      p[1 + 2 * q] = reinterpret_cast<const char *>(a.pf_s1 + (size_t)(u - E) * H);
+      p[2 + 2 * q] = reinterpret_cast<const char *>(a.pf_s3 + (size_t)(u - E) * H);
+      n[1 + 2 * q] = n[2 + 2 * q] = ((unsigned)H * 2u + 63u) >> 6;
     }
+  }
+  const unsigned total = n[0] + n[1] + n[2] + n[3] + n[4];
+  const int tt = (int)threadIdx.x - t0, nt = kFT - t0;
+  unsigned acc = 0;
+  for (unsigned s0 = 0; s0 < total; s0 += (unsigned)(kPfDepth * nt)) {
+    unsigned v[kPfDepth];
+#pragma unroll
+    for (int j = 0; j < kPfDepth; ++j) {
+      // sector s of the concatenated ranges (past the end: the last one)
+      unsigned s = min(s0 + tt + (unsigned)nt * j, total - 1u);
+      const char *b = p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (s < n[r]) {
+          b = p[r];
+          break;
+        }
+        s -= n[r];
+      }
+      v[j] = *reinterpret_cast<const unsigned *>(b + 64u * s);
+    }
+#pragma unroll
+    for (int j = 0; j < kPfDepth; ++j) acc ^= v[j];
   }
   return acc;
 }
@@ -618,6 +634,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   if (tid == 0) {
     L.bad = 0;
     L.arrive = 0;
+    L.tk_arrive = 0;
   }
   __syncthreads();
   const int i0 = w * a.slice;
@@ -843,30 +860,19 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     if (j < a.Dq)
       a.qkv[(size_t)t * a.Dq + j] = ((L.qkvp[0][r][t] + L.qkvp[1][r][t]) + L.qkvp[2][r][t]) + L.qkvp[3][r][t];
   }
-  // The waves the top-k leaves idle (waves B..7) touch the next layer's
-  // first rows meanwhile: no wave polls during the top-k, so HBM is idle.
-  if (a.pf_w_o && B < kFWaves && wv >= B) pf_acc = prefetch_next(a, w, G, i0, ni, B * kWave);
-  // top-k per token, one wave per token: lane l holds experts l, l+64, ...
-  for (int t = wv; t < B; t += kFWaves) {
-    int my_idx;
-    float my_l;
-    stamp(a, 14);
-    auto pick = [&](auto ncc) {  // as many candidates per lane as E needs
-      constexpr int NC = decltype(ncc)::value;
-      float lv[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int e = lane + 64 * c;
-        lv[c] = e < E ? L.u.logits[t * E + e] : 0.f;
-      }
-      wave_topk<NC>(lv, E, K, my_idx, my_l);
-    };
-    if (E <= 128) pick(std::integral_constant<int, 2>{});
-    else if (E <= 256) pick(std::integral_constant<int, 4>{});
-    else if (E <= 384) pick(std::integral_constant<int, 6>{});
-    else pick(std::integral_constant<int, kFusedMaxE / 64>{});
-    stamp(a, 15);
-    // scores of the k picks, renormalised (lane j holds pick j)
+  // One token: its candidates are spread over nwk waves, one per lane; each
+  // takes its k largest, and wave 0 merges those lists.  A round then costs a
+  // wave maximum and a ballot instead of a maximum over several candidates
+  // per lane and a search for the lowest index holding it.
+  const int nwk = (E + kWave - 1) / kWave;
+  const bool split_topk = B == 1 && nwk * K <= kWave;
+  const int busy = split_topk ? nwk : B;  // waves the top-k uses
+  // The waves the top-k leaves idle touch the next layer's first rows
+  // meanwhile: no wave polls during the top-k, so HBM is idle.
+  if (a.pf_w_o && busy < kFWaves && wv >= busy) pf_acc = prefetch_next(a, w, G, i0, ni, busy * kWave);
+  // scores of the k picks of token t, renormalised (lane j holds pick j),
+  // written out; with one token its lists as well
+  auto finish_token = [&](int t, int my_idx, float my_l) __attribute__((always_inline)) {
     const float wgt = pick_weights(my_l, K);
     if (lane < K) {
       L.sel[t * K + lane] = my_idx;
@@ -891,6 +897,56 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         L.act_off[rank] = rank;
       }
       if (lane == 0) L.n_active = K;
+    }
+  };
+  if (split_topk) {
+    if (wv < nwk) {
+      stamp(a, 14);
+      const int e = wv * kWave + lane;
+      unsigned key[1] = {e < E ? rank_bits(L.u.logits[e]) : 0u};
+      unsigned pk;
+      int pi;
+      wave_topk_blocks<1>(key, wv * kWave, K, pk, pi);
+      if (lane < K) {
+        L.tk_key[wv * K + lane] = pk;
+        L.tk_idx[wv * K + lane] = pi;
+      }
+      // wave 0 waits for the other lists only: a workgroup barrier would
+      // also wait for the prefetching waves
+      if (wv > 0) {
+        if (lane == 0) __hip_atomic_fetch_add(&L.tk_arrive, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        while (__hip_atomic_load(&L.tk_arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < nwk - 1) {
+        }
+        const unsigned mk = lane < nwk * K ? L.tk_key[lane] : 0u;
+        const int mi = lane < nwk * K ? L.tk_idx[lane] : 0;
+        wave_topk_merge(mk, mi, K, pk, pi);
+        stamp(a, 15);
+        finish_token(0, pi, unrank_bits(pk));
+      }
+    }
+  } else {
+    // one wave per token: lane l holds experts l, l+64, ...
+    for (int t = wv; t < B; t += kFWaves) {
+      int my_idx;
+      float my_l;
+      stamp(a, 14);
+      auto pick = [&](auto ncc) {  // as many candidates per lane as E needs
+        constexpr int NC = decltype(ncc)::value;
+        float lv[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int e = lane + 64 * c;
+          lv[c] = e < E ? L.u.logits[t * E + e] : 0.f;
+        }
+        wave_topk<NC>(lv, E, K, my_idx, my_l);
+      };
+      if (E <= 128) pick(std::integral_constant<int, 2>{});
+      else if (E <= 256) pick(std::integral_constant<int, 4>{});
+      else if (E <= 384) pick(std::integral_constant<int, 6>{});
+      else pick(std::integral_constant<int, kFusedMaxE / 64>{});
+      stamp(a, 15);
+      finish_token(t, my_idx, my_l);
     }
   }
   if (B > 1) {  // several tokens: counted in parallel by all waves

@@ -133,6 +133,41 @@ def test_exact_logit_ties(path):
     check(layer, got, f"ties_{used_name(obj, 1, path)}")
 
 
+@pytest.mark.parametrize("case", ["ties_over_waves", "all_equal", "k10", "k11"])
+def test_one_token_topk_over_waves(case):
+    """Batch 1, TP16 shard (384 experts) on the single launch, which spreads
+    the token's candidates one per lane over six waves and merges the six pick
+    lists on one wave.  Cases: eleven equal maximal logits in six 64-expert
+    ranges (the eight lowest ids win); all 384 logits equal (ids 0..7); k = 10,
+    the largest k whose six lists fit one wave; k = 11, one wave per token."""
+    import dataclasses
+    say(f"[one-token top-k over waves, TP16 shard batch 1, {case}] start")
+    if case in ("k10", "k11"):
+        layer = workload.build(1, h_source="stored", top_k=int(case[1:]))
+        got, obj = run_gpu(layer)
+        assert used_single(obj, 1, AUTO)
+        check(layer, got, f"one_token_{case}")
+        return
+    base = workload.build(1, h_source="stored")
+    k = base.shape.top_k
+    wr = base.w_router.copy()
+    if case == "ties_over_waves":
+        top = int(np.argmax(workload.expected(base)["logits"][0]))
+        group = [e for e in (1, 3, 64, 65, 70, 129, 190, 250, 300, 383) if e != top]
+        wr[group] = wr[top]
+        want = sorted(group + [top])[:k]
+    else:
+        wr[:] = wr[0]
+        want = list(range(k))
+    layer = dataclasses.replace(base, w_router=wr)
+    ref = workload.expected(layer)
+    assert ref["topk_idx"][0].tolist() == want
+    layer = dataclasses.replace(layer, targets=np.asarray(ref["topk_idx"], np.int32))
+    got, obj = run_gpu(layer)
+    assert used_single(obj, 1, AUTO)
+    check(layer, got, f"one_token_{case}")
+
+
 def test_batch_zero_is_noop():
     say("[batch 0] start")
     from decode_step_moe_amd import IO
