@@ -927,11 +927,14 @@ __device__ __forceinline__ void gu_chunk(GuUnit &s, int u, int NK) {
 // While a unit streams its weights, the next unit's activations are loaded
 // into registers and then written to the other LDS buffer, so staging does
 // not stall the weight stream.  VALU units are dealt round-robin after.
+__device__ void dn_plan_runs(const BatchArgs &a, int G_gu, int *s_pre, int *s_wsum);
+
 __global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
   __shared__ __align__(16) uint16_t lds[2][kGuLds / 2];
   __shared__ __align__(16) uint4 gws[kWavesPerBlock][256];  // each wave's weight pair rows (W1 | W3)
   __shared__ int tok_l[2][16];
-  __shared__ int s_flag;
+  __shared__ int s_flag, s_first;
+  __shared__ int s_wsum[kWavesPerBlock];
   const int tid = threadIdx.x;
   const int n_qm = a.n_q[0], n_qv = a.n_q[1];
   GuGeom q;
@@ -1029,6 +1032,18 @@ __global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
     }
     gateup_valu(a, it);
   }
+  // The first workgroup to finish lays out the down projection's runs (it
+  // has the other workgroups' remaining gate/up time to do so); the last
+  // re-arms the counter.
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.gu_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_first = prev == 0u;
+    if (prev == (unsigned)G - 1u) __hip_atomic_store(a.gu_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  // (the staging area is free once every wave has passed that barrier)
+  static_assert(sizeof(int) * (kMaxExperts + 2) <= sizeof(lds), "cost prefix fits the staging area");
+  if (s_first) dn_plan_runs(a, G, reinterpret_cast<int *>(&lds[0][0]), s_wsum);
 }
 
 // ================================================================ launch 5
@@ -1050,9 +1065,79 @@ __global__ void __launch_bounds__(kBlock, 2) gateup_b(BatchArgs a) {
 // the group's slot numbered by its place among the group's workgroups
 // (written through to the device coherence point) and counts itself; the
 // last to arrive adds the slots in slot order into moe_out.
+// The units laid end to end (group-major, entries in slot order, the shared
+// expert last) are cut into runs of equal cost: a unit costs 1 + its number
+// of 16-token chunks (its weights once, then one staged chunk of
+// activations each), so the shared expert's units at 64 tokens count 5 and
+// a hot expert's 2.  Unit u then belongs to workgroup floor(P(u) Ga / C),
+// with P(u) the cost of the units before it and C the total.  When no unit
+// costs more than C / Ga, consecutive units differ by at most one workgroup,
+// so every workgroup between the first and the last of a group holds some
+// of its units; otherwise every unit counts 1.  The run bounds are laid out
+// by the first gate/up workgroup to finish, so this launch only reads them.
 constexpr int kDnRows = 64;
 constexpr int kDnLd = 256 + 8;   // bf16 per LDS row of a staged chunk plane (F <= 256)
 constexpr int kDnLdF = 256 + 4;  // fp32 per LDS row of a staged VALU chunk
+
+// Run bounds of the down launch (grid min(G_gu, kDnMaxGrid)), by one
+// workgroup: the entries' costs and their exclusive prefix s_pre (a scan
+// over the workgroup), then for each run w the first unit u with
+// P(u) Ga >= w C: group T / S, entry = the smallest i with s_pre[i] >= T mod S
+// (T = ceil(w C / Ga), S a group's cost).
+__device__ void dn_plan_runs(const BatchArgs &a, int G_gu, int *s_pre, int *s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int B = a.B, n_act = *a.n_active;
+  const int ne = n_act + (a.Fs > 0 ? 1 : 0), ng = a.H / kDnRows;
+  const long U = (long)ng * ne;
+  const int Ga = (int)min((long)min(G_gu, kDnMaxGrid), U);
+  if (U == 0) return;
+  const bool by_cost = (long)(1 + (B + 15) / 16) * Ga <= U;
+  constexpr int EPT = (kMaxExperts + kBlock) / kBlock;
+  int cq[EPT], run = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j)  // every load issued (clamped address) before any is used
+    cq[j] = a.act_cnt[min(EPT * tid + j, max(n_act - 1, 0))];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int q = EPT * tid + j;
+    const int cnt = q < n_act ? cq[j] : B;
+    cq[j] = q >= ne ? 0 : !by_cost ? 1 : 1 + (cnt + 15) / 16;
+    run += cq[j];
+  }
+  int incl = run;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += t;
+  }
+  if (lane == kWave - 1) s_wsum[wv] = incl;
+  __syncthreads();
+  int before = incl - run;
+  for (int v = 0; v < wv; ++v) before += s_wsum[v];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int q = EPT * tid + j;
+    if (q <= ne) s_pre[q] = before;
+    before += cq[j];
+  }
+  __syncthreads();
+  const unsigned long long S = (unsigned)s_pre[ne], C = (unsigned long long)ng * S;
+  for (int w = tid; w <= Ga; w += kBlock) {
+    const unsigned long long T = ((unsigned long long)w * C + (unsigned long long)(Ga - 1)) / (unsigned long long)Ga;
+    const unsigned long long g = T / S, rem = T - g * S;
+    int lo = 0, hi = ne;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((unsigned long long)s_pre[mid] >= rem) hi = mid;
+      else lo = mid + 1;
+    }
+    a.dn_runs[2 + w] = (int)(g * (unsigned long long)ne) + lo;
+  }
+  if (tid == 0) {
+    a.dn_runs[0] = (int)S;
+    a.dn_runs[1] = s_pre[ne - 1];
+  }
+}
 
 __device__ __forceinline__ int dn_run(int w, int G) {
   const int half = G >> 1;
@@ -1199,6 +1284,10 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
   const int G = gridDim.x, ri = dn_run(blockIdx.x, G);
   const int Ga = (int)min((long)G, U);
   if (U == 0 || ri >= Ga) return;
+  // this run's units, a group's cost and its cost before its last entry
+  long u = a.dn_runs[2 + ri];
+  const long ue = a.dn_runs[3 + ri];
+  const unsigned long long S = (unsigned)a.dn_runs[0], P_last = (unsigned)a.dn_runs[1];
   for (int q = tid; q < n_act; q += kBlock) {
     s_exp[q] = a.act_exp[q];
     s_cnt[q] = a.act_cnt[q];
@@ -1206,6 +1295,13 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
   }
   for (int q = tid; q < kMaxBatch * kDnRows; q += kBlock) ytile[q] = 0.f;
   __syncthreads();
+  const unsigned long long C = (unsigned long long)ng * S;
+  const bool narrow = (C + 1ull) * (unsigned long long)Ga < (1ull << 32);
+  // workgroup holding unit cost prefix P: floor(P Ga / C)
+  auto run_of = [&](unsigned long long P) -> int {
+    const unsigned long long x = P * (unsigned long long)Ga;
+    return narrow ? (int)((unsigned)x / (unsigned)C) : (int)(x / C);
+  };
   auto rows_of = [&](long u, int &Fd) -> const uint16_t * {
     const int r = (int)(u / ne), i = (int)(u % ne);
     if (i < n_act) {
@@ -1215,8 +1311,6 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
     Fd = Fs;
     return a.s2 + (size_t)r * kDnRows * Fs;
   };
-  long u = (long)ri * U / Ga;
-  const long ue = (long)(ri + 1) * U / Ga;
   uint4 wc[8], wn[8], wm[8];
   {
     int Fd;
@@ -1264,8 +1358,7 @@ __global__ void __launch_bounds__(kBlock, 2) down_b(BatchArgs a) {
     for (int s = 0; s < 8; ++s) wc[s] = wn[s];
     if (u + 1 == ue || (u + 1) / ne != r) {
       // this workgroup is done with group r: its tile goes to its slot
-      const int first = (int)((((long)r * ne + 1) * Ga - 1) / U);
-      const int last = (int)((((long)r + 1) * ne * Ga - 1) / U);
+      const int first = run_of((unsigned long long)r * S), last = run_of((unsigned long long)r * S + P_last);
       const int slot = ri - first, nslots = last - first + 1;
       const int tile_f = kMaxBatch * kDnRows;
       float *slots = a.dn_part + (size_t)r * a.dn_slots * tile_f;

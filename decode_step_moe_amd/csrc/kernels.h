@@ -125,6 +125,8 @@ struct BatchArgs {
   float *dn_part;     // [H/64][dn_slots][64][64] partial y tiles of the down projection
   unsigned *dn_cnt;   // [H/64] arrivals of a row group's workgroups (re-armed by the last)
   int dn_slots;       // batch_dn_slots(H)
+  unsigned *gu_done;  // [1] gate/up workgroups finished (re-armed by the last)
+  int *dn_runs;       // [kDnMaxGrid + 3]: a group's unit cost, its cost before its last entry, first unit of each run
   unsigned *counter;  // [1] arrivals of the top-k workgroups (re-armed by the last)
   int B, H, Dq, Do, E, K, F, Fs;
   int qkv_split;      // K splits of the input projection: 8 when H % 1024 == 0, else 4

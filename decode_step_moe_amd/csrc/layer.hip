@@ -84,7 +84,7 @@ Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
   const size_t sizes[kNumBuf] = {
       // hand-off state
       (size_t)kFusedMaxGrid * kFusedMaxB * 8, (size_t)kFusedBig * 8, (size_t)kFusedBig * 8, (size_t)kFusedActS * 8,
-      4, 4, 4, 3 * 4, kMaxGuGroups * 4, kMaxDnGroups * 4,
+      4, 4, 4, 4 * 4, kMaxGuGroups * 4, kMaxDnGroups * 4,
       // step data
       B * H * 4, (size_t)nblk_o_of(c) * B * 4, B * 4, B * E * 4, B * K * 4, B * K * 4,
       E * 4, E * 4, E * 4, 4, B * K * (size_t)c.expert_ffn * 4, B * (size_t)(c.shared_ffn > 0 ? c.shared_ffn : 1) * 4,
@@ -92,7 +92,7 @@ Layout layout_of(const decode_layer_config &c, const SinglePlan &sp) {
       (size_t)kBatchQkvSplit * Bb * c.qkv_out * 4, (H / kBatchRtrK) * Bb * E * 4, Bb * H * 4, 2 * Bb * H * 2,
       Bb ? 4 * E * 4 : size_t(0), Bb ? size_t(8) : size_t(0),
       Bb ? (gu_groups_routed(c) + gu_groups_shared(c)) * batch_gu_chunks(c.hidden) * kGuSlotFloatsR * 4 : size_t(0),
-      Bb ? (H / 64) * batch_dn_slots(c.hidden) * kMaxBatch * 64 * 4 : size_t(0)};
+      Bb ? (H / 64) * batch_dn_slots(c.hidden) * kMaxBatch * 64 * 4 : size_t(0), Bb ? (kDnMaxGrid + 3) * 4 : size_t(0)};
   Layout L;
   size_t o = 0;
   for (int i = 0; i < kNumBuf; ++i) { L.off[i] = o; o += align256(sizes[i]); }
@@ -133,6 +133,7 @@ Scratch bind_scratch(char *b, const Layout &L) {
   s.n_q = (int *)(b + L.off[kBNQ]);
   s.gu_part = (float *)(b + L.off[kBGuPart]);
   s.dn_part = (float *)(b + L.off[kBDnPart]);
+  s.dn_runs = (int *)(b + L.off[kBDnRuns]);
   return s;
 }
 
@@ -400,6 +401,8 @@ int enqueue_step(const StepCtx &x, const decode_layer_io *io, hipStream_t st) {
     ba.dn_cnt = S.dn_cnt;
     ba.dn_slots = batch_dn_slots(c.hidden);
     ba.counter = S.counters + 2;
+    ba.gu_done = S.counters + 3;
+    ba.dn_runs = S.dn_runs;
     ba.B = B;
     ba.H = c.hidden;
     ba.Dq = c.qkv_out;

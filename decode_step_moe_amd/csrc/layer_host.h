@@ -29,7 +29,7 @@ struct Scratch {
   unsigned *epoch = nullptr;     // [1] tag of the last single-launch step
   unsigned *status = nullptr;    // [1]
   unsigned *wrap = nullptr;      // [1] arrivals at the tag-wrap grid barrier
-  unsigned *counters = nullptr;  // [3]: out-projection, router, batched top-k
+  unsigned *counters = nullptr;  // [4]: out-projection, router, batched top-k, batched gate/up finished
   unsigned *gu_cnt = nullptr;    // routed group counters, then shared group counters
   unsigned *dn_cnt = nullptr;    // [H/64]
   size_t tag_words = 0;          // 64-bit words from pss to the end of act_s64
@@ -55,6 +55,7 @@ struct Scratch {
   int *n_q = nullptr;            // [2]
   float *gu_part = nullptr;      // routed group slots, then shared group slots
   float *dn_part = nullptr;      // [H/64][dn slots][64][64] partial y tiles
+  int *dn_runs = nullptr;        // [kDnMaxGrid + 3] down-projection run bounds
 };
 
 // the most gate/up groups and down row groups any configuration in the envelope has
@@ -70,7 +71,7 @@ constexpr size_t kMaxDnGroups = 16384 / 64;
 enum Buf {
   kBPss, kBLogit64, kBAct64, kBActS64, kBEpoch, kBStatus, kBWrap, kBCounters, kBGuCnt, kBDnCnt,
   kBHg, kBSsPart, kBInvRms, kBLogits, kBPairTok, kBPairW, kBActExp, kBActCnt, kBActOff, kBNActive,
-  kBAct, kBActS, kBQkvPart, kBRlogPart, kBHn, kBHp, kBGuQ, kBNQ, kBGuPart, kBDnPart, kNumBuf
+  kBAct, kBActS, kBQkvPart, kBRlogPart, kBHn, kBHp, kBGuQ, kBNQ, kBGuPart, kBDnPart, kBDnRuns, kNumBuf
 };
 struct Layout {
   size_t off[kNumBuf];

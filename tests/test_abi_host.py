@@ -108,8 +108,8 @@ def test_handoff_region_is_configuration_independent():
 
 def test_batched_scratch_follows_the_path():
     """The batched path's arrays (qkv and router partial sums, h in fp32 and
-    as bf16 hi + lo planes, gate/up and down partial tiles) exist exactly when
-    some step can take that path."""
+    as bf16 hi + lo planes, gate/up and down partial tiles, the down
+    projection's run bounds) exist exactly when some step can take that path."""
     c = good()                       # TP16 shard shapes, max_batch 64
     B, H, Dq, E = 64, 7168, 512, 384
     F = Fs = 128
@@ -119,7 +119,8 @@ def test_batched_scratch_follows_the_path():
     batched = (_a256(8 * 4 * B * Dq) + _a256(4 * (H // 256) * B * E) + _a256(4 * B * H)
                + _a256(2 * 2 * B * H) + _a256(4 * 4 * E) + _a256(8)
                + _a256((groups_r + groups_s) * chunks * 2048 * 4)
-               + _a256((H // 64) * (-(-512 // (H // 64)) + 2) * 64 * 64 * 4))
+               + _a256((H // 64) * (-(-512 // (H // 64)) + 2) * 64 * 64 * 4)
+               + _a256((512 + 3) * 4))            # down-projection run bounds
     auto = dl.scratch_bytes(c, 256)
     c.path = dl.DL_PATH_MULTI
     multi = dl.scratch_bytes(c, 256)
