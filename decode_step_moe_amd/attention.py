@@ -21,7 +21,7 @@ class AttnConfig(ctypes.Structure):
 class AttnIO(ctypes.Structure):
     _fields_ = [("n_requests", ctypes.c_int32), ("n_tokens", ctypes.c_int32), ("max_past", ctypes.c_int32)] + \
                [(n, ctypes.c_void_p) for n in ("past_len", "q", "k_new", "v_new", "k_cache", "v_cache",
-                                               "k_scale", "v_scale", "out", "workspace")]
+                                               "k_scale", "v_scale", "out", "workspace", "out_bf16")]
 
 
 _done = False
@@ -56,7 +56,9 @@ def check(cfg: AttnConfig, io: AttnIO) -> int:
 
 
 def make_io(cfg: AttnConfig, past_len, max_past, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, out,
-            workspace) -> AttnIO:
+            workspace, out_bf16=None) -> AttnIO:
+    """out_bf16 (optional): bf16 [R][T][Hq][D], the output rounded to bf16 in
+    the decode layer step's attn layout [R*T][Hq*D]."""
     import torch
     R, T = q.shape[0], q.shape[1]
     Hq, Hkv, D, C = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.cache_len
@@ -68,7 +70,8 @@ def make_io(cfg: AttnConfig, past_len, max_past, q, k_new, v_new, k_cache, v_cac
                   _ptr(v_cache, u8, (cfg.max_requests, Hkv, C, D), "v_cache"),
                   _ptr(k_scale, f32, (Hkv,), "k_scale"), _ptr(v_scale, f32, (Hkv,), "v_scale"),
                   _ptr(out, f32, (R, T, Hq, D), "out"),
-                  _ptr(workspace, u8, (workspace_bytes(cfg),), "workspace"))
+                  _ptr(workspace, u8, (workspace_bytes(cfg),), "workspace"),
+                  None if out_bf16 is None else _ptr(out_bf16, bf, (R, T, Hq, D), "out_bf16"))
 
 
 def step_io(cfg: AttnConfig, io: AttnIO, stream=None):

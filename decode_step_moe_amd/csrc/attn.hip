@@ -65,6 +65,7 @@ struct AttnArgs {
   uint8_t *k_cache, *v_cache;
   const float *k_scale, *v_scale;
   float *out;
+  uint16_t *out_bf16;  // optional: out rounded to bf16, same element order
   float *slots;        // [max_requests * Hkv][n_split][kASlot]
   unsigned *counters;  // [max_requests * Hkv * row splits]
   int R, T, Hq, Hkv, C, max_past, grp, M, RS, tps, n_split;
@@ -173,6 +174,24 @@ __device__ __forceinline__ int slice_key(int q, int g4, int jj) { return 32 * q 
 // goes to the output directly when it is the request's only one, else to its
 // slot, and the last workgroup of the (request, KV head, row split) to arrive
 // combines the slots.
+// fp32 to bf16, rounded to nearest even (a NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const unsigned u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Four consecutive outputs at element index i (a multiple of 4), and their
+// bf16 copy when asked for.
+__device__ __forceinline__ void put_out4(const AttnArgs &a, size_t i, float4 v) {
+  *reinterpret_cast<float4 *>(a.out + i) = v;
+  if (a.out_bf16) {
+    const unsigned lo = bf16_rne(v.x) | ((unsigned)bf16_rne(v.y) << 16);
+    const unsigned hi = bf16_rne(v.z) | ((unsigned)bf16_rne(v.w) << 16);
+    *reinterpret_cast<uint2 *>(a.out_bf16 + i) = make_uint2(lo, hi);
+  }
+}
+
 template <bool PF>
 __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
   __shared__ __align__(16) uint8_t lds[kALds];         // V^T slices; later the wave merge and combine weights
@@ -188,7 +207,11 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
     if (s == 0)
       for (int q = tid; q < 16 * kAD; q += 256) {
         const int row = row0 + q / kAD, d = q % kAD, j = row / grp, h = g * grp + row % grp;
-        if (row < M) a.out[((size_t)(r * T + j) * a.Hq + h) * kAD + d] = __builtin_nanf("");
+        if (row < M) {
+          const size_t i = ((size_t)(r * T + j) * a.Hq + h) * kAD + d;
+          a.out[i] = __builtin_nanf("");
+          if (a.out_bf16) a.out_bf16[i] = 0x7fc0u;
+        }
       }
     return;
   }
@@ -412,8 +435,8 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
       const float f = vsc / lsum;
 #pragma unroll
       for (int k = 0; k < 2; ++k)
-        *reinterpret_cast<float4 *>(a.out + ((size_t)(r * T + gj) * a.Hq + gh) * kAD + 4 * ((tid >> 4) + 16 * k)) =
-            make_float4(o2[k][0] * f, o2[k][1] * f, o2[k][2] * f, o2[k][3] * f);
+        put_out4(a, ((size_t)(r * T + gj) * a.Hq + gh) * kAD + 4 * ((tid >> 4) + 16 * k),
+                 make_float4(o2[k][0] * f, o2[k][1] * f, o2[k][2] * f, o2[k][3] * f));
     }
     return;
   }
@@ -490,8 +513,8 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      *reinterpret_cast<float4 *>(a.out + ((size_t)(r * T + gj) * a.Hq + gh) * kAD + 4 * ((tid >> 4) + 16 * k)) =
-          make_float4(o[k][0], o[k][1], o[k][2], o[k][3]);
+      put_out4(a, ((size_t)(r * T + gj) * a.Hq + gh) * kAD + 4 * ((tid >> 4) + 16 * k),
+               make_float4(o[k][0], o[k][1], o[k][2], o[k][3]));
   }
 }
 
@@ -546,6 +569,8 @@ int check_io(const decode_attention_config *c, const decode_attention_io *io) {
   }
   if (reinterpret_cast<uintptr_t>(io->workspace) & 255u)
     return fail(nullptr, DL_ERR_INVALID_ARG, "attention io.workspace is not 256-byte aligned");
+  if (io->out_bf16 && (reinterpret_cast<uintptr_t>(io->out_bf16) & 7u))
+    return fail(nullptr, DL_ERR_INVALID_ARG, "attention io.out_bf16 is not 8-byte aligned");
   return DL_OK;
 }
 
@@ -604,6 +629,7 @@ int decode_attention_step(const decode_attention_config *cfg, const decode_atten
   a.k_scale = io->k_scale;
   a.v_scale = io->v_scale;
   a.out = io->out;
+  a.out_bf16 = (uint16_t *)io->out_bf16;
   a.slots = (float *)io->workspace;
   a.counters = (unsigned *)((char *)io->workspace + align256(slot_bytes(cfg)));
   a.R = io->n_requests;

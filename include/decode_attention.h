@@ -78,6 +78,9 @@ typedef struct {
   float *out;                /* fp32 [R][T][Hq][D] */
   void *workspace;           /* decode_attention_workspace_bytes(cfg) bytes, 256-byte aligned, zeroed
                                 once before first use (the kernels leave it as they found it) */
+  void *out_bf16;            /* optional (NULL: not written): bf16 [R][T][Hq][D], each element out
+                                rounded to nearest even - laid out as the decode layer step's attn
+                                input [R*T][Hq*D] (token r*T + j), so a step can take it as is */
 } decode_attention_io;
 
 /* Bytes of workspace a call site with this configuration needs (0 if invalid).

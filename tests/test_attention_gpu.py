@@ -42,7 +42,8 @@ def _at():
 class Dev:
     """One step's device buffers (outputs poisoned with NaN) and its workspace."""
 
-    def __init__(self, st: attn_gen.AttnStep, max_tokens=None, max_requests=None, max_past=None, max_splits=0):
+    def __init__(self, st: attn_gen.AttnStep, max_tokens=None, max_requests=None, max_past=None, max_splits=0,
+                 with_bf16=False):
         at = _at()
         R, T, Hq, Hkv, D, C = st.shape
         self.cfg = at.make_attn_config(Hq, Hkv, max_tokens or T, max_requests or R, C, st.softmax_scale,
@@ -58,10 +59,11 @@ class Dev:
         self.k_scale, self.v_scale = f32_tensor(st.k_scale, d), f32_tensor(st.v_scale, d)
         self.past = torch.from_numpy(np.ascontiguousarray(st.past_len, np.int32)).to(d)
         self.out = torch.full((R, T, Hq, D), float("nan"), device=d)
+        self.out_bf16 = torch.full((R, T, Hq, D), float("nan"), dtype=torch.bfloat16, device=d) if with_bf16 else None
         self.ws = torch.zeros(at.workspace_bytes(self.cfg), dtype=torch.uint8, device=d)
         mp = int(st.past_len.max()) if max_past is None else max_past
         self.io = at.make_io(self.cfg, self.past, mp, self.q, self.k_new, self.v_new, self.k_cache,
-                             self.v_cache, self.k_scale, self.v_scale, self.out, self.ws)
+                             self.v_cache, self.k_scale, self.v_scale, self.out, self.ws, self.out_bf16)
 
     def step(self):
         _at().step_io(self.cfg, self.io)
@@ -282,3 +284,47 @@ def test_zero_requests_is_a_noop():
     assert np.isnan(out).all()
     np.testing.assert_array_equal(kc, st.k_cache)
     assert at.check(dev.cfg, dev.io) == 0
+
+
+def test_bf16_output_feeds_the_layer_step():
+    """One decode step of a TP16 shard, attention into the MoE layer on the GPU:
+    8 requests x 1 token (4 query heads on 1 KV head of 128, FP8 cache,
+    contexts 100..4095, so some requests run in one workgroup and others are
+    split and combined) write their output also as bf16, laid out as the
+    layer step's attn input [8][512]; the layer step (batch 8) then reads
+    that buffer as it is.  Checks: the bf16 output is the nearest-even
+    rounding of the fp32 output (torch's CPU conversion), bit for bit; the
+    fp32 output is within the attention gates of the attention oracle; the
+    layer's outputs are within the layer gates of the layer oracle run on
+    the same attn input."""
+    import dataclasses  # noqa: F401
+    from decode_step_moe_amd import DecodeLayer
+    from synth import device as sdev, gen, routing
+    from tests import parity, workload
+    say("[attention -> layer step, TP16 shard, 8 requests x 1 token] start")
+    st = attn_gen.draw(8, 1, 4, 1, 4096, 100, 4095, seed=91)
+    dev = Dev(st, with_bf16=True)
+    dev.step()
+    out, _, _ = dev.results()
+    check_out("attn_to_layer", out, expect(st)[0])
+    ob = dev.out_bf16.cpu()
+    want_bits = torch.from_numpy(out).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(ob.view(torch.int16).numpy(), want_bits), "bf16 output is not out rounded to nearest even"
+    # the layer step on that buffer (no copy: the attention's own output tensor)
+    raw = gen.draw(2)
+    assert raw.attn.shape == (8, 512)
+    raw.attn = ob.view(torch.int16).numpy().view(np.uint16).reshape(8, 512)
+    layer = routing.shape_router(raw, workload.oracle_h(raw))
+    h = DecodeLayer(sdev.config_of(layer), sdev.upload_weights(layer))
+    x, _, resid = sdev.upload_inputs(layer)
+    res = h.alloc_outputs(8, with_h=True)
+    h.step(x, dev.out_bf16.view(8, 512), resid, res)
+    torch.cuda.synchronize()
+    assert h.status() == 0
+    got = {"qkv": res.qkv.cpu().numpy(), "resid_out": res.resid_out.cpu().numpy(),
+           "logits": res.router_logits.cpu().numpy(), "topk_idx": res.topk_idx.cpu().numpy(),
+           "topk_w": res.topk_w.cpu().numpy(), "moe_out": res.moe_out.cpu().numpy(),
+           "h": res.h_out.cpu().numpy()}
+    m = parity.compare(got, workload.expected(layer))
+    say("[attention -> layer step] " + ", ".join(f"{k}={v:.3e}" for k, v in m.items() if k != "fails"))
+    assert not m["fails"], m["fails"]
