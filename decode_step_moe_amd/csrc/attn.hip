@@ -466,45 +466,67 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
   if (!s_last) return;
 
   // ---- the last workgroup of (request, KV head, row split): combine the nact
-  // partials in slot order.  Phase A: every slot's max and sum -> per-row
-  // weights exp2(m_c - max) * v_scale / total; phase B: outputs = sum_c
-  // weight * O_c, 16 slots' loads in flight per thread at a time.
-  const int mrows = min(16, M - row0);
+  // partials in slot order: per-row weights exp2(m_c - max) * v_scale / total
+  // from every slot's max and sum, then outputs = sum_c weight_c * O_c.
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       a.slots + (size_t)rgs * a.n_split * kASlot, 0, a.n_split * kASlot * 4, 0x00020000);
-  float *wm = reinterpret_cast<float *>(lds), *wl = wm + kAMaxSplit * 16;
-  for (int qi = tid; qi < nact * 16; qi += 256) {
-    const int c = qi >> 4, row = qi & 15, base = c * kASlot + 16 * kAD + row;
-    wm[qi] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, base * 4, 0, kCoherent));
-    wl[qi] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, (base + 16) * 4, 0, kCoherent));
-  }
-  __syncthreads();
-  if (tid < mrows) {
-    float mx = kNegInf;
-    for (int c = 0; c < nact; ++c) mx = fmaxf(mx, wm[c * 16 + tid]);
-    float tot = 0.f;
-    for (int c = 0; c < nact; ++c) {
-      const float f = __builtin_amdgcn_exp2f(wm[c * 16 + tid] - mx);   // 0 for a slot at -inf
-      wm[c * 16 + tid] = f;
-      tot += f * wl[c * 16 + tid];
+  float *wm = reinterpret_cast<float *>(lds);
+  // one round trip: as (row ar, lane aj) = (tid / 16, tid % 16) every thread
+  // requests the maxima and sums of slots aj, aj + 16, ..., then its outputs'
+  // words of the first 16 slots (clamped slots, used only when real; a thread
+  // of a row past the step's rows gets an offset past the buffer's end, which
+  // loads zero without a memory access); the weights are reduced over the 16
+  // lanes of a row while the output words are in flight
+  f32x4a v[2][16];
+  const int obase = grow < M ? (lrow * kAD + 4 * (tid >> 4)) * 4 : 0x40000000;   // bytes; past the end for no row
+  auto load_o = [&](int c0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = min(c0 + cc, nact - 1);
+        v[k][cc] = __builtin_bit_cast(f32x4a, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rsb, obase + (c * kASlot + 64 * k) * 4, 0, kCoherent));
+      }
+  };
+  {
+    constexpr int kPer = kAMaxSplit / 16;
+    const int ar = tid >> 4, aj = tid & 15;
+    float mc[kPer], lc[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int base = min(aj + 16 * i, nact - 1) * kASlot + 16 * kAD + ar;
+      mc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, base * 4, 0, kCoherent));
+      lc[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, (base + 16) * 4, 0, kCoherent));
     }
+    // the output words after them: the weights need only the maxima and sums
+    __builtin_amdgcn_sched_barrier(0);
+    load_o(0);
+    __builtin_amdgcn_sched_barrier(0);
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (aj + 16 * i < nact) mx = fmaxf(mx, mc[i]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float f[kPer], tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      f[i] = aj + 16 * i < nact ? __builtin_amdgcn_exp2f(mc[i] - mx) : 0.f;   // 0 for a slot at -inf
+      tot += f[i] * lc[i];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) tot += __shfl_xor(tot, o);
     const float scl = vsc / tot;
-    for (int c = 0; c < nact; ++c) wm[c * 16 + tid] *= scl;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (aj + 16 * i < nact) wm[(aj + 16 * i) * 16 + ar] = f[i] * scl;
   }
   __syncthreads();
   if (grow < M) {
     f32x4a o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     for (int c0 = 0; c0 < nact; c0 += 16) {
-      f32x4a v[2][16];
-#pragma unroll
-      for (int cc = 0; cc < 16; ++cc)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int c = min(c0 + cc, nact - 1);
-          v[k][cc] = __builtin_bit_cast(f32x4a, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rsb, (c * kASlot + lrow * kAD + 4 * ((tid >> 4) + 16 * k)) * 4, 0,
-                                                    kCoherent));
-        }
+      if (c0 > 0) load_o(c0);
 #pragma unroll
       for (int cc = 0; cc < 16; ++cc)
         if (c0 + cc < nact)
