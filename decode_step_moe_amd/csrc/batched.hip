@@ -482,6 +482,8 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
   __shared__ int s_pe[kMaxBatch * kMaxTopK];   // the last workgroup: every pick's expert
   __shared__ float s_pw[kMaxBatch * kMaxTopK]; // and weight
   __shared__ int last_flag;
+  __shared__ unsigned s_tk_key[kWave];  // split top-k: each wave's picks
+  __shared__ int s_tk_idx[kWave];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int B = a.B, H = a.H, E = a.E, K = a.K, t = blockIdx.x;
   // every load of the token's hg row is requested together with the norm's
@@ -569,7 +571,37 @@ __global__ void __launch_bounds__(kBlock) topk_b(BatchArgs a, int n_ow, int n_rk
     if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
   }
   __syncthreads();
-  if (wv == 0) {  // lane holds experts lane, lane + 64, ... (as many as E needs)
+  // The token's candidates over nwk waves, two 64-expert blocks each: every
+  // wave takes its k largest (the lowest lane of the first block holding the
+  // maximum has the lowest id, so equal logits cost nothing), then wave 0
+  // merges the lists, concatenated in expert-id order, in k more rounds.
+  const int nwk = (E + 2 * kWave - 1) / (2 * kWave);
+  if (nwk <= kWavesPerBlock && nwk * K <= kWave) {
+    unsigned pk;
+    int pi;
+    if (wv < nwk) {
+      unsigned key[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int e = 2 * kWave * wv + kWave * c + lane;
+        key[c] = e < E ? rank_bits(lg[e]) : 0u;
+      }
+      wave_topk_blocks<2>(key, 2 * kWave * wv, K, pk, pi);
+      if (lane < K) {
+        s_tk_key[wv * K + lane] = pk;
+        s_tk_idx[wv * K + lane] = pi;
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+      wave_topk_merge(lane < nwk * K ? s_tk_key[lane] : 0u, lane < nwk * K ? s_tk_idx[lane] : 0, K, pk, pi);
+      const float wgt = pick_weights(unrank_bits(pk), K);
+      if (lane < K) {  // written through: the last workgroup reads them back
+        __hip_atomic_store(a.topk_idx + (size_t)t * K + lane, pi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.topk_w + (size_t)t * K + lane, wgt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  } else if (wv == 0) {  // lane holds experts lane, lane + 64, ... (as many as E needs)
     int my_idx;
     float my_l;
     auto pick = [&](auto ncc) {
