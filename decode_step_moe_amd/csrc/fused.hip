@@ -871,15 +871,18 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
   // meanwhile: no wave polls during the top-k, so HBM is idle.
   if (a.pf_w_o && busy < kFWaves && wv >= busy) pf_acc = prefetch_next(a, w, G, i0, ni, busy * kWave);
   // scores of the k picks of token t, renormalised (lane j holds pick j),
-  // written out; with one token its lists as well
+  // written out; with one token its lists as well.  With the split top-k
+  // the weights are deferred: selw keeps the picks' logits, and a control
+  // wave turns them into weights in phase D, while it waits for the
+  // activations (only phase D reads them), so gate/up starts earlier.
   auto finish_token = [&](int t, int my_idx, float my_l) __attribute__((always_inline)) {
-    const float wgt = pick_weights(my_l, K);
+    const float wgt = split_topk ? my_l : pick_weights(my_l, K);
     if (lane < K) {
       L.sel[t * K + lane] = my_idx;
       L.selw[t * K + lane] = wgt;
       if (w == 0) {
         a.topk_idx[(size_t)t * K + lane] = poison_c ? -1 : my_idx;
-        a.topk_w[(size_t)t * K + lane] = poison_c ? kNaN : wgt;
+        if (!split_topk) a.topk_w[(size_t)t * K + lane] = poison_c ? kNaN : wgt;
       }
     }
     if (B == 1) {
@@ -1159,6 +1162,13 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       if (!ctl) {
         d.stage();   // the first down-projection rows (static weights) -> LDS
       } else {
+        if (split_topk && wv == 0) {  // the one token's deferred pick weights
+          const float wgt = pick_weights(lane < K ? L.selw[lane] : 0.f, K);
+          if (lane < K) {
+            L.pair_w[L.pos[lane]] = wgt;
+            if (w == 0) a.topk_w[lane] = poison_c ? kNaN : wgt;
+          }
+        }
         // every SwiGLU activation -> LDS
         gather_tagged(a.act, L.u.d.act, tid, kCtl, P * a.F, tag, a.spin_limit, &L.bad);
         gather_tagged(a.act_s, L.u.d.act_s, tid, kCtl, B * a.Fs, tag, a.spin_limit, &L.bad);
