@@ -123,8 +123,12 @@ def draw(cfg: int, seed: int | None = None, batch: int | None = None,
         rt = s.routing if routing is None else routing
         s = LayerShape(s.name + f"_b{b}_k{k}_fs{fs}_{rt}", s.hidden, b, s.qkv_out, s.attn_dim,
                        s.n_experts, k, s.expert_ffn, fs, rt)
-    if seed is None:
-        seed = cfg
+    return draw_shape(s, cfg if seed is None else seed)
+
+
+def draw_shape(s: LayerShape, seed: int) -> RawLayer:
+    """Draw every tensor of a layer of shape `s` from `seed` (any shape in the
+    library's envelope, e.g. the seeded random shapes of the sweep tests)."""
     H, B = s.hidden, s.batch
     ga = rng(seed, S_ACT)
     # 64 rows are always drawn, so a smaller batch is a prefix of a larger one
