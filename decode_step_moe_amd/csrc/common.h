@@ -36,6 +36,13 @@ __device__ __forceinline__ float4 ld_stream16f(const void *p) {
 }
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ float4 ld16f(const void *p) { return *reinterpret_cast<const float4 *>(p); }
+// Four floats at float index i of buffer r, read at device scope (past the
+// CU's and the XCD's caches): a value another XCD wrote through is seen even
+// where this XCD still holds an earlier copy of the line.
+__device__ __forceinline__ float4 ld16f_dev(__amdgpu_buffer_rsrc_t r, int i) {
+  const v4f v = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, i * 4, 0, 16));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 // ---- wave reductions -------------------------------------------------------
 // DPP lane permutes inside rows of 16 lanes, then readlane across the 4 rows:

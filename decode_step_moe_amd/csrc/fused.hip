@@ -753,9 +753,12 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     s = wave_sum(s);
     if (lane == 0) L.inv_rms[wv] = 1.0f / sqrtf(s / (float)H + a.eps);
   }
-  // every workgroup's hg is now announced: acquire before reading it (drops
-  // any line of an earlier step's hg from this XCD's caches)
-  if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // every workgroup's hg is now announced.  With several tokens, acquire
+  // before reading it through the caches (drops any line of an earlier
+  // step's hg from this XCD's caches).  With one token every read of hg is
+  // at device scope instead (phase B here, the copy staged in LDS in phase
+  // C), which spares the acquire's cache invalidation on the critical path.
+  if (B > 1 && tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   stamp(a, 4);
   // After a wait of this workgroup has expired, every value it publishes and
@@ -776,14 +779,24 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     constexpr int TG = decltype(tgc)::value;
     for (int t0 = 0; t0 < B; t0 += TG) {
       float4 hx[TG][kChunkJ][2];
-#pragma unroll
-      for (int tt = 0; tt < TG; ++tt) {
-        const float *hrow = a.hg + (size_t)min(t0 + tt, B - 1) * H;
+      if constexpr (TG == 1) {  // one token: device scope, no acquire before
+        const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc((void *)a.hg, 0, H * 4, 0x00020000);
 #pragma unroll
         for (int j = 0; j < kChunkJ; ++j) {
           const int c = min(tid + kFT * j, nc - 1);
-          hx[tt][j][0] = ld16f(hrow + 8 * c);
-          hx[tt][j][1] = ld16f(hrow + 8 * c + 4);
+          hx[0][j][0] = ld16f_dev(hr, 8 * c);
+          hx[0][j][1] = ld16f_dev(hr, 8 * c + 4);
+        }
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < TG; ++tt) {
+          const float *hrow = a.hg + (size_t)min(t0 + tt, B - 1) * H;
+#pragma unroll
+          for (int j = 0; j < kChunkJ; ++j) {
+            const int c = min(tid + kFT * j, nc - 1);
+            hx[tt][j][0] = ld16f(hrow + 8 * c);
+            hx[tt][j][1] = ld16f(hrow + 8 * c + 4);
+          }
         }
       }
       DL_SCHED_FENCE();
@@ -850,8 +863,25 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
 
   // ================= phase C =================
   unsigned pf_acc = 0;
-  if (ctl) gather_tagged(a.logit, L.u.logits, tid, kCtl, B * E, tag, a.spin_limit, &L.bad);
-  else by_tokens(B, [&](auto nt) { qkv_rows<decltype(nt)::value>(a, L, w, G); });
+  if (ctl) {
+    gather_tagged(a.logit, L.u.logits, tid, kCtl, B * E, tag, a.spin_limit, &L.bad);
+  } else {
+    by_tokens(B, [&](auto nt) { qkv_rows<decltype(nt)::value>(a, L, w, G); });
+    // one token: its hg row, at device scope, into the down-projection
+    // staging area (free until phase D), where every gate/up item reads it
+    if (B == 1) {
+      static_assert(sizeof(float) * kFusedMaxH <= sizeof(L.w2), "one hg row fits the staging area");
+      const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc((void *)a.hg, 0, H * 4, 0x00020000);
+      constexpr int PT = kFusedMaxH / 4 / kStr;  // 16-byte words per stream thread (at most)
+      const int nw = H >> 2, st = tid - kCtl;
+      float4 v[PT];
+#pragma unroll
+      for (int j = 0; j < PT; ++j) v[j] = ld16f_dev(hr, 4 * min(st + kStr * j, nw - 1));
+#pragma unroll
+      for (int j = 0; j < PT; ++j)
+        if (st + kStr * j < nw) reinterpret_cast<float4 *>(L.w2)[st + kStr * j] = v[j];
+    }
+  }
   __syncthreads();
   stamp(a, 7);
   const bool poison_c = L.bad != 0;
@@ -1055,8 +1085,10 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       return sl * a.F + (int)((x - es + cs - 1) / cs);
     };
     const int kb = first_item((long)w * C / G), ke = first_item((long)(w + 1) * C / G);
-    const bool stage = ke - kb >= 8;
-    float *hl = reinterpret_cast<float *>(&L.u);
+    // one token: its hg row is already in LDS (phase C) and every item reads it there
+    const bool pre = B == 1;
+    const bool stage = !pre && ke - kb >= 8;
+    float *hl = pre ? reinterpret_cast<float *>(L.w2) : reinterpret_cast<float *>(&L.u);
     int staged = -2;  // token set in LDS: active slot, or -1 for the shared expert
     auto set_of = [&](int it) { return it < n_rt ? it / a.F : -1; };
     for (int k0 = kb; k0 < ke;) {
@@ -1069,8 +1101,8 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
             break;
           }
       const int cnt0 = sk0 >= 0 ? L.act_cnt[sk0] : B;
-      const bool lds = stage && cnt0 <= cap;  // this round's activations come from LDS
-      if (lds && staged != sk0) {
+      const bool lds = pre || (stage && cnt0 <= cap);  // this round's activations come from LDS
+      if (lds && !pre && staged != sk0) {
         GuRow r0;
         r0.toks = sk0 >= 0 ? L.pair_tok + L.act_off[sk0] : nullptr;
         r0.cnt = cnt0;
