@@ -60,9 +60,11 @@
 // exactly for the data it needs, with one memory round trip and no counter
 // that every workgroup would have to serialise on.  The tag is the handle's
 // step counter + 1, kept in device memory and advanced by workgroup 0 at the
-// end of each step, so it is also right under HIP-graph replay.  hg and the
-// outputs are ordinary stores; hg is released (agent-scope fence) before the
-// phase-A hand-off values and acquired after them.  Only static weights are
+// end of each step, so it is also right under HIP-graph replay.  hg is
+// written with device-scope stores that have completed before the phase-A
+// hand-off values are published; after that hand-off a step of several tokens
+// acquires (agent-scope fence) and reads hg through the caches, and a step of
+// one token reads it at device scope.  Only static weights are
 // read before a wait (the ordering rule of wireai.ir, "Oversight and
 // validation for AI-generated kernels").  Every wait is bounded: on expiry the
 // kernel records an error in the handle's status word and runs to completion.
