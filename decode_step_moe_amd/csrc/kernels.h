@@ -19,7 +19,7 @@ constexpr int kDownRows = 16;
 constexpr int kTokChunk = 8;
 // Router tail limits (LDS sizing).
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxTopK = 32;
+constexpr int kMaxTopK = 64;
 constexpr int kMaxBatch = 64;
 
 // Single-launch path (fused.hip): one 512-thread workgroup per CU, all

@@ -63,15 +63,14 @@ enum {
  *   qkv_out Dq    : 1..65536
  *   attn_dim Do   : 8..16384, multiple of 8
  *   n_experts E   : 1..1024
- *   top_k k       : 1..min(E, 32)
+ *   top_k k       : 1..min(E, 64) (each pick of a token is one lane of a
+ *                   wave-wide top-k)
  *   expert_ffn F  : 32, 64, 128 or 256
  *   shared_ffn Fs : 0 (no shared expert) or 32, 64, 128 or 256
- *     (k and F are narrower than a generic MoE layer would need: the kernels
- *     give each of the k picks of a token one lane of a wave-wide top-k and
- *     size their per-token pick lists for 32, and they map an expert's ffn
- *     row onto F/8 lanes of 16-byte loads, specialised for these four widths;
- *     the shapes this library is measured on use k = 2 or 8 and F = 128 or
- *     256.  Other values return DL_ERR_UNSUPPORTED, the pages' fallback case.)
+ *     (F is narrower than a generic MoE layer would need: the kernels map an
+ *     expert's ffn row onto F/8 lanes of 16-byte loads, specialised for these
+ *     four widths; the shapes this library is measured on use F = 128 or 256.
+ *     Other values return DL_ERR_UNSUPPORTED, the pages' fallback case.)
  *   max_batch     : 1..64
  *   rms_eps       : > 0 and finite
  *   score_fn      : 0 = sigmoid (the only value supported)

@@ -4,7 +4,7 @@ parity tests (test infrastructure).
 Each shape draws every size of the layer: hidden and attention widths (three
 fifths of them meeting the batched path's tilings, the rest only the general multiple of
 8), any qkv width, expert counts from 1 to 1024 with their edge values
-favoured, top-k up to min(E, 32) (mostly up to 8), every routed and shared
+favoured, top-k up to min(E, 64) (mostly up to 8), every routed and shared
 ffn width (shared expert on or off), batches 1-64 with single-launch batches favoured, and a
 routing mode.  The expert weights the oracle has to draw are kept below a
 budget so that one case costs the oracle about a second.
@@ -38,7 +38,7 @@ def random_shape(i: int) -> LayerShape:
         Do = 8 * int(g.integers(1, 257))          # 8 .. 2048
     Dq = int(g.integers(1, 2049))
     E = int(g.choice(EDGE_EXPERTS)) if g.random() < 0.4 else int(g.integers(1, 1025))
-    k = int(g.integers(1, min(E, 32 if g.random() < 0.4 else 8) + 1))
+    k = int(g.integers(1, min(E, 64 if g.random() < 0.4 else 8) + 1))
     F = int(g.choice(FFNS))
     Fs = 0 if g.random() < 0.3 else int(g.choice(FFNS))
     B = int(g.integers(1, 9)) if g.random() < 0.5 else int(g.integers(9, 65))
@@ -47,7 +47,8 @@ def random_shape(i: int) -> LayerShape:
         F //= 2
     while B > 1 and min(E, B * k) * 3 * F * H > DRAW_BUDGET:
         B = max(1, B // 2)
-    modes = ["natural", "zipf"] + (["hot"] if E >= 32 else []) + (["skewed"] if E >= 256 else [])
+    # hot routing draws each token's picks from 32 hot experts
+    modes = ["natural", "zipf"] + (["hot"] if E >= 32 and k <= 32 else []) + (["skewed"] if E >= 256 else [])
     rt = str(g.choice(modes))
     return LayerShape(f"sweep{i}_H{H}_Dq{Dq}_Do{Do}_E{E}_k{k}_F{F}_Fs{Fs}_B{B}_{rt}",
                       H, B, Dq, Do, E, k, F, Fs, rt)
@@ -67,7 +68,7 @@ def random_single_shape(i: int) -> LayerShape:
         Do = 8 * int(g.integers(1, 257))
     Dq = int(g.integers(1, 2049))
     E = int(g.choice([e for e in EDGE_EXPERTS if e <= 512])) if g.random() < 0.4 else int(g.integers(1, 513))
-    k = int(g.integers(1, min(E, 32 if g.random() < 0.4 else 8) + 1))
+    k = int(g.integers(1, min(E, 64 if g.random() < 0.4 else 8) + 1))
     F = int(g.choice(FFNS))
     Fs = 0 if g.random() < 0.3 else F
     bmax = min(8, 64 // k, 8192 // E, 8192 // (k * F), H // 2)
@@ -75,7 +76,7 @@ def random_single_shape(i: int) -> LayerShape:
     while F > 32 and min(E, B * k) * 3 * F * H > DRAW_BUDGET:
         F //= 2
         Fs = min(Fs, F) if Fs else 0
-    modes = ["natural", "zipf"] + (["hot"] if E >= 32 else []) + (["skewed"] if E >= 256 else [])
+    modes = ["natural", "zipf"] + (["hot"] if E >= 32 and k <= 32 else []) + (["skewed"] if E >= 256 else [])
     rt = str(g.choice(modes))
     return LayerShape(f"single{i}_H{H}_Dq{Dq}_Do{Do}_E{E}_k{k}_F{F}_Fs{Fs}_B{B}_{rt}",
                       H, B, Dq, Do, E, k, F, Fs, rt)
@@ -92,5 +93,5 @@ def in_envelope(s: LayerShape) -> bool:
     """The library's configuration limits (decode_layer_init's checks)."""
     return (8 <= s.hidden <= 16384 and s.hidden % 8 == 0 and 1 <= s.qkv_out <= 65536
             and 8 <= s.attn_dim <= 16384 and s.attn_dim % 8 == 0 and 1 <= s.n_experts <= 1024
-            and 1 <= s.top_k <= min(s.n_experts, 32) and s.expert_ffn in FFNS
+            and 1 <= s.top_k <= min(s.n_experts, 64) and s.expert_ffn in FFNS
             and s.shared_ffn in (0,) + FFNS and 1 <= s.batch <= 64)

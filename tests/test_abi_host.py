@@ -43,7 +43,7 @@ def good():
     ("hidden", 7170, dl.DL_ERR_UNSUPPORTED), ("hidden", 0, dl.DL_ERR_UNSUPPORTED),
     ("attn_dim", 12, dl.DL_ERR_UNSUPPORTED), ("qkv_out", 0, dl.DL_ERR_UNSUPPORTED),
     ("n_experts", 2000, dl.DL_ERR_UNSUPPORTED), ("top_k", 0, dl.DL_ERR_UNSUPPORTED),
-    ("top_k", 33, dl.DL_ERR_UNSUPPORTED), ("expert_ffn", 100, dl.DL_ERR_UNSUPPORTED),
+    ("top_k", 65, dl.DL_ERR_UNSUPPORTED), ("expert_ffn", 100, dl.DL_ERR_UNSUPPORTED),
     ("expert_ffn", 512, dl.DL_ERR_UNSUPPORTED), ("shared_ffn", 96, dl.DL_ERR_UNSUPPORTED),
     ("max_batch", 65, dl.DL_ERR_UNSUPPORTED), ("max_batch", 0, dl.DL_ERR_UNSUPPORTED),
     ("rms_eps", 0.0, dl.DL_ERR_UNSUPPORTED), ("rms_eps", float("inf"), dl.DL_ERR_UNSUPPORTED),
@@ -79,7 +79,7 @@ def _a256(n):
 # activations [8192], [4096]), the step counter, the status word, the wrap
 # barrier count, three arrival counters, and the batched path's gate/up group
 # and down row-group counters, all sized for the whole envelope.
-MAX_GU_GROUPS = (64 * 32 + 7) // 8 * (256 // 32) + (64 + 15) // 16 * (256 // 32)
+MAX_GU_GROUPS = (64 * 64 + 7) // 8 * (256 // 32) + (64 + 15) // 16 * (256 // 32)
 HANDOFF = (_a256(8 * 256 * 8) + 2 * _a256(8 * 8192) + _a256(8 * 4096) + 3 * 256 + _a256(12)
            + _a256(4 * MAX_GU_GROUPS) + _a256(4 * (16384 // 64)))
 

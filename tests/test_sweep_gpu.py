@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from synth import device as sdev, gen, routing
+from synth.gen import LayerShape
 from tests import sweep_shapes, workload
 from tests.parity import say
 from tests.test_parity_gpu import AUTO, BATCHED, MULTI, PATH_NAMES, check, run_gpu
@@ -78,6 +79,21 @@ def run_every_path(layer, tag: str) -> set:
 @pytest.mark.parametrize("i", range(N_SHAPES))
 def test_random_shape_parity(i):
     run_every_path(build(sweep_shapes.random_shape(i), 1000 + i), f"sweep{i}")
+
+
+@pytest.mark.parametrize("shape", [
+    # 64 picks of 384 experts (one token fits the single launch: B k <= 64)
+    LayerShape("k64_E384_b1", 1024, 1, 512, 512, 384, 64, 128, 128, "natural"),
+    LayerShape("k64_E384_b5", 1024, 5, 512, 512, 384, 64, 128, 128, "zipf"),
+    LayerShape("k48_E384_b3", 1024, 3, 512, 512, 384, 48, 128, 128, "natural"),
+    # every expert picked by every token: 4 matrix-core chunks per expert
+    LayerShape("k64_E64_b64", 1024, 64, 512, 512, 64, 64, 128, 128, "natural"),
+    LayerShape("k64_E64_b17", 1024, 17, 512, 512, 64, 64, 64, 0, "natural"),
+], ids=lambda s: s.name)
+def test_top_k_up_to_64(shape):
+    """top_k up to its limit of min(E, 64), on every path that takes the shape."""
+    ran = run_every_path(build(shape, 77), shape.name)
+    assert "multi" in ran
 
 
 @pytest.mark.parametrize("i", range(N_SINGLE_SHAPES))
