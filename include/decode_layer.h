@@ -90,8 +90,7 @@ enum {
  *                   Available on devices with at most 256 CUs when
  *                   hidden <= 8192 and <= 32 * CUs, n_experts <= 512 and
  *                   <= 2 * CUs, qkv_out <= 8 * CUs, and shared_ffn == 0 or
- *                   == expert_ffn; for
- *                   batches up to
+ *                   == expert_ffn; for batches up to
  *                   decode_layer_single_max_batch(), which is at most 8 and
  *                   also bounded by B*k <= 64, B*E <= 8192, B*k*F <= 8192 and
  *                   B*Fs <= 4096.
