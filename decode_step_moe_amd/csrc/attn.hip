@@ -52,6 +52,7 @@ constexpr int kAPoRow = 20;              // floats per head-dim row of a wave's 
 constexpr int kALds = (4 * kAVWave > (128 + 4 * kAD * kAPoRow) * 4) ? 4 * kAVWave : (128 + 4 * kAD * kAPoRow) * 4;
 static_assert(2 * kAMaxSplit * 16 * 4 <= kALds, "combine weights");
 constexpr unsigned kCoherent = 16;       // buffer cache policy: coherent at agent scope
+constexpr int kASpecRequests = 4;        // at most this many requests: the first tile is loaded speculatively
 
 typedef __bf16 bf16x8a __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2a __attribute__((ext_vector_type(2)));
@@ -70,6 +71,7 @@ struct AttnArgs {
   unsigned *counters;  // [max_requests * Hkv * row splits]
   int R, T, Hq, Hkv, C, max_past, grp, M, RS, tps, n_split;
   float softmax_scale;
+  int spec;            // nonzero: the first tile is requested before the past length arrives
 };
 
 __device__ __forceinline__ f32x4a mfma16(const uint4 &a, const uint4 &b, f32x4a c) {
@@ -202,6 +204,47 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
   const int L = a.past_len[r];
   const int M = a.M, grp = a.grp, T = a.T, row0 = 16 * rs;
   constexpr float kNegInf = -__builtin_inff();
+  const size_t cbase = (size_t)rg * a.C * kAD;
+  const int tb = s * a.tps;
+
+  // ---- loads of one tile: this wave's 64 V rows (lane m = lane / 8 takes
+  // the 8 keys of P V chunk m, 16 head-dim bytes 16 (lane % 8) ..) and its
+  // K fragments (key 16 kt + n, head-dim bytes 64 h + 16 g4 ..), positions
+  // clamped to pmax; none when the wave's keys all lie at or past pend.
+  const int vm = lane >> 3, vdg = lane & 7;
+  // plain locals: a lambda must not take the address of the kernel arguments
+  const uint8_t *const kcache = a.k_cache, *const vcache = a.v_cache;
+  uint4 vst[8], kr[4][2];
+  auto load_tile = [&](int t, int pmax, int pend) __attribute__((always_inline)) {
+    const int p0 = t * kATile + 64 * wv;
+    if (p0 >= pend) return;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int p = min(p0 + slice_key(vm >> 2, vm & 3, k), pmax);
+      vst[k] = ld16(vcache + cbase + (size_t)p * kAD + 16 * vdg);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint8_t *kp = kcache + cbase + (size_t)min(p0 + 16 * kt + n, pmax) * kAD + 16 * g4;
+      kr[kt][0] = ld16(kp);
+      kr[kt][1] = ld16(kp + 64);
+    }
+  };
+  // With few requests the first tile is requested before the past length
+  // arrives, its positions clamped to the cache's capacity (the step's own
+  // positions and those past the end are replaced or masked below, as in
+  // every tile); a split that then finds itself past its request's end has
+  // read one tile for nothing.
+  if (a.spec) load_tile(tb, a.C - 1, a.C);
+  // query fragments: row row0 + n, head-dim elements in the K fragments' order
+  uint4 qa[4];
+  {
+    const int row = min(row0 + n, M - 1), j = row / grp, h = g * grp + row % grp;
+    const uint16_t *qp = a.q + ((size_t)(r * T + j) * a.Hq + h) * kAD + 16 * g4;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qa[st] = ld16(qp + 64 * (st >> 1) + 8 * (st & 1));
+  }
+  const float ksc = a.k_scale[g], vsc = a.v_scale[g];
   if (request_bad(a, L)) {
     // an impossible length: this request's outputs are NaN, nothing else runs
     if (s == 0)
@@ -213,50 +256,19 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
           if (a.out_bf16) a.out_bf16[i] = 0x7fc0u;
         }
       }
+    __builtin_amdgcn_s_waitcnt(0x0f70);                  // vmcnt(0): no load left in flight
     return;
   }
   const int len = L + T;                                 // positions after this step's tokens
   const int ntile = (len + kATile - 1) / kATile;
-  const int tb = s * a.tps;
-  if (tb >= ntile) return;                               // past this request's end: not counted
-  const int te = min(tb + a.tps, ntile), nact = (ntile + a.tps - 1) / a.tps;
-  const size_t cbase = (size_t)rg * a.C * kAD;
-  const int lr = max(L - 1, 0);                          // cache reads stay below the step's own positions
-  const float ksc = a.k_scale[g], vsc = a.v_scale[g];
-  const size_t new_row0 = (size_t)r * T * a.Hkv + g;    // row (r, j, g) of k_new / v_new is new_row0 + j Hkv
-
-  // ---- loads of one tile: this wave's 64 V rows (lane m = lane / 8 takes
-  // the 8 keys of P V chunk m, 16 head-dim bytes 16 (lane % 8) ..) and its
-  // K fragments (key 16 kt + n, head-dim bytes 64 h + 16 g4 ..).  Reads stay
-  // below the step's own positions (their codes come from LDS, see below).
-  const int vm = lane >> 3, vdg = lane & 7;
-  // plain locals: a lambda must not take the address of the kernel arguments
-  const uint8_t *const kcache = a.k_cache, *const vcache = a.v_cache;
-  uint4 vst[8], kr[4][2];
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
-    const int p0 = t * kATile + 64 * wv;
-    if (p0 >= len) return;                               // the wave's keys all lie past the end
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int p = min(p0 + slice_key(vm >> 2, vm & 3, k), lr);
-      vst[k] = ld16(vcache + cbase + (size_t)p * kAD + 16 * vdg);
-    }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const uint8_t *kp = kcache + cbase + (size_t)min(p0 + 16 * kt + n, lr) * kAD + 16 * g4;
-      kr[kt][0] = ld16(kp);
-      kr[kt][1] = ld16(kp + 64);
-    }
-  };
-  if (PF) load_tile(tb);
-  // query fragments: row row0 + n, head-dim elements in the K fragments' order
-  uint4 qa[4];
-  {
-    const int row = min(row0 + n, M - 1), j = row / grp, h = g * grp + row % grp;
-    const uint16_t *qp = a.q + ((size_t)(r * T + j) * a.Hq + h) * kAD + 16 * g4;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) qa[st] = ld16(qp + 64 * (st >> 1) + 8 * (st & 1));
+  if (tb >= ntile) {                                     // past this request's end: not counted
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    return;
   }
+  const int te = min(tb + a.tps, ntile), nact = (ntile + a.tps - 1) / a.tps;
+  const int lr = max(L - 1, 0);                          // cache reads stay below the step's own positions
+  const size_t new_row0 = (size_t)r * T * a.Hkv + g;    // row (r, j, g) of k_new / v_new is new_row0 + j Hkv
+  if (!a.spec) load_tile(tb, lr, len);
   // a wave's running state for row row0 + n: its maximum (the same in the 4
   // lane groups), its sum over the lane's own keys, O^T columns d = 16 dt + 4 g4 + i
   float am = kNegInf, al = 0.f;
@@ -288,7 +300,6 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
     const int p0 = t * kATile + 64 * wv;
     const bool live = p0 < len;                          // wave-uniform
     f32x4a sa[4];
-    if (!PF) load_tile(t);
     if (live) {
       if (p0 + 64 > L) {                                 // wave-uniform: the slice holds new or past-the-end keys
 #pragma unroll
@@ -331,7 +342,7 @@ __global__ void __launch_bounds__(256, 2) attn_step(AttnArgs a) {
           sa[kt] = mfma16(kb, qa[st], sa[kt]);
         }
     }
-    if (PF && t + 1 < te) load_tile(t + 1);              // overlaps the softmax and P V below
+    if (PF && t + 1 < te) load_tile(t + 1, lr, len);     // overlaps the softmax and P V below
     if (live) {
       uint4 ph[2], pl[2];
       float mt = kNegInf;
@@ -677,6 +688,9 @@ int decode_attention_step(const decode_attention_config *cfg, const decode_atten
   if (cfg->max_splits > 0) split = std::min(split, cfg->max_splits);
   a.tps = (tiles + split - 1) / split;
   split = (tiles + a.tps - 1) / a.tps;
+  // few requests: the step is latency-bound and splits past a short
+  // request's end are few, so the first tile is worth requesting early
+  a.spec = a.R <= kASpecRequests;
   const dim3 grid(split, rg);
   void (*kern)(AttnArgs) = a.tps > 1 ? attn_step<true> : attn_step<false>;
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
