@@ -328,3 +328,38 @@ def test_bf16_output_feeds_the_layer_step():
     m = parity.compare(got, workload.expected(layer))
     say("[attention -> layer step] " + ", ".join(f"{k}={v:.3e}" for k, v in m.items() if k != "fails"))
     assert not m["fails"], m["fails"]
+
+
+def random_attention_case(i: int):
+    """Seeded random shape across the attention envelope: 1-16 requests, 1-8
+    tokens, 1-4 KV heads with up to 32 query rows each, caches of 8-4096
+    positions with past lengths anywhere below them (zero included), forced
+    split counts now and then, and the bf16 copy of the output on half."""
+    g = np.random.default_rng([0xA77E, i])
+    T = int(g.integers(1, 9))
+    grp = int(g.integers(1, 32 // T + 1))
+    Hkv = int(g.choice([1, 1, 2, 3, 4]))
+    R = int(g.integers(1, 17))
+    C = int(g.choice([8, 64, 255, 256, 257, 1000, 2048, 4096])) if g.random() < 0.4 else int(g.integers(8, 4097))
+    C = max(C, T)
+    hi = int(g.integers(0, C - T + 1))
+    lo = int(g.integers(0, hi + 1))
+    splits = int(g.integers(1, 9)) if g.random() < 0.3 else 0
+    return dict(R=R, T=T, Hq=grp * Hkv, Hkv=Hkv, C=C, lo=lo, hi=hi, splits=splits, bf16=bool(g.random() < 0.5))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    c = random_attention_case(i)
+    name = f"rand{i}_R{c['R']}_T{c['T']}_Hq{c['Hq']}_Hkv{c['Hkv']}_C{c['C']}_past{c['lo']}-{c['hi']}_s{c['splits']}"
+    st = attn_gen.draw(c["R"], c["T"], c["Hq"], c["Hkv"], c["C"], c["lo"], c["hi"], seed=100 + i)
+    say(f"attention {name}: start")
+    dev = Dev(st, max_splits=c["splits"], with_bf16=c["bf16"])
+    dev.step()
+    out, kc, vc = dev.results()
+    want, wk, wv = expect(st)
+    check_caches(name, kc, vc, wk, wv)
+    check_out(name, out, want)
+    if c["bf16"]:
+        b = dev.out_bf16.float().cpu().numpy()
+        assert np.array_equal(b, torch.from_numpy(out).to(torch.bfloat16).float().numpy()), name
