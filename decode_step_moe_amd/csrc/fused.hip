@@ -802,6 +802,20 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
         }
       }
       DL_SCHED_FENCE();
+      if constexpr (TG == 1) {
+        // the whole row is now in this workgroup's registers: keep a copy in
+        // the down-projection staging area (free until phase D), where every
+        // gate/up item of phase C reads it
+        float4 *hl = reinterpret_cast<float4 *>(L.w2);
+#pragma unroll
+        for (int j = 0; j < kChunkJ; ++j) {
+          const int c = tid + kFT * j;
+          if (c < nc) {
+            hl[2 * c] = hx[0][j][0];
+            hl[2 * c + 1] = hx[0][j][1];
+          }
+        }
+      }
 #pragma unroll
       for (int tt = 0; tt < TG; ++tt) {
         const int t = t0 + tt;
@@ -869,9 +883,9 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
     gather_tagged(a.logit, L.u.logits, tid, kCtl, B * E, tag, a.spin_limit, &L.bad);
   } else {
     by_tokens(B, [&](auto nt) { qkv_rows<decltype(nt)::value>(a, L, w, G); });
-    // one token: its hg row, at device scope, into the down-projection
-    // staging area (free until phase D), where every gate/up item reads it
-    if (B == 1) {
+    // one token, in a workgroup without units (phase B did not read hg):
+    // its hg row, at device scope, into the down-projection staging area
+    if (B == 1 && !(kind[0] || kind[1])) {
       static_assert(sizeof(float) * kFusedMaxH <= sizeof(L.w2), "one hg row fits the staging area");
       const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc((void *)a.hg, 0, H * 4, 0x00020000);
       constexpr int PT = kFusedMaxH / 4 / kStr;  // 16-byte words per stream thread (at most)
@@ -1087,7 +1101,7 @@ __global__ void __launch_bounds__(kFT, 1) fused_step_kernel(FusedArgs a) {
       return sl * a.F + (int)((x - es + cs - 1) / cs);
     };
     const int kb = first_item((long)w * C / G), ke = first_item((long)(w + 1) * C / G);
-    // one token: its hg row is already in LDS (phase C) and every item reads it there
+    // one token: its hg row is already in LDS (phase B or C) and every item reads it there
     const bool pre = B == 1;
     const bool stage = !pre && ke - kb >= 8;
     float *hl = pre ? reinterpret_cast<float *>(L.w2) : reinterpret_cast<float *>(&L.u);
