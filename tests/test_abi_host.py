@@ -258,3 +258,37 @@ def test_attention_workspace_and_validation():
     assert at.check(c, io(out=0x9004)) == dl.DL_ERR_INVALID_ARG
     assert at.check(c, io(workspace=0x10010)) == dl.DL_ERR_INVALID_ARG  # 256-byte alignment
     assert "workspace" in dl.last_error()
+
+
+def test_kernels_use_no_scratch_memory(tmp_path):
+    """Every kernel of the built library keeps its state in registers and LDS:
+    a kernel with a private segment (a stack, or an array spilled to scratch
+    memory) runs every phase far slower, so the device code objects of the
+    objects the build compiled are read back and each kernel's fixed private
+    segment size must be 0."""
+    import glob
+    import subprocess
+    llvm = "/opt/rocm/lib/llvm/bin"
+    objs = sorted(glob.glob(os.path.join(ROOT, "_build", "*.o")))
+    tools = [os.path.join(llvm, t) for t in ("llvm-objcopy", "clang-offload-bundler", "llvm-readelf")]
+    if not objs or not all(os.path.exists(t) for t in tools):
+        pytest.skip("no build objects or no LLVM tools")
+    seen = {}
+    for o in objs:
+        base = os.path.splitext(os.path.basename(o))[0]
+        fb, co = tmp_path / f"{base}.fatbin", tmp_path / f"{base}.co"
+        r = subprocess.run([tools[0], f"--dump-section=.hip_fatbin={fb}", o, str(tmp_path / f"{base}.host.o")],
+                           capture_output=True, text=True)
+        if r.returncode != 0 and "not found" in r.stderr:
+            continue   # host code only
+        assert r.returncode == 0, r.stderr
+        subprocess.run([tools[1], "--unbundle", "--type=o", f"--input={fb}",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"],
+                       check=True, capture_output=True)
+        notes = subprocess.run([tools[2], "--notes", str(co)], check=True, capture_output=True, text=True).stdout
+        names = re.findall(r"^\s+\.name:\s+(\S+)$", notes, re.M)
+        sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", notes)
+        assert len(names) == len(sizes), base
+        seen.update({n: int(sz) for n, sz in zip(names, sizes)})
+    assert any("fused_step_kernel" in n for n in seen) and any("gateup_b" in n for n in seen)
+    assert {n: sz for n, sz in seen.items() if sz} == {}
